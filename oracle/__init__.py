@@ -1,0 +1,37 @@
+"""Plain fp64 CPU oracle for the masked-diffusion loss path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product package may import, call,
+link or execute anything under this directory; only the test-suite, the smoke
+check in ``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` use it.
+
+The oracle is written from the pages' definitions and shares no code with the
+HIP library (no common helpers, tables or constants).  It is deliberately slow
+and obvious: numpy in float64, one library matmul per V-chunk, no fusion.
+
+Sources for what is computed:
+  * LLaDA-8B-MDLM-LoRA model card, "Training" table, "Objective" row:
+    t ~ U(0,1) per sequence, mask probability p = (1-1e-3) t + 1e-3,
+    cross-entropy on masked tokens divided by p.
+  * diffusiongemma-26B-A4B-it-ALWAYS-THINK, "Finetuning notes": corrupt
+    positions with uniform-random vocabulary ids at a per-example rate
+    t ~ U(eps, 1), no mask token; the logit softcap is applied exactly once.
+  * Native diffusion language-model training (Axolotl docs): model table
+    (aligned vs shifted logits; inverse-time weighted CE), "Packed training"
+    (documents stay isolated; padding is excluded from loss) and
+    "Adapters, merging and inference" (full-vocabulary CE from hidden states
+    through a plain linear output head, aligned targets).
+"""
+
+from .philox import philox4x32_10  # noqa: F401
+from .mdlm import (  # noqa: F401
+    NOISE_ABSORB,
+    NOISE_UNIFORM,
+    ALIGNED,
+    SHIFTED,
+    noise_levels,
+    corrupt,
+    compact,
+    head_ce,
+    head_ce_rows,
+    mdlm_loss,
+)

@@ -1,0 +1,257 @@
+"""fp64 reference for corruption, compaction and the fused head + CE loss.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).  Each function follows
+the definition on the pages, step by step, in float64.  Where the pages are
+silent the reading taken is stated next to the step.
+
+Pages cited:
+  [LLaDA]  LLaDA-8B-MDLM-LoRA model card, "Training" table ("Objective",
+           "Batch", "Precision" rows) and the paragraph after it.
+  [Gemma]  diffusiongemma-26B-A4B-it-ALWAYS-THINK, "Finetuning notes".
+  [Axolotl] Native diffusion language-model training: the model table,
+           "Start with Nemotron 3B", "Packed training", "Attention backends",
+           "Adapters, merging and inference", "Batching".
+"""
+
+import numpy as np
+from scipy.special import logsumexp
+
+from .philox import philox4x32_10
+
+NOISE_ABSORB = 0
+NOISE_UNIFORM = 1
+ALIGNED = 0
+SHIFTED = 1
+
+# Stream tags carried in the last counter word: one independent stream per
+# kind of draw, so no two draws ever share a counter.
+TAG_DOC_T = 0      # per-document noise level t
+TAG_BERNOULLI = 1  # per-token keep/corrupt decision
+TAG_REPLACE = 2    # per-token replacement id under uniform noise
+
+_TWO24 = float(1 << 24)
+
+
+def _key(seed):
+    seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    return seed & 0xFFFFFFFF, seed >> 32
+
+
+def noise_levels(seed, eps, n_docs):
+    """Per-document noise level t_b, corruption probability p_b and threshold.
+
+    [LLaDA] Objective row: t ~ U(0,1) per sequence, mask probability
+    p = (1 - 1e-3) t + 1e-3.  [Gemma] Finetuning notes: per-example rate
+    t ~ U(eps, 1) -- the same affine map with general eps, so both noise modes
+    share this step.
+
+    Reading taken: t is the top 24 bits of Philox word 0 at counter
+    (b, 0, 0, TAG_DOC_T), scaled by 2^-24, so t lies on the grid
+    {0, 2^-24, ..., 1 - 2^-24}.  p is evaluated in IEEE fp64 in the order
+    (1 - eps), times t, plus eps (each step rounded).  The integer threshold
+    thr = ceil(p * 2^24) is exact (power-of-two scaling) and turns the test
+    "u < p" for a 24-bit uniform u = u24 * 2^-24 into "u24 < thr".
+
+    Returns (t, p, thr): float64[B], float64[B], int64[B].
+    """
+    k0, k1 = _key(seed)
+    b = np.arange(n_docs, dtype=np.uint64)
+    r0, _, _, _ = philox4x32_10(b & 0xFFFFFFFF, b >> 32, 0, TAG_DOC_T, k0, k1)
+    u24 = (r0 >> np.uint32(8)).astype(np.float64)
+    t = u24 / _TWO24
+    one_minus_eps = 1.0 - float(eps)
+    p = float(eps) + one_minus_eps * t
+    thr = np.ceil(p * _TWO24).astype(np.int64)
+    return t, p, thr
+
+
+def _token_words(seed, n_tokens, tag):
+    """Philox word for each token index g: word (g & 3) of the call at counter
+    (g >> 2 low 32 bits, g >> 2 high 32 bits, 0, tag)."""
+    k0, k1 = _key(seed)
+    g = np.arange(n_tokens, dtype=np.uint64)
+    q = g >> np.uint64(2)
+    words = np.stack(philox4x32_10(q & 0xFFFFFFFF, q >> 32, 0, tag, k0, k1), axis=1)
+    return words[np.arange(n_tokens), (g & np.uint64(3)).astype(np.int64)]
+
+
+def corrupt(x0, cu_seqlens, seed, eps, noise, mask_id, rand_vocab):
+    """Corrupt a packed token stream, one noise level per document.
+
+    [LLaDA] Objective row: absorbing corruption; each token of a sequence is
+    masked with probability p (read here as independent Bernoulli(p) draws,
+    no forced minimum count).  [Axolotl] "Start with Nemotron 3B": masked
+    tokens become the mask id (100 there).  [Gemma] Finetuning notes: under
+    uniform noise a corrupted position takes a uniform-random vocabulary id
+    (no mask token).  [Axolotl] "Packed training": documents in one packed
+    stream stay isolated, so each document draws its own t.
+
+    Readings taken: the decision for token g is (word1(g) >> 8) < thr_b with
+    word1 from stream TAG_BERNOULLI; the replacement id is
+    floor(word2(g) * rand_vocab / 2^32) with word2 from stream TAG_REPLACE
+    (multiply-shift; a draw equal to x0 still counts as corrupted).
+
+    x0: int[N]; cu_seqlens: int[B+1] with cu[0] = 0, cu[B] = N, nondecreasing.
+    Returns (xt int32[N], corrupted uint8[N], p_doc float64[B],
+    doc_counts int32[B]).
+    """
+    x0 = np.asarray(x0, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    n = x0.shape[0]
+    n_docs = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == n
+    _, p, thr = noise_levels(seed, eps, n_docs)
+    w1 = _token_words(seed, n, TAG_BERNOULLI).astype(np.int64)
+    if noise == NOISE_UNIFORM:
+        w2 = _token_words(seed, n, TAG_REPLACE).astype(np.uint64)
+    xt = x0.copy()
+    corrupted = np.zeros(n, dtype=np.uint8)
+    doc_counts = np.zeros(n_docs, dtype=np.int32)
+    for b in range(n_docs):
+        lo, hi = cu[b], cu[b + 1]
+        sel = (w1[lo:hi] >> 8) < thr[b]
+        corrupted[lo:hi] = sel
+        doc_counts[b] = int(sel.sum())
+        if noise == NOISE_ABSORB:
+            xt[lo:hi][sel] = mask_id
+        else:
+            ids = (w2[lo:hi] * np.uint64(rand_vocab)) >> np.uint64(32)
+            xt[lo:hi][sel] = ids[sel].astype(np.int64)
+    return xt.astype(np.int32), corrupted, p, doc_counts
+
+
+def compact(corrupted, x0, cu_seqlens, p_doc, align):
+    """List the scored rows in ascending token order, with targets and weights.
+
+    [LLaDA] Objective row: the loss is cross-entropy on masked tokens divided
+    by the mask probability.  [Axolotl] model table: Nemotron uses aligned
+    logits (the hidden state at position g predicts token g), Dream uses
+    shifted logits (position g-1 predicts token g).
+
+    Readings taken:
+      * aligned: every corrupted g gives (row g, target x0[g]);
+      * shifted: every corrupted g except a document's first token gives
+        (row g-1, target x0[g]); a document start has no predecessor inside
+        its own document ("Packed training": documents stay isolated);
+      * weight w = 1 / (p_b * N) with N the total number of tokens in the
+        call ("loss = sum_masked CE/p / total tokens"), evaluated in fp64.
+
+    Returns (row_idx int64[M], tgt int64[M], w float64[M]).  The weight the
+    library stores is fp32; ``np.float32(w)`` is its exact expected value.
+    """
+    corrupted = np.asarray(corrupted).astype(bool)
+    x0 = np.asarray(x0, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    p_doc = np.asarray(p_doc, dtype=np.float64)
+    n = x0.shape[0]
+    rows, tgts, ws = [], [], []
+    for b in range(cu.shape[0] - 1):
+        for g in range(cu[b], cu[b + 1]):
+            if not corrupted[g]:
+                continue
+            if align == SHIFTED:
+                if g == cu[b]:
+                    continue
+                rows.append(g - 1)
+            else:
+                rows.append(g)
+            tgts.append(x0[g])
+            ws.append(1.0 / (p_doc[b] * float(n)))
+    return (np.asarray(rows, dtype=np.int64), np.asarray(tgts, dtype=np.int64),
+            np.asarray(ws, dtype=np.float64))
+
+
+def _capped_logits(rows_h, w_chunk, softcap):
+    """Logits of the plain linear head, z = h W^T (no bias: [Axolotl]
+    "Adapters, merging and inference" requires a plain linear output head),
+    then the tanh softcap c*tanh(z/c) applied once when c > 0 ([Gemma]
+    Finetuning notes: the forward already softcaps; do not apply it twice).
+    Returns (capped logits, d capped / d z)."""
+    z = rows_h @ w_chunk.T
+    if softcap > 0.0:
+        th = np.tanh(z / softcap)
+        return softcap * th, 1.0 - th * th
+    return z, np.ones_like(z)
+
+
+def head_ce_rows(hidden, W, row_idx, tgt, softcap=0.0, chunk=8192):
+    """Per-row cross-entropy of hidden[row_idx] through the head W against tgt.
+
+    CE_j = logsumexp_v(zhat_jv) - zhat_j,tgt_j over the full vocabulary.
+    The vocabulary is processed in chunks only to bound memory; the
+    log-sum-exp of the whole row is the log-sum-exp of the chunk values.
+
+    Returns (ce float64[M], lse float64[M]).
+    """
+    rows_h = np.asarray(hidden)[np.asarray(row_idx, dtype=np.int64)].astype(np.float64)
+    tgt = np.asarray(tgt, dtype=np.int64)
+    W = np.asarray(W)
+    m = rows_h.shape[0]
+    v_total = W.shape[0]
+    chunk_lse = []
+    z_tgt = np.zeros(m, dtype=np.float64)
+    for v0 in range(0, v_total, chunk):
+        v1 = min(v0 + chunk, v_total)
+        zc, _ = _capped_logits(rows_h, W[v0:v1].astype(np.float64), softcap)
+        chunk_lse.append(logsumexp(zc, axis=1))
+        hit = (tgt >= v0) & (tgt < v1)
+        z_tgt[hit] = zc[np.flatnonzero(hit), tgt[hit] - v0]
+    if m == 0:
+        return np.zeros(0), np.zeros(0)
+    lse = logsumexp(np.stack(chunk_lse, axis=1), axis=1)
+    return lse - z_tgt, lse
+
+
+def head_ce(hidden, W, row_idx, tgt, w, softcap=0.0, want_grad=True, chunk=8192):
+    """Weighted CE loss and its gradient with respect to every hidden row.
+
+    loss = sum_j w_j * CE_j.
+    d loss / d h_row_j = w_j * ((softmax(zhat_j) - onehot(tgt_j)) * zhat'_j) W
+    where zhat' is the softcap's derivative (1 without a cap).  The head is
+    frozen ([LLaDA] LoRA row: embeddings and output layer frozen), so no
+    gradient for W is formed.  Rows of hidden that are not scored get an
+    exact zero gradient.
+
+    Returns (loss float64, ce float64[M], d_hidden float64[N,H] or None).
+    """
+    hidden = np.asarray(hidden)
+    row_idx = np.asarray(row_idx, dtype=np.int64)
+    tgt = np.asarray(tgt, dtype=np.int64)
+    w = np.asarray(w, dtype=np.float64)
+    ce, lse = head_ce_rows(hidden, W, row_idx, tgt, softcap, chunk)
+    loss = float(np.sum(w * ce)) if ce.size else 0.0
+    if not want_grad:
+        return loss, ce, None
+    d_hidden = np.zeros(hidden.shape, dtype=np.float64)
+    if row_idx.size == 0:
+        return loss, ce, d_hidden
+    rows_h = hidden[row_idx].astype(np.float64)
+    d_rows = np.zeros_like(rows_h)
+    W = np.asarray(W)
+    for v0 in range(0, W.shape[0], chunk):
+        v1 = min(v0 + chunk, W.shape[0])
+        wc = W[v0:v1].astype(np.float64)
+        zc, dcap = _capped_logits(rows_h, wc, softcap)
+        prob = np.exp(zc - lse[:, None])
+        hit = np.flatnonzero((tgt >= v0) & (tgt < v1))
+        prob[hit, tgt[hit] - v0] -= 1.0
+        d_rows += (w[:, None] * prob * dcap) @ wc
+    d_hidden[row_idx] = d_rows
+    return loss, ce, d_hidden
+
+
+def mdlm_loss(x0, cu_seqlens, hidden, W, seed, eps, noise, mask_id, rand_vocab,
+              align, softcap=0.0, want_grad=True, chunk=8192):
+    """The whole path: corrupt, list scored rows, weighted head + CE.
+
+    The model forward that would turn xt into hidden states lies outside this
+    path; ``hidden`` is given.  Returns a dict of every intermediate.
+    """
+    xt, corrupted, p_doc, doc_counts = corrupt(
+        x0, cu_seqlens, seed, eps, noise, mask_id, rand_vocab)
+    row_idx, tgt, w = compact(corrupted, x0, cu_seqlens, p_doc, align)
+    loss, ce, d_hidden = head_ce(hidden, W, row_idx, tgt, w, softcap,
+                                 want_grad, chunk)
+    return dict(xt=xt, corrupted=corrupted, p_doc=p_doc, doc_counts=doc_counts,
+                row_idx=row_idx, tgt=tgt, w=w, loss=loss, ce=ce,
+                d_hidden=d_hidden)
