@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Throughput of the masked-diffusion loss path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+mdlm_corrupt -> mdlm_compact_masked -> mdlm_fused_head_ce_fwd_bwd (loss and
+d_hidden), enqueued on one stream with no host synchronisation.  Each timed
+step draws fresh noise (Philox seed = step index), as a training loop would.
+
+Default workload: one sequence of 4,096 tokens, H = 4,096, V = 126,464, bf16
+inputs with fp32 accumulation, absorbing noise (eps = 1e-3), aligned logits
+(LLaDA-8B-MDLM-LoRA card, Training table: batch of sequences of at most 4,096
+tokens, bf16 base weights).  Inputs are seeded synthetic data resident in HBM
+before timing starts.
+
+Prints ONE JSON line: tokens/s of whole steps, the roofline of the fused
+head + CE call (algorithmic 4 M H V flops per call over its HIP-event time
+on the launch stream, against the 2.5 PFLOP/s dense bf16 MFMA peak), the
+HBM rate of corruption and compaction at 2^27 tokens, and the fp64 CPU oracle
+timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "corrupted-LM loss fwd+bwd tokens/s at V=126,464; % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", type=int, default=2)
+    p.add_argument("--align", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--bandwidth-tokens", type=int, default=1 << 27,
+                   help="tokens of the corruption/compaction bandwidth run (0 = skip)")
+    p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles",
+                                                          "head_ce_traffic.json"),
+                   help="measured HBM traffic of the fused call, if current")
+    return p.parse_args()
+
+
+def to_device(inp, dev):
+    import torch
+    x0 = torch.from_numpy(inp.x0).to(dev)
+    cu = torch.from_numpy(inp.cu_seqlens).to(dev)
+    if inp.wl.dtype == "bf16":
+        h = torch.from_numpy(inp.hidden_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+        W = torch.from_numpy(inp.W_bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        h = torch.from_numpy(inp.hidden).to(dev)
+        W = torch.from_numpy(inp.W).to(dev)
+    return x0, cu, h, W
+
+
+def gpu_steps(args, inp, dev):
+    import torch
+    from uniform_noise_diffusion_amd.pipeline import MdlmLossStep
+    wl = inp.wl
+    align = wl.align if args.align is None else args.align
+    x0, cu, h, W = to_device(inp, dev)
+    dtype = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    step = MdlmLossStep(wl.n_tokens, wl.n_docs, wl.H, wl.V, dtype=dtype, device=dev)
+
+    def one(seed, ev=None):
+        step.corrupt(x0, cu, seed, wl.eps, wl.noise, wl.mask_id, wl.rand_vocab)
+        step.compact(x0, cu, align)
+        if ev is not None:
+            ev[0].record()
+        step.head_ce(h, W, wl.softcap, row_ce=False)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        one(1_000_000 + i)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        one(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    head_ms = [a.elapsed_time(b) for a, b in evs]
+    losses = []
+    rows = []
+    # scored-row counts of the timed seeds, recomputed after the timed region
+    for i in range(K):
+        step.corrupt(x0, cu, i, wl.eps, wl.noise, wl.mask_id, wl.rand_vocab)
+        step.compact(x0, cu, align)
+        rows.append(int(step.n_rows.item()))
+    step.head_ce(h, W, wl.softcap)
+    torch.cuda.synchronize()
+    losses.append(float(step.loss.item()))
+    if not all(np.isfinite(losses)):
+        raise RuntimeError("non-finite loss")
+    return dict(total_ms=total_ms, wall_s=wall, head_ms=head_ms, rows=rows, align=align)
+
+
+def bandwidth(n_tokens, dev, reps=10):
+    """Corruption and compaction at a bandwidth-sized stream: 2^27 tokens in
+    documents of 4,096 (32,768 documents)."""
+    import torch
+    from uniform_noise_diffusion_amd.pipeline import MdlmLossStep
+    L = 4096
+    n = n_tokens // L * L
+    n_docs = n // L
+    g = torch.Generator(device=dev).manual_seed(0)
+    x0 = torch.randint(0, 126336, (n,), dtype=torch.int32, device=dev, generator=g)
+    cu = torch.arange(0, n + 1, L, dtype=torch.int32, device=dev)
+    step = MdlmLossStep(n, n_docs, 64, 64, device=dev, head_workspace_bytes=0, want_grad=False)
+    for i in range(2):
+        step.corrupt(x0, cu, i, 1e-3, 0, 126336, 126464)
+        step.compact(x0, cu, 0)
+    torch.cuda.synchronize()
+    ec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        ec[i][0].record()
+        step.corrupt(x0, cu, 100 + i, 1e-3, 0, 126336, 126464)
+        ec[i][1].record()
+        step.compact(x0, cu, 0)
+        ec[i][2].record()
+    torch.cuda.synchronize()
+    t_cor = np.mean([a.elapsed_time(b) for a, b, _ in ec]) * 1e-3
+    t_cmp = np.mean([b.elapsed_time(c) for _, b, c in ec]) * 1e-3
+    m = int(step.n_rows.item())
+    # algorithmic bytes: corrupt reads x0 (4 B) and writes xt (4 B) and the
+    # mask (1 B) per token; compact reads the mask (1 B) per token and, per
+    # scored row, the target (4 B) and writes row, target and weight (12 B)
+    b_cor = 9.0 * n
+    b_cmp = 1.0 * n + 16.0 * m
+    return dict(n_tokens=n, scored_rows=m,
+                corrupt_us=t_cor * 1e6, corrupt_GBs=b_cor / t_cor / 1e9,
+                corrupt_frac=b_cor / t_cor / 1e9 / PEAK_HBM_GBS,
+                compact_us=t_cmp * 1e6, compact_GBs=b_cmp / t_cmp / 1e9,
+                compact_frac=b_cmp / t_cmp / 1e9 / PEAK_HBM_GBS)
+
+
+def cpu_baseline(inp, mean_rows, seconds):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload."""
+    import oracle
+    wl = inp.wl
+    t0 = time.perf_counter()
+    xt, corrupted, p, _ = oracle.corrupt(inp.x0, inp.cu_seqlens, 0, wl.eps, wl.noise,
+                                         wl.mask_id, wl.rand_vocab)
+    rows, tgt, w = oracle.compact(corrupted, inp.x0, inp.cu_seqlens, p, wl.align)
+    t_cc = time.perf_counter() - t0
+    # calibrate on a few rows, then size the sample to about `seconds`
+    t1 = time.perf_counter()
+    oracle.head_ce(inp.hidden, inp.W, rows[:4], tgt[:4], w[:4], wl.softcap)
+    per_row = (time.perf_counter() - t1) / 4
+    s = int(max(4, min(rows.shape[0], seconds / max(per_row, 1e-9))))
+    t2 = time.perf_counter()
+    oracle.head_ce(inp.hidden, inp.W, rows[:s], tgt[:s], w[:s], wl.softcap)
+    t_rows = time.perf_counter() - t2
+    est_step = t_cc + t_rows / s * mean_rows
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or os.cpu_count()
+    except Exception:  # noqa: BLE001
+        cores = os.cpu_count()
+    return dict(value=wl.n_tokens / est_step, unit="tokens/s", cores=cores, kind="oracle",
+                sample=(f"oracle corrupt+compact over all {wl.n_tokens} tokens "
+                        f"({t_cc:.2f} s) plus fp64 head+CE fwd+bwd over {s} scored rows "
+                        f"({t_rows:.2f} s), scaled to {mean_rows:.0f} scored rows per step"))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library runs the loss path on a single "
+              "MI355X and has no multi-GPU mode; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads as WL
+    from uniform_noise_diffusion_amd import binding
+    binding.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    wl = WL.make_workload(args.workload)
+    log(f"generating workload {wl.name}: N={wl.n_tokens} H={wl.H} V={wl.V}")
+    inp = WL.generate(wl)
+    log("timing steps")
+    r = gpu_steps(args, inp, dev)
+    K = args.steps
+    rows = np.array(r["rows"], dtype=np.float64)
+    head_s = np.array(r["head_ms"]) * 1e-3
+    flops_alg = 4.0 * rows * wl.H * wl.V
+    flops_exec = 6.0 * rows * wl.H * wl.V
+    achieved = flops_alg.sum() / head_s.sum() / 1e12
+    executed = flops_exec.sum() / head_s.sum() / 1e12
+    total_s = r["total_ms"] * 1e-3
+    value = wl.n_tokens * K / total_s
+    log(f"steps: {r['total_ms'] / K:.3f} ms/step, head+CE {head_s.mean() * 1e3:.3f} ms/call, "
+        f"mean scored rows {rows.mean():.0f}, {achieved:.1f} TFLOP/s algorithmic, "
+        f"{executed:.1f} TFLOP/s executed")
+    traffic = None
+    if args.traffic_json and os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            t = json.load(f)
+        if t.get("current"):
+            traffic = t.get("bytes_per_call")
+    roofline = dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic,
+                    kernel="mdlm_fused_head_ce_fwd_bwd",
+                    executed_tflops=executed, executed_frac=executed / PEAK_BF16_TFLOPS,
+                    ms_per_call=float(head_s.mean() * 1e3),
+                    algorithmic_flops_per_call=float(flops_alg.mean()))
+    out = dict(metric=METRIC, value=value, unit="tokens/s", n_gpus=1, steps=K,
+               warmup=args.warmup, ms_per_step=r["total_ms"] / K, higher_is_better=True,
+               scaling="weak", vs_baseline=None, dtype="bf16" if wl.dtype == "bf16" else "f32",
+               data="synthetic",
+               config=dict(workload=wl.name, global_batch=wl.n_docs, seq_len=wl.n_tokens,
+                           H=wl.H, V=wl.V, noise="absorb" if wl.noise == 0 else "uniform",
+                           align="aligned" if r["align"] == 0 else "shifted",
+                           softcap=wl.softcap, eps=wl.eps, seeds=f"0..{K - 1}",
+                           mean_scored_rows=float(rows.mean()), parallelism="none (1 GPU)"),
+               roofline=roofline)
+    if args.bandwidth_tokens:
+        log("timing corruption/compaction bandwidth")
+        out["corrupt_compact_hbm"] = bandwidth(args.bandwidth_tokens, dev)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(inp, rows.mean(), args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+/*
+ * mdlm.h -- C ABI of the masked-diffusion loss library for AMD MI355X (gfx950).
+ *
+ * The library computes the training objective of masked-diffusion language
+ * models on one GPU, in three calls that a trainer makes each step:
+ *
+ *   mdlm_corrupt                 per-document noise level t, then per-token
+ *                                corruption (absorbing mask or uniform ids);
+ *   mdlm_compact_masked          ascending list of scored rows with their
+ *                                targets and 1/p weights;
+ *   mdlm_fused_head_ce_fwd_bwd   frozen LM head + cross-entropy over the full
+ *                                vocabulary, weighted and summed to a scalar
+ *                                loss, plus the gradient with respect to the
+ *                                hidden states, without writing logits to
+ *                                memory.
+ *
+ * The method is defined on these pages:
+ *   - LLaDA-8B-MDLM-LoRA model card, "Training" table, "Objective" row:
+ *     t ~ U(0,1) per sequence, mask probability p = (1 - 1e-3) t + 1e-3,
+ *     cross-entropy on masked tokens divided by p; "LoRA" row: embeddings
+ *     and output layer frozen.
+ *   - diffusiongemma-26B-A4B-it-ALWAYS-THINK, "Finetuning notes": corrupt
+ *     canvas positions with uniform-random vocabulary ids at a per-example
+ *     rate t ~ U(eps, 1) (no mask token); the logit softcap is applied once.
+ *   - Native diffusion language-model training (Axolotl docs): model table
+ *     (aligned vs shifted logits, inverse-time weighted CE), "Attention
+ *     backends" (cumulative document offsets), "Packed training" (documents
+ *     isolated, padding excluded from loss), "Adapters, merging and
+ *     inference" (full-vocabulary CE from hidden states through a plain
+ *     linear head without materialising vocabulary logits).
+ *
+ * Conventions shared by every entry point
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or retains device memory; scratch space is passed
+ *     in as `workspace`.
+ *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL means the default stream).  Outputs are valid once the stream
+ *     reaches the call.  No call synchronises with the host.
+ *   - Host-side argument checks run first.  If one fails the call returns a
+ *     non-zero status, enqueues nothing and records a message readable
+ *     through mdlm_last_error().  Launch failures return MDLM_EHIP.
+ *   - Device-resident data is not inspected on the host.  Preconditions on it
+ *     (cu_seqlens nondecreasing from 0 to n_tokens, token and target ids in
+ *     range) are the caller's responsibility; violating them gives
+ *     unspecified results but never out-of-bounds writes to outputs.
+ *   - Calls hold no global mutable state apart from a thread-local error
+ *     string, and may be made concurrently from several host threads on
+ *     different streams.  Calls on one stream that share a workspace must not
+ *     overlap (they do not on one stream).
+ */
+#ifndef MDLM_H
+#define MDLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  MDLM_OK = 0,
+  MDLM_EINVAL = 1,       /* bad argument (null pointer, size, range, enum) */
+  MDLM_EUNSUPPORTED = 2, /* valid but unsupported shape or dtype           */
+  MDLM_EWORKSPACE = 3,   /* workspace missing or smaller than required     */
+  MDLM_EHIP = 4          /* a HIP runtime call or kernel launch failed     */
+};
+
+/* Noise processes. */
+enum { MDLM_NOISE_ABSORB = 0, MDLM_NOISE_UNIFORM = 1 };
+
+/* Logit alignment.  ALIGNED: the hidden state at position g predicts token g
+ * (Nemotron-Labs-Diffusion).  SHIFTED: the hidden state at g-1 predicts
+ * token g (Dream); a document's first token has no predecessor inside its
+ * document and is never scored. */
+enum { MDLM_ALIGNED = 0, MDLM_SHIFTED = 1 };
+
+/* Element types of `hidden`, `W` and `d_hidden`. */
+enum { MDLM_F32 = 0, MDLM_BF16 = 1 };
+
+/*
+ * mdlm_corrupt -- draw per-document noise levels and corrupt the tokens.
+ *
+ * Defined by: LLaDA-8B-MDLM-LoRA card, Training table, "Objective" row
+ * (absorbing, p = (1 - eps) t + eps with eps = 1e-3); diffusiongemma card,
+ * "Finetuning notes" (uniform ids at rate t ~ U(eps, 1)); Axolotl docs,
+ * "Start with Nemotron 3B" (mask id) and "Packed training" (isolation).
+ *
+ * Random numbers come from Philox4x32-10 (Salmon et al., SC'11) keyed by
+ * (seed mod 2^32, seed >> 32).  For document b, word 0 of the call at counter
+ * (b, 0, 0, 0) gives t_b = (word >> 8) * 2^-24, then in fp64
+ * p_b = eps + (1 - eps) * t_b.  For token g (absolute index into x0), word
+ * (g & 3) of the call at counter (lo32(g >> 2), hi32(g >> 2), 0, 1) decides:
+ * corrupted iff (word >> 8) < ceil(p_b * 2^24), i.e. u < p_b for the 24-bit
+ * uniform u.  A corrupted token becomes mask_id (ABSORB) or
+ * (word2 * rand_vocab) >> 32 with word2 = word (g & 3) at counter
+ * (lo32(g >> 2), hi32(g >> 2), 0, 2) (UNIFORM); a replacement equal to the
+ * clean token still counts as corrupted.
+ *
+ *   x0          [n_tokens] int32, clean tokens of the packed stream.
+ *   n_tokens    >= 0.
+ *   cu_seqlens  [n_docs + 1] int32, cumulative document offsets, cu[0] = 0,
+ *               cu[n_docs] = n_tokens, nondecreasing (empty documents
+ *               allowed).  n_tokens must fit in int32 (< 2^31).
+ *   n_docs      >= 1 (or 0 with n_tokens = 0).
+ *   seed        64-bit Philox key.  Same seed -> same draw, bit for bit.
+ *   eps         in (0, 1].  eps = 1 corrupts every token.
+ *   noise       MDLM_NOISE_ABSORB or MDLM_NOISE_UNIFORM.
+ *   mask_id     replacement id under ABSORB (ignored under UNIFORM).
+ *   rand_vocab  >= 1; UNIFORM replacement ids lie in [0, rand_vocab).
+ *   xt          [n_tokens] int32 out, corrupted tokens.
+ *   corrupted   [n_tokens] uint8 out, 1 where corrupted else 0.
+ *   p_doc       [n_docs] double out, p_b.
+ *   doc_counts  [n_docs] int32 out, number of corrupted tokens per document.
+ *   stream      hipStream_t or NULL.
+ * Returns MDLM_OK, MDLM_EINVAL or MDLM_EHIP.
+ */
+int mdlm_corrupt(const int32_t* x0, int64_t n_tokens,
+                 const int32_t* cu_seqlens, int32_t n_docs,
+                 uint64_t seed, double eps,
+                 int32_t noise, int32_t mask_id, int32_t rand_vocab,
+                 int32_t* xt, uint8_t* corrupted, double* p_doc,
+                 int32_t* doc_counts, void* stream);
+
+/*
+ * Workspace bytes that mdlm_compact_masked needs for n_tokens tokens
+ * (per-tile scan state).  Returns 0 only for n_tokens <= 0.
+ */
+size_t mdlm_compact_workspace_bytes(int64_t n_tokens);
+
+/*
+ * mdlm_compact_masked -- list the scored rows in ascending token order.
+ *
+ * Defined by: LLaDA-8B-MDLM-LoRA card, Training table, "Objective" row (CE
+ * on masked tokens divided by p); Axolotl docs, model table (aligned vs
+ * shifted logits) and "Batching" (logits only where a label is scored).
+ *
+ * For every corrupted token g of document b (ascending g):
+ *   ALIGNED: row g, target x0[g];
+ *   SHIFTED: row g - 1, target x0[g], except g = cu_seqlens[b] (skipped);
+ * with weight w = (float)(1.0 / (p_doc[b] * (double)n_tokens)), so that
+ * sum_j w_j CE_j is the 1/p-weighted CE over the call's total token count.
+ *
+ *   corrupted   [n_tokens] uint8 (as written by mdlm_corrupt).
+ *   x0          [n_tokens] int32 clean tokens.
+ *   cu_seqlens  [n_docs + 1] int32, as for mdlm_corrupt.
+ *   p_doc       [n_docs] double, as written by mdlm_corrupt.
+ *   align       MDLM_ALIGNED or MDLM_SHIFTED.
+ *   row_idx     [n_tokens] int32 out (capacity n_tokens; first *n_rows valid).
+ *   tgt         [n_tokens] int32 out.
+ *   w           [n_tokens] float out.
+ *   n_rows      [1] int32 out (device scalar).
+ *   workspace   >= mdlm_compact_workspace_bytes(n_tokens) bytes, 256-byte
+ *               aligned device memory; contents on entry are ignored.
+ * Returns MDLM_OK, MDLM_EINVAL, MDLM_EWORKSPACE or MDLM_EHIP.
+ */
+int mdlm_compact_masked(const uint8_t* corrupted, const int32_t* x0,
+                        int64_t n_tokens, const int32_t* cu_seqlens,
+                        int32_t n_docs, const double* p_doc, int32_t align,
+                        int32_t* row_idx, int32_t* tgt, float* w,
+                        int32_t* n_rows, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes that mdlm_fused_head_ce_fwd_bwd needs for up to max_rows
+ * scored rows of hidden size H against a vocabulary of V.  This is the size
+ * the library prefers; a larger workspace is accepted (and lets the backward
+ * use fewer, larger vocabulary chunks), a smaller one than
+ * mdlm_head_ce_workspace_min_bytes is rejected.  Returns 0 for invalid sizes.
+ */
+size_t mdlm_head_ce_workspace_bytes(int64_t max_rows, int32_t H, int32_t V,
+                                    int32_t dtype);
+size_t mdlm_head_ce_workspace_min_bytes(int64_t max_rows, int32_t H, int32_t V,
+                                        int32_t dtype);
+
+/*
+ * mdlm_fused_head_ce_fwd_bwd -- weighted full-vocabulary cross-entropy of
+ * the scored rows through a frozen linear head, and its gradient.
+ *
+ * Defined by: Axolotl docs, "Adapters, merging and inference" (CE over the
+ * full vocabulary computed from hidden states without materialising
+ * vocabulary logits; plain linear head); LLaDA-8B-MDLM-LoRA card, Training
+ * table (CE on masked tokens divided by p; output layer frozen, so no weight
+ * gradient); diffusiongemma card, "Finetuning notes" (softcap applied once).
+ *
+ * For j < *n_rows, with h = hidden[row_idx[j]] and z = W h (no bias):
+ *   zhat  = softcap > 0 ? softcap * tanh(z / softcap) : z
+ *   CE_j  = logsumexp(zhat) - zhat[tgt[j]]
+ *   loss  = sum_j w[j] * CE_j
+ *   d_hidden[row_idx[j]] = w[j] * ((softmax(zhat) - onehot(tgt[j])) * zhat') W
+ * where zhat' = 1 - (zhat / softcap)^2 (1 without a cap); every other row of
+ * d_hidden is set to exactly zero.  The upstream gradient is taken as 1.
+ * row_idx entries must be distinct (as mdlm_compact_masked produces).
+ *
+ * BF16: inputs bf16, products accumulated in fp32, the per-logit gradient
+ * rounded to bf16 before the second product, d_hidden written as bf16.
+ * F32: everything in fp32.
+ *
+ *   hidden      [n_tokens, H] row-major, element type `dtype`.
+ *   W           [V, H] row-major, element type `dtype`.
+ *   dtype       MDLM_BF16 or MDLM_F32.
+ *   n_tokens    rows of hidden / d_hidden, >= 0.
+ *   H           > 0, a multiple of 64 (else MDLM_EUNSUPPORTED).
+ *   V           > 0.
+ *   row_idx, tgt, w   as written by mdlm_compact_masked (tgt in [0, V)).
+ *   n_rows      [1] int32 device scalar, 0 <= *n_rows <= max_rows.
+ *   max_rows    host bound on *n_rows, 0 <= max_rows <= n_tokens; sizes
+ *               the launch (no host read of *n_rows is ever made).
+ *   softcap     0 = none, else > 0 and finite.
+ *   loss        [1] float out.
+ *   row_ce      [max_rows] float out, CE_j, or NULL.
+ *   d_hidden    [n_tokens, H] out, element type `dtype`, or NULL for a
+ *               forward-only call.
+ *   workspace   device memory, 256-byte aligned, of workspace_bytes >=
+ *               mdlm_head_ce_workspace_min_bytes(max_rows, H, V, dtype).
+ * Returns MDLM_OK, MDLM_EINVAL, MDLM_EUNSUPPORTED, MDLM_EWORKSPACE or
+ * MDLM_EHIP.
+ */
+int mdlm_fused_head_ce_fwd_bwd(const void* hidden, const void* W, int32_t dtype,
+                               int64_t n_tokens, int32_t H, int32_t V,
+                               const int32_t* row_idx, const int32_t* tgt,
+                               const float* w, const int32_t* n_rows,
+                               int64_t max_rows, float softcap, float* loss,
+                               float* row_ce, void* d_hidden, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Message describing the last failure on the calling thread ("" if none).
+ * Valid until the next library call on that thread. */
+const char* mdlm_last_error(void);
+
+/* Library ABI version, (major << 16) | minor. */
+int mdlm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MDLM_H */

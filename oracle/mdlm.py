@@ -65,11 +65,12 @@ def noise_levels(seed, eps, n_docs):
     return t, p, thr
 
 
-def _token_words(seed, n_tokens, tag):
-    """Philox word for each token index g: word (g & 3) of the call at counter
-    (g >> 2 low 32 bits, g >> 2 high 32 bits, 0, tag)."""
+def token_words(seed, n_tokens, tag, start=0):
+    """Philox word for each token index g in [start, start + n_tokens): word
+    (g & 3) of the call at counter (g >> 2 low 32 bits, g >> 2 high 32 bits,
+    0, tag)."""
     k0, k1 = _key(seed)
-    g = np.arange(n_tokens, dtype=np.uint64)
+    g = np.arange(start, start + n_tokens, dtype=np.uint64)
     q = g >> np.uint64(2)
     words = np.stack(philox4x32_10(q & 0xFFFFFFFF, q >> 32, 0, tag, k0, k1), axis=1)
     return words[np.arange(n_tokens), (g & np.uint64(3)).astype(np.int64)]
@@ -101,9 +102,9 @@ def corrupt(x0, cu_seqlens, seed, eps, noise, mask_id, rand_vocab):
     n_docs = cu.shape[0] - 1
     assert cu[0] == 0 and cu[-1] == n
     _, p, thr = noise_levels(seed, eps, n_docs)
-    w1 = _token_words(seed, n, TAG_BERNOULLI).astype(np.int64)
+    w1 = token_words(seed, n, TAG_BERNOULLI).astype(np.int64)
     if noise == NOISE_UNIFORM:
-        w2 = _token_words(seed, n, TAG_REPLACE).astype(np.uint64)
+        w2 = token_words(seed, n, TAG_REPLACE).astype(np.uint64)
     xt = x0.copy()
     corrupted = np.zeros(n, dtype=np.uint8)
     doc_counts = np.zeros(n_docs, dtype=np.int32)

@@ -1,0 +1,66 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the
+library through its C ABI, and bring results back for comparison with the
+oracle."""
+
+import numpy as np
+import torch
+
+from uniform_noise_diffusion_amd import binding as B
+from uniform_noise_diffusion_amd.pipeline import MdlmLossStep
+
+DEV = "cuda:0"
+
+
+def dev_tokens(inp):
+    x0 = torch.from_numpy(np.ascontiguousarray(inp.x0)).to(DEV)
+    cu = torch.from_numpy(np.ascontiguousarray(inp.cu_seqlens)).to(DEV)
+    return x0, cu
+
+
+def dev_float(inp):
+    """hidden and W on the device in the workload's dtype (bf16 from the exact
+    bit patterns, so the device reads the values the oracle reads)."""
+    if inp.wl.dtype == "bf16":
+        h = torch.from_numpy(inp.hidden_bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+        w = torch.from_numpy(inp.W_bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    else:
+        h = torch.from_numpy(inp.hidden).to(DEV)
+        w = torch.from_numpy(inp.W).to(DEV)
+    return h, w
+
+
+def torch_dtype(inp):
+    return torch.bfloat16 if inp.wl.dtype == "bf16" else torch.float32
+
+
+def run_step(inp, seed=None, eps=None, align=None, softcap=None, noise=None,
+             head_workspace_bytes=None, want_grad=True, h=None, W=None):
+    """All three calls on one stream; returns the step object (device buffers)."""
+    wl = inp.wl
+    x0, cu = dev_tokens(inp)
+    if h is None:
+        h, W = dev_float(inp)
+    step = MdlmLossStep(wl.n_tokens, wl.n_docs, wl.H, wl.V, dtype=torch_dtype(inp),
+                        device=DEV, head_workspace_bytes=head_workspace_bytes,
+                        want_grad=want_grad)
+    step.step(x0, cu, h, W, wl.seed if seed is None else seed,
+              wl.eps if eps is None else eps, wl.noise if noise is None else noise,
+              wl.mask_id, wl.rand_vocab, wl.align if align is None else align,
+              wl.softcap if softcap is None else softcap, want_grad=want_grad)
+    torch.cuda.synchronize()
+    return step
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / den) if den > 0 else float(np.linalg.norm(a))
+
+
+def d_hidden_host(step):
+    return host(step.d_hidden.float())

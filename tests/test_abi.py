@@ -1,0 +1,187 @@
+"""Host-side checks of the C ABI: no GPU needed.
+
+The library must load, export every function include/mdlm.h declares, size
+its workspaces, and reject bad arguments on the host (returning a status and
+a message) before enqueueing anything.  Every rejected call below passes null
+data pointers, so nothing could run even if a check were missing.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from uniform_noise_diffusion_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mdlm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mdlm_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libmdlm.so not built")
+    return B.load()
+
+
+def test_header_declares_the_three_entry_points():
+    names = declared_functions()
+    for n in ("mdlm_corrupt", "mdlm_compact_masked", "mdlm_fused_head_ce_fwd_bwd",
+              "mdlm_head_ce_workspace_bytes", "mdlm_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(B.EXPORTED) == set(names)
+
+
+def test_version(lib):
+    assert B.mdlm_version() >> 16 == 1
+
+
+def test_compact_workspace_sizes(lib):
+    assert B.mdlm_compact_workspace_bytes(0) == 0
+    assert B.mdlm_compact_workspace_bytes(1) == 256 + 8
+    assert B.mdlm_compact_workspace_bytes(4096) == 256 + 8
+    assert B.mdlm_compact_workspace_bytes(4097) == 256 + 16
+    assert B.mdlm_compact_workspace_bytes(1 << 27) == 256 + 8 * (1 << 15)
+
+
+def test_head_workspace_sizes(lib):
+    for dt in (B.MDLM_BF16, B.MDLM_F32):
+        lo = B.mdlm_head_ce_workspace_min_bytes(4096, 4096, 126464, dt)
+        hi = B.mdlm_head_ce_workspace_bytes(4096, 4096, 126464, dt)
+        assert 0 < lo <= hi
+    assert B.mdlm_head_ce_workspace_bytes(-1, 64, 64, B.MDLM_BF16) == 0
+    assert B.mdlm_head_ce_workspace_bytes(8, 0, 64, B.MDLM_BF16) == 0
+    assert B.mdlm_head_ce_workspace_bytes(8, 64, 64, 7) == 0
+    # the bf16 gradient chunk grows with the workspace but never beyond V
+    small = B.mdlm_head_ce_workspace_bytes(16, 64, 1000, B.MDLM_BF16)
+    assert small == B.mdlm_head_ce_workspace_bytes(16, 64, 1024, B.MDLM_BF16)
+
+
+NULL = None
+
+
+def corrupt_call(lib, **kw):
+    a = dict(x0=NULL, n=16, cu=NULL, n_docs=1, seed=0, eps=1e-3, noise=0, mask_id=1,
+             rand_vocab=2, xt=NULL, corrupted=NULL, p_doc=NULL, counts=NULL, stream=NULL)
+    a.update(kw)
+    return lib.mdlm_corrupt(a["x0"], a["n"], a["cu"], a["n_docs"], a["seed"], a["eps"],
+                            a["noise"], a["mask_id"], a["rand_vocab"], a["xt"],
+                            a["corrupted"], a["p_doc"], a["counts"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(n=-1), B.MDLM_EINVAL, "n_tokens < 0"),
+    (dict(n=1 << 31), B.MDLM_EUNSUPPORTED, "below 2^31"),
+    (dict(n_docs=-2), B.MDLM_EINVAL, "n_docs < 0"),
+    (dict(n_docs=0), B.MDLM_EINVAL, "n_docs = 0"),
+    (dict(eps=0.0), B.MDLM_EINVAL, "eps"),
+    (dict(eps=1.5), B.MDLM_EINVAL, "eps"),
+    (dict(eps=float("nan")), B.MDLM_EINVAL, "eps"),
+    (dict(noise=5), B.MDLM_EINVAL, "noise"),
+    (dict(noise=1, rand_vocab=0), B.MDLM_EINVAL, "rand_vocab"),
+    (dict(), B.MDLM_EINVAL, "null token pointer"),
+])
+def test_corrupt_rejects_bad_arguments(lib, kw, code, msg):
+    assert corrupt_call(lib, **kw) == code
+    assert msg in B.mdlm_last_error()
+
+
+def compact_call(lib, **kw):
+    a = dict(corrupted=NULL, x0=NULL, n=16, cu=NULL, n_docs=1, p_doc=NULL, align=0,
+             row_idx=NULL, tgt=NULL, w=NULL, n_rows=NULL, ws=NULL, ws_bytes=0, stream=NULL)
+    a.update(kw)
+    return lib.mdlm_compact_masked(a["corrupted"], a["x0"], a["n"], a["cu"], a["n_docs"],
+                                   a["p_doc"], a["align"], a["row_idx"], a["tgt"], a["w"],
+                                   a["n_rows"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(n=-3), B.MDLM_EINVAL, "n_tokens < 0"),
+    (dict(n_docs=0), B.MDLM_EINVAL, "n_docs"),
+    (dict(align=2), B.MDLM_EINVAL, "alignment"),
+    (dict(), B.MDLM_EINVAL, "null n_rows"),
+])
+def test_compact_rejects_bad_arguments(lib, kw, code, msg):
+    assert compact_call(lib, **kw) == code
+    assert msg in B.mdlm_last_error()
+
+
+def head_call(lib, **kw):
+    a = dict(hidden=NULL, W=NULL, dtype=B.MDLM_BF16, n=64, H=128, V=1000, row_idx=NULL,
+             tgt=NULL, w=NULL, n_rows=NULL, max_rows=32, softcap=0.0, loss=NULL, row_ce=NULL,
+             d_hidden=NULL, ws=NULL, ws_bytes=0, stream=NULL)
+    a.update(kw)
+    return lib.mdlm_fused_head_ce_fwd_bwd(
+        a["hidden"], a["W"], a["dtype"], a["n"], a["H"], a["V"], a["row_idx"], a["tgt"],
+        a["w"], a["n_rows"], a["max_rows"], a["softcap"], a["loss"], a["row_ce"],
+        a["d_hidden"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(dtype=3), B.MDLM_EINVAL, "dtype"),
+    (dict(H=0), B.MDLM_EINVAL, "bad sizes"),
+    (dict(V=-1), B.MDLM_EINVAL, "bad sizes"),
+    (dict(max_rows=65), B.MDLM_EINVAL, "max_rows"),
+    (dict(max_rows=-1), B.MDLM_EINVAL, "max_rows"),
+    (dict(H=96), B.MDLM_EUNSUPPORTED, "multiple of 64"),
+    (dict(softcap=-1.0), B.MDLM_EINVAL, "softcap"),
+    (dict(softcap=float("inf")), B.MDLM_EINVAL, "softcap"),
+    (dict(), B.MDLM_EINVAL, "null loss"),
+])
+def test_head_rejects_bad_arguments(lib, kw, code, msg):
+    assert head_call(lib, **kw) == code
+    assert msg in B.mdlm_last_error()
+
+
+def test_head_rejects_missing_or_small_workspace(lib):
+    # the inputs are non-null placeholders that are never dereferenced: the
+    # workspace check fails first and nothing is enqueued
+    fake = ctypes.c_void_p(1 << 20)
+    kw = dict(hidden=fake, W=fake, row_idx=fake, tgt=fake, w=fake, n_rows=fake, loss=fake)
+    assert head_call(lib, **kw) == B.MDLM_EWORKSPACE
+    assert "workspace" in B.mdlm_last_error()
+    need = B.mdlm_head_ce_workspace_min_bytes(32, 128, 1000, B.MDLM_BF16)
+    assert head_call(lib, ws=fake, ws_bytes=need - 1, **kw) == B.MDLM_EWORKSPACE
+    # a misaligned input is rejected before the workspace is looked at
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    kw2 = dict(kw, hidden=odd)
+    assert head_call(lib, **kw2) == B.MDLM_EINVAL
+    assert "16-byte aligned" in B.mdlm_last_error()
+
+
+def test_compact_rejects_small_workspace(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    kw = dict(corrupted=fake, x0=fake, cu=fake, p_doc=fake, row_idx=fake, tgt=fake, w=fake,
+              n_rows=fake)
+    assert compact_call(lib, **kw) == B.MDLM_EWORKSPACE
+    assert compact_call(lib, ws=fake, ws_bytes=10, **kw) == B.MDLM_EWORKSPACE
+
+
+def test_error_is_cleared_by_next_call(lib):
+    assert corrupt_call(lib, eps=0.0) == B.MDLM_EINVAL
+    assert B.mdlm_last_error() != ""
+    assert B.mdlm_compact_workspace_bytes(5) > 0
+    # size queries do not touch the error slot; a failing call overwrites it
+    assert compact_call(lib, align=9) == B.MDLM_EINVAL
+    assert "alignment" in B.mdlm_last_error()
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        B.load()

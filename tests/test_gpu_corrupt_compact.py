@@ -1,0 +1,157 @@
+"""GPU parity of corruption and compaction: bit-exact against the oracle.
+
+Integer outputs (xt, corrupted, doc_counts, row_idx, tgt, n_rows) must be
+identical; p_doc is fp64 and must be identical bit for bit (same operation
+order, no fused multiply-add); w is fp32(1/(p N)) and must be identical.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.mdlm import token_words
+import workloads as WL
+from uniform_noise_diffusion_amd import binding as B
+from uniform_noise_diffusion_amd.pipeline import MdlmLossStep
+
+from gpu_common import DEV, dev_tokens, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, n_docs, max_len, empty=False, V=1000):
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(1, max_len + 1, size=n_docs)
+    if empty:
+        lengths[rng.random(n_docs) < 0.3] = 0
+    cu = np.zeros(n_docs + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    x0 = rng.integers(0, V - 1, size=int(cu[-1])).astype(np.int32)
+    return x0, cu
+
+
+def _gpu_corrupt_compact(x0, cu, seed, eps, noise, mask_id, rand_vocab, align):
+    n, nd = x0.shape[0], cu.shape[0] - 1
+    step = MdlmLossStep(n, nd, 64, 64, device=DEV, head_workspace_bytes=0, want_grad=False)
+    tx0 = torch.from_numpy(x0).to(DEV)
+    tcu = torch.from_numpy(cu).to(DEV)
+    step.corrupt(tx0, tcu, seed, eps, noise, mask_id, rand_vocab)
+    step.compact(tx0, tcu, align)
+    torch.cuda.synchronize()
+    m = int(host(step.n_rows)[0])
+    return dict(xt=host(step.xt), corrupted=host(step.corrupted), p_doc=host(step.p_doc),
+                doc_counts=host(step.doc_counts), n_rows=m, row_idx=host(step.row_idx)[:m],
+                tgt=host(step.tgt)[:m], w=host(step.w)[:m])
+
+
+def _check(x0, cu, seed, eps, noise, mask_id, rand_vocab, align):
+    g = _gpu_corrupt_compact(x0, cu, seed, eps, noise, mask_id, rand_vocab, align)
+    xt, corrupted, p, counts = oracle.corrupt(x0, cu, seed, eps, noise, mask_id, rand_vocab)
+    assert np.array_equal(g["xt"], xt)
+    assert np.array_equal(g["corrupted"], corrupted)
+    assert np.array_equal(g["p_doc"].view(np.uint64), p.view(np.uint64))
+    assert np.array_equal(g["doc_counts"], counts)
+    rows, tgt, w = oracle.compact(corrupted, x0, cu, p, align)
+    assert g["n_rows"] == rows.shape[0]
+    assert np.array_equal(g["row_idx"], rows)
+    assert np.array_equal(g["tgt"], tgt)
+    assert np.array_equal(g["w"].view(np.uint32), w.astype(np.float32).view(np.uint32))
+    return g
+
+
+@pytest.mark.parametrize("noise", [oracle.NOISE_ABSORB, oracle.NOISE_UNIFORM])
+@pytest.mark.parametrize("align", [oracle.ALIGNED, oracle.SHIFTED])
+@pytest.mark.parametrize("seed,n_docs,max_len,empty", [
+    (1, 1, 7, False),        # a single tiny document, N not a multiple of 4
+    (2, 40, 300, True),      # empty documents, several compaction tiles
+    (3, 7, 3000, False),     # documents spanning block boundaries
+    (4, 600, 20, True),      # many short documents per block
+])
+def test_corrupt_compact_bit_exact_small(noise, align, seed, n_docs, max_len, empty):
+    x0, cu = _case(seed, n_docs, max_len, empty)
+    _check(x0, cu, seed * 7919 + 13, 1e-3, noise, 999, 1000, align)
+
+
+@pytest.mark.parametrize("eps", [1.0, 0.5, 1e-6])
+def test_corrupt_eps_extremes(eps):
+    x0, cu = _case(9, 20, 500)
+    g = _check(x0, cu, 2**63 + 12345, eps, oracle.NOISE_ABSORB, 999, 1000, oracle.ALIGNED)
+    if eps == 1.0:
+        assert g["corrupted"].all()
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("align", [oracle.ALIGNED, oracle.SHIFTED])
+def test_corrupt_compact_bit_exact_workloads(k, align):
+    wl = WL.make_workload(k)
+    inp = WL.generate(wl, with_hidden=False, with_head=False)
+    for seed in (wl.seed, 1, 2, 3):
+        _check(inp.x0, inp.cu_seqlens, seed, wl.eps, wl.noise, wl.mask_id, wl.rand_vocab, align)
+
+
+def test_empty_stream():
+    x0 = np.zeros(0, dtype=np.int32)
+    cu = np.zeros(2, dtype=np.int32)
+    g = _gpu_corrupt_compact(x0, cu, 5, 1e-3, 0, 1, 2, oracle.ALIGNED)
+    assert g["n_rows"] == 0
+    _, _, p, counts = oracle.corrupt(x0, cu, 5, 1e-3, 0, 1, 2)
+    assert np.array_equal(g["p_doc"].view(np.uint64), p.view(np.uint64))
+    assert g["doc_counts"][0] == 0
+
+
+def test_shifted_single_token_documents_score_nothing():
+    cu = np.arange(0, 301, dtype=np.int32)
+    x0 = np.arange(300, dtype=np.int32) % 50
+    g = _gpu_corrupt_compact(x0, cu, 3, 1.0, 0, 99, 100, oracle.SHIFTED)
+    assert g["n_rows"] == 0 and g["corrupted"].all()
+
+
+def test_repeat_is_deterministic():
+    x0, cu = _case(11, 50, 400, True)
+    a = _gpu_corrupt_compact(x0, cu, 77, 1e-3, 1, 0, 1000, oracle.SHIFTED)
+    b = _gpu_corrupt_compact(x0, cu, 77, 1e-3, 1, 0, 1000, oracle.SHIFTED)
+    for key in a:
+        assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), key
+
+
+def test_large_stream_sampled():
+    """2^27 tokens in 32,768 documents of 4,096 (the bandwidth shape): the
+    full corruption mask is checked against the oracle on sampled documents
+    and the compaction by its invariants plus sampled rows."""
+    n_docs, L = 32768, 4096
+    n = n_docs * L
+    cu = torch.arange(0, n + 1, L, dtype=torch.int32, device=DEV)
+    x0 = torch.randint(0, 126336, (n,), dtype=torch.int32,
+                       generator=torch.Generator().manual_seed(0)).to(DEV)
+    step = MdlmLossStep(n, n_docs, 64, 64, device=DEV, head_workspace_bytes=0,
+                        want_grad=False)
+    step.corrupt(x0, cu, 42, 1e-3, oracle.NOISE_ABSORB, 126336, 126464)
+    step.compact(x0, cu, oracle.ALIGNED)
+    torch.cuda.synchronize()
+    counts = host(step.doc_counts)
+    m = int(host(step.n_rows)[0])
+    assert m == int(counts.astype(np.int64).sum())
+    # the oracle on sampled documents: the draw of document b depends only on
+    # (seed, b, absolute token index), so a document is checked in place
+    rng = np.random.default_rng(1)
+    x0h = host(x0)
+    corr = host(step.corrupted)
+    xt = host(step.xt)
+    _, p_all, thr_all = oracle.noise_levels(42, 1e-3, n_docs)
+    assert np.array_equal(host(step.p_doc).view(np.uint64), p_all.view(np.uint64))
+    for b in rng.choice(n_docs, size=6, replace=False):
+        lo, hi = b * L, (b + 1) * L
+        wsub = token_words(42, L, oracle.mdlm.TAG_BERNOULLI, start=lo)
+        exp = ((wsub >> 8) < thr_all[b]).astype(np.uint8)
+        assert np.array_equal(corr[lo:hi], exp)
+        assert np.array_equal(xt[lo:hi], np.where(exp == 1, 126336, x0h[lo:hi]))
+    # compaction: rows ascending, exactly the corrupted positions
+    rows = host(step.row_idx)[:m]
+    assert np.array_equal(rows, np.flatnonzero(corr))
+    tg = host(step.tgt)[:m]
+    assert np.array_equal(tg, x0h[rows])
+    w = host(step.w)[:m]
+    doc = rows // L
+    assert np.array_equal(w.view(np.uint32),
+                          (1.0 / (p_all[doc] * float(n))).astype(np.float32).view(np.uint32))

@@ -1,0 +1,18 @@
+"""Masked-diffusion LM loss on AMD MI355X (gfx950).
+
+The HIP library libmdlm.so (C ABI in include/mdlm.h) implements per-document
+noise levels, corruption, ordered compaction of scored rows and the fused
+frozen-head + cross-entropy forward and backward.  `binding` exposes its
+entry points under the same names; `pipeline` owns the buffers of one step.
+"""
+
+from .binding import (  # noqa: F401
+    MdlmError,
+    MDLM_OK, MDLM_EINVAL, MDLM_EUNSUPPORTED, MDLM_EWORKSPACE, MDLM_EHIP,
+    MDLM_NOISE_ABSORB, MDLM_NOISE_UNIFORM, MDLM_ALIGNED, MDLM_SHIFTED,
+    MDLM_F32, MDLM_BF16,
+    mdlm_corrupt, mdlm_compact_workspace_bytes, mdlm_compact_masked,
+    mdlm_head_ce_workspace_bytes, mdlm_head_ce_workspace_min_bytes,
+    mdlm_fused_head_ce_fwd_bwd, mdlm_last_error, mdlm_version,
+)
+from .pipeline import MdlmLossStep  # noqa: F401

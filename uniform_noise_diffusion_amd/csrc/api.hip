@@ -1,0 +1,169 @@
+// C ABI entry points: host-side argument checks, then launches on the
+// caller's stream.  A failed check returns before anything is enqueued.
+#include "mdlm_internal.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+namespace mdlm {
+namespace {
+thread_local char g_error[512];
+}
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_error[0] = '\0'; }
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MDLM_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return MDLM_OK;
+}
+
+}  // namespace mdlm
+
+using namespace mdlm;
+
+extern "C" {
+
+int mdlm_version(void) { return (1 << 16) | 0; }
+
+const char* mdlm_last_error(void) { return g_error; }
+
+int mdlm_corrupt(const int32_t* x0, int64_t n_tokens, const int32_t* cu_seqlens,
+                 int32_t n_docs, uint64_t seed, double eps, int32_t noise, int32_t mask_id,
+                 int32_t rand_vocab, int32_t* xt, uint8_t* corrupted, double* p_doc,
+                 int32_t* doc_counts, void* stream) {
+  clear_error();
+  if (n_tokens < 0) return fail(MDLM_EINVAL, "mdlm_corrupt: n_tokens < 0");
+  if (n_tokens > INT32_MAX)
+    return fail(MDLM_EUNSUPPORTED, "mdlm_corrupt: n_tokens must be below 2^31");
+  if (n_docs < 0) return fail(MDLM_EINVAL, "mdlm_corrupt: n_docs < 0");
+  if (n_docs == 0 && n_tokens > 0)
+    return fail(MDLM_EINVAL, "mdlm_corrupt: tokens given but n_docs = 0");
+  if (!(eps > 0.0 && eps <= 1.0)) return fail(MDLM_EINVAL, "mdlm_corrupt: eps must lie in (0, 1]");
+  if (noise != MDLM_NOISE_ABSORB && noise != MDLM_NOISE_UNIFORM)
+    return fail(MDLM_EINVAL, "mdlm_corrupt: unknown noise mode %d", noise);
+  if (noise == MDLM_NOISE_UNIFORM && rand_vocab < 1)
+    return fail(MDLM_EINVAL, "mdlm_corrupt: rand_vocab must be >= 1");
+  if (n_tokens > 0 && (!x0 || !xt || !corrupted))
+    return fail(MDLM_EINVAL, "mdlm_corrupt: null token pointer");
+  if (n_docs > 0 && (!cu_seqlens || !p_doc || !doc_counts))
+    return fail(MDLM_EINVAL, "mdlm_corrupt: null document pointer");
+  if (launch_corrupt(x0, n_tokens, cu_seqlens, n_docs, seed, eps, noise, mask_id, rand_vocab,
+                     xt, corrupted, p_doc, doc_counts,
+                     reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return check_launch("mdlm_corrupt");
+  return MDLM_OK;
+}
+
+size_t mdlm_compact_workspace_bytes(int64_t n_tokens) {
+  return compact_workspace_bytes(n_tokens);
+}
+
+int mdlm_compact_masked(const uint8_t* corrupted, const int32_t* x0, int64_t n_tokens,
+                        const int32_t* cu_seqlens, int32_t n_docs, const double* p_doc,
+                        int32_t align, int32_t* row_idx, int32_t* tgt, float* w,
+                        int32_t* n_rows, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  clear_error();
+  if (n_tokens < 0) return fail(MDLM_EINVAL, "mdlm_compact_masked: n_tokens < 0");
+  if (n_tokens > INT32_MAX)
+    return fail(MDLM_EUNSUPPORTED, "mdlm_compact_masked: n_tokens must be below 2^31");
+  if (n_docs < 0 || (n_docs == 0 && n_tokens > 0))
+    return fail(MDLM_EINVAL, "mdlm_compact_masked: bad n_docs %d", n_docs);
+  if (align != MDLM_ALIGNED && align != MDLM_SHIFTED)
+    return fail(MDLM_EINVAL, "mdlm_compact_masked: unknown alignment %d", align);
+  if (!n_rows) return fail(MDLM_EINVAL, "mdlm_compact_masked: null n_rows");
+  if (n_tokens > 0 && (!corrupted || !x0 || !cu_seqlens || !p_doc || !row_idx || !tgt || !w))
+    return fail(MDLM_EINVAL, "mdlm_compact_masked: null pointer");
+  const size_t need = compact_workspace_bytes(n_tokens);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MDLM_EWORKSPACE, "mdlm_compact_masked: workspace of %zu bytes, need %zu",
+                workspace_bytes, need);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 8) != 0)
+    return fail(MDLM_EINVAL, "mdlm_compact_masked: workspace must be 8-byte aligned");
+  if (launch_compact(corrupted, x0, n_tokens, cu_seqlens, n_docs, p_doc, align, row_idx, tgt,
+                     w, n_rows, workspace, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return check_launch("mdlm_compact_masked");
+  return MDLM_OK;
+}
+
+static bool head_sizes_ok(int64_t max_rows, int32_t H, int32_t V, int32_t dtype) {
+  return max_rows >= 0 && max_rows <= INT32_MAX && H > 0 && V > 0 &&
+         (dtype == MDLM_F32 || dtype == MDLM_BF16);
+}
+
+size_t mdlm_head_ce_workspace_bytes(int64_t max_rows, int32_t H, int32_t V, int32_t dtype) {
+  if (!head_sizes_ok(max_rows, H, V, dtype)) return 0;
+  return head_ce_workspace_bytes(max_rows, H, V, dtype, false);
+}
+
+size_t mdlm_head_ce_workspace_min_bytes(int64_t max_rows, int32_t H, int32_t V,
+                                        int32_t dtype) {
+  if (!head_sizes_ok(max_rows, H, V, dtype)) return 0;
+  return head_ce_workspace_bytes(max_rows, H, V, dtype, true);
+}
+
+int mdlm_fused_head_ce_fwd_bwd(const void* hidden, const void* W, int32_t dtype,
+                               int64_t n_tokens, int32_t H, int32_t V,
+                               const int32_t* row_idx, const int32_t* tgt, const float* w,
+                               const int32_t* n_rows, int64_t max_rows, float softcap,
+                               float* loss, float* row_ce, void* d_hidden, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* fn = "mdlm_fused_head_ce_fwd_bwd";
+  if (dtype != MDLM_F32 && dtype != MDLM_BF16)
+    return fail(MDLM_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (n_tokens < 0 || H <= 0 || V <= 0)
+    return fail(MDLM_EINVAL, "%s: bad sizes n_tokens=%lld H=%d V=%d", fn, (long long)n_tokens,
+                H, V);
+  if (max_rows < 0 || max_rows > n_tokens)
+    return fail(MDLM_EINVAL, "%s: max_rows must lie in [0, n_tokens]", fn);
+  if (n_tokens > INT32_MAX) return fail(MDLM_EUNSUPPORTED, "%s: n_tokens must be below 2^31", fn);
+  if (H % 64 != 0) return fail(MDLM_EUNSUPPORTED, "%s: H = %d is not a multiple of 64", fn, H);
+  if (!(softcap >= 0.f) || !isfinite(softcap))
+    return fail(MDLM_EINVAL, "%s: softcap must be finite and >= 0", fn);
+  if (!loss) return fail(MDLM_EINVAL, "%s: null loss", fn);
+  if (max_rows > 0 && (!hidden || !W || !row_idx || !tgt || !w || !n_rows))
+    return fail(MDLM_EINVAL, "%s: null input pointer", fn);
+  if (dtype == MDLM_BF16 && max_rows > 0 &&
+      ((reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(W)) % 16) != 0)
+    return fail(MDLM_EINVAL, "%s: hidden and W must be 16-byte aligned", fn);
+  const size_t need = max_rows > 0 ? head_ce_workspace_bytes(max_rows, H, V, dtype, true) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MDLM_EWORKSPACE, "%s: workspace of %zu bytes, need at least %zu", fn,
+                workspace_bytes, need);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 256) != 0)
+    return fail(MDLM_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  HeadCeArgs a;
+  a.hidden = hidden;
+  a.W = W;
+  a.dtype = dtype;
+  a.n_tokens = n_tokens;
+  a.H = H;
+  a.V = V;
+  a.row_idx = row_idx;
+  a.tgt = tgt;
+  a.w = w;
+  a.n_rows = n_rows;
+  a.max_rows = max_rows;
+  a.softcap = softcap;
+  a.loss = loss;
+  a.row_ce = row_ce;
+  a.d_hidden = d_hidden;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  if (launch_head_ce(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return check_launch(fn);
+  return MDLM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,101 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "mdlm.h"
+
+namespace mdlm {
+
+// Records a formatted message in the calling thread's error slot and returns
+// `code`.
+int fail(int code, const char* fmt, ...);
+void clear_error();
+// Maps the last launch error to MDLM_EHIP (with the kernel's name) or MDLM_OK.
+int check_launch(const char* what);
+
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u;
+constexpr uint32_t kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u;
+constexpr uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw: "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC'11): ten rounds of two 32x32->64 multiplies and xors,
+// the key advanced by the Weyl constants between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kPhiloxW0;
+      k1 += kPhiloxW1;
+    }
+    const uint32_t hi0 = __umulhi(kPhiloxM0, c.x);
+    const uint32_t lo0 = kPhiloxM0 * c.x;
+    const uint32_t hi1 = __umulhi(kPhiloxM1, c.z);
+    const uint32_t lo1 = kPhiloxM1 * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
+// Stream tags carried in counter word 3.
+constexpr uint32_t kTagDocT = 0;
+constexpr uint32_t kTagBernoulli = 1;
+constexpr uint32_t kTagReplace = 2;
+
+// Index of the document holding token g: the b with cu[b] <= g < cu[b+1],
+// searched among documents [lo, hi] (which must contain it).
+__device__ __forceinline__ int find_doc(const int32_t* __restrict__ cu, int lo, int hi,
+                                        int64_t g) {
+  // first i in [lo+1, hi+1] with cu[i] > g, minus one
+  int a = lo + 1, b = hi + 1;
+  while (a < b) {
+    const int mid = (a + b) >> 1;
+    if ((int64_t)cu[mid] > g)
+      b = mid;
+    else
+      a = mid + 1;
+  }
+  return a - 1;
+}
+
+// ---- launchers implemented in the kernel translation units ---------------
+hipError_t launch_corrupt(const int32_t* x0, int64_t n_tokens, const int32_t* cu,
+                          int32_t n_docs, uint64_t seed, double eps, int32_t noise,
+                          int32_t mask_id, int32_t rand_vocab, int32_t* xt,
+                          uint8_t* corrupted, double* p_doc, int32_t* doc_counts,
+                          hipStream_t stream);
+
+size_t compact_workspace_bytes(int64_t n_tokens);
+hipError_t launch_compact(const uint8_t* corrupted, const int32_t* x0, int64_t n_tokens,
+                          const int32_t* cu, int32_t n_docs, const double* p_doc,
+                          int32_t align, int32_t* row_idx, int32_t* tgt, float* w,
+                          int32_t* n_rows, void* workspace, hipStream_t stream);
+
+struct HeadCeArgs {
+  const void* hidden;
+  const void* W;
+  int32_t dtype;
+  int64_t n_tokens;
+  int32_t H;
+  int32_t V;
+  const int32_t* row_idx;
+  const int32_t* tgt;
+  const float* w;
+  const int32_t* n_rows;
+  int64_t max_rows;
+  float softcap;
+  float* loss;
+  float* row_ce;
+  void* d_hidden;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+size_t head_ce_workspace_bytes(int64_t max_rows, int32_t H, int32_t V, int32_t dtype,
+                               bool minimal);
+hipError_t launch_head_ce(const HeadCeArgs& a, hipStream_t stream);
+
+}  // namespace mdlm
