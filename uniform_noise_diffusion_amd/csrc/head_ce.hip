@@ -8,22 +8,23 @@
 //
 // Pipeline for M scored rows (M lives on the device; grids are persistent and
 // read it there):
-//   1. logits_kernel<fwd>: z = W h over 256x128 (vocab x row) tiles, K = H,
-//      on bf16 MFMA with fp32 accumulation, operands staged through LDS.  The
-//      epilogue caps, takes each row's (max, sum 2^(s-max)) over the tile's
-//      256 vocabulary entries and picks the target logit.  Logits never leave
-//      registers.
+//   1. logits_kernel<fwd>: z = W h over 256 x 256 (vocab x row) tiles, K = H,
+//      on bf16 MFMA with fp32 accumulation.  Operands go from global memory
+//      straight into a two-stage LDS ring (no register staging), two waves per
+//      SIMD.  The epilogue caps, takes each row's (max, sum 2^(s-max)) over the
+//      tile's 256 vocabulary entries and picks the target logit.  Logits never
+//      leave registers.
 //   2. merge_kernel: per row, combine the per-tile partials into the
 //      log-sum-exp and CE; per-block sums of w * CE in fp64.
 //   3. loss_kernel: fixed-order sum of the block sums -> loss.
-//   4. (gradient) for each vocabulary chunk [v0, v1):
-//      logits_kernel<grad> recomputes the chunk's tiles and writes
-//      G = w (softmax - onehot) zhat' as bf16 into a bounded workspace;
-//      dh_kernel accumulates dH += G W over the chunk (tiles of 128 rows x 256
-//      hidden columns, whole tiles per workgroup, the leftover tiles split
-//      along K), dh_fixup_kernel sums the split tiles in a fixed order.
+//   4. (gradient) for each vocabulary chunk [v0, v1) (one chunk unless the
+//      workspace is small): logits_kernel<grad> recomputes the tiles and
+//      writes G = w (softmax - onehot) zhat' as bf16; dh_kernel forms
+//      dH = G W over 256 x 256 (row x hidden) tiles with W read through LDS
+//      transpose loads, split along the vocabulary into S slices chosen on
+//      the device so that the tile x slice units fill the grid.
 //   5. zero_kernel + scatter_kernel: d_hidden = 0, then d_hidden[row_idx[j]]
-//      = dH[j] in the hidden dtype.
+//      = sum of the S slices of dH[j], in the hidden dtype.
 #include "mdlm_internal.h"
 
 #include <math.h>
@@ -37,19 +38,25 @@ typedef __bf16 bf16_t;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;         // reduction and utility kernels
+constexpr int kGemmThreads = 512;     // MFMA kernels: 8 waves, two per SIMD
+constexpr int kTile = 256;            // rows of each operand tile
 constexpr int kBK = 64;               // K elements per main-loop step
-constexpr int kStride = kBK + 8;      // LDS row pitch in elements (144 bytes)
-constexpr int kLA = 256, kLB = 128;   // logits tile: vocab rows x scored rows
-constexpr int kDA = 128, kDB = 256;   // dH tile: scored rows x hidden columns
+constexpr int kKRow = kBK * 2;        // bytes per row of a K-major tile (128)
+constexpr int kNRow = kTile * 2;      // bytes per row of an N-major tile (512)
+constexpr int kOpBytes = kTile * kKRow;       // one operand tile: 32 KiB
+constexpr int kStageBytes = 2 * kOpBytes;     // A + B: 64 KiB
+constexpr int kLdsBytes = 2 * kStageBytes;    // two stages: 128 KiB
+constexpr int kMaxSplit = 8;          // K-splits of the dH product
 constexpr int kMergeRows = 4;         // rows per merge block (one per wave)
 constexpr int kGrid = 256;            // persistent grid: one workgroup per CU
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr size_t kAlign = 256;
+static_assert(kTile * kKRow == 64 * kNRow, "K-major and N-major tiles share a size");
 
-static_assert((kLA + kLB) == (kDA + kDB), "both GEMMs share one LDS footprint");
-constexpr int kLdsElems = 2 * (kLA + kLB) * kStride;
+#define MDLM_LDS __attribute__((address_space(3)))
+#define MDLM_GLOBAL __attribute__((address_space(1)))
 
 __device__ __forceinline__ int logical_block() {
   // Consecutive logical ids on one XCD: the hardware hands workgroup b to XCD
@@ -74,32 +81,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// One 64-deep K step of a wave's (32*NI) x (32*NJ) tile.  `as`/`bs` point at
-// this lane's operand row in LDS (row = wave base + lane % 32, column offset
-// (lane / 32) * 8).  Blocks whose mask bit is clear (rows past the end) are
-// skipped; the masks are wave-uniform.
-template <int NI, int NJ>
-__device__ __forceinline__ void mma_step(const bf16_t* __restrict__ as,
-                                         const bf16_t* __restrict__ bs,
-                                         f32x16 (&acc)[NI][NJ], uint32_t imask,
-                                         uint32_t jmask) {
-#pragma unroll
-  for (int kk = 0; kk < kBK / 16; ++kk) {
-    bf16x8 af[NI], bfr[NJ];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      af[i] = *reinterpret_cast<const bf16x8*>(as + i * 32 * kStride + kk * 16);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      bfr[j] = *reinterpret_cast<const bf16x8*>(bs + j * 32 * kStride + kk * 16);
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        if (((imask >> i) & 1u) && ((jmask >> j) & 1u))
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0,
-                                                              0);
-  }
+// LDS swizzles.  K-major tile rows are 128 bytes (eight 16-byte chunks); the
+// chunk index is xor-ed with a function of the row so that 16 consecutive
+// rows read at one logical chunk hit distinct banks.  N-major tile rows are
+// 512 bytes; their chunk index is xor-ed with 4 * (row % 4), which spreads the
+// four rows of a transpose read over distinct banks.
+__device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz_n(int r) { return (r & 3) << 2; }
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16 * l (the LDS address must be uniform across the wave).
+__device__ __forceinline__ void g2l(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds((const MDLM_GLOBAL void*)g, (MDLM_LDS void*)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short shortx4;
+
+// Four K-consecutive bf16 of one column of an N-major LDS tile (transpose
+// read): in each group of 16 lanes, lane j names row j / 4 of a 4 x 16 block
+// (its columns 4 (j % 4) .. 4 (j % 4) + 3); lane i then receives column i of
+// that block, rows 0..3.
+__device__ __forceinline__ shortx4 ds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MDLM_LDS shortx4*)(p));
 }
 
 // --------------------------------------------------------------------------
@@ -120,80 +125,65 @@ struct LogitsArgs {
   float inv_softcap;
   int v_begin;  // vocabulary range of this launch
   int v_end;
-  float2* partial;  // fwd: [ceil(V/kLA)][max_rows] (max, sum) in log2 units
+  float2* partial;  // fwd: [ceil(V/kTile)][max_rows] (max, sum) in log2 units
   float* ztgt;      // fwd: [max_rows] capped target logit
   const float* lse; // grad: [max_rows]
   bf16_t* G;        // grad: [max_rows][ldg], column = v - v_begin
   int64_t ldg;
 };
 
+// Tile of 256 vocabulary rows (operand A, rows of W) by 256 scored rows
+// (operand B, rows of hidden gathered through row_idx), K = H.  Wave w owns
+// vocabulary rows 128 (w % 2) .. +127 and scored rows 64 (w / 2) .. +63: a
+// 4 x 2 grid of 32 x 32 MFMA blocks.
 template <bool kGrad>
-__global__ void __launch_bounds__(kThreads, 1) logits_kernel(LogitsArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[kLdsElems];
-  __shared__ float2 red[2][kLB];
+__global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
+  // the two stages are separate objects so that the compiler can tell a
+  // prefetch into one from reads of the other
+  __shared__ __attribute__((aligned(1024))) char smem0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem1[kStageBytes];
+  __shared__ float2 red[2][kTile];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wa = wave >> 1, wb = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wa = wave & 1, wb = wave >> 1;
   const int n_rows = min(*a.n_rows, a.max_rows);
-  const int n_mt = (n_rows + kLB - 1) / kLB;
-  const int n_vt = (a.v_end - a.v_begin + kLA - 1) / kLA;
+  const int n_mt = (n_rows + kTile - 1) / kTile;
+  const int n_vt = (a.v_end - a.v_begin + kTile - 1) / kTile;
   const int64_t n_tiles = (int64_t)n_mt * n_vt;
   const int KT = a.H / kBK;
   const bool capped = a.softcap > 0.f;
-  const int kc = tid & 7, rsub = tid >> 3;
+
+  // fragment-read offsets (bytes within a stage)
+  const int fx = swz_k(lane & 15), khalf = lane >> 5;
+  const int a_off = (wa * 128 + (lane & 31)) * kKRow;
+  const int b_off = kOpBytes + (wb * 64 + (lane & 31)) * kKRow;
+  // direct-load roles: load q of this wave fills tile rows 8 (4 wave + q) ..
+  // +7; lane l supplies row 8 (4 wave + q) + l / 8 at physical chunk l % 8
+  const int lrow = lane >> 3, lphys = lane & 7;
 
   for (int64_t t = logical_block(); t < n_tiles; t += gridDim.x) {
     const int vt = (int)(t / n_mt), mt = (int)(t % n_mt);
-    const int v0 = a.v_begin + vt * kLA;
-    const int m0 = mt * kLB;
+    const int v0 = a.v_begin + vt * kTile;
+    const int m0 = mt * kTile;
 
-    // ---- operand row pointers for this thread's global loads -------------
-    const bf16_t* a_ptr = a.W + (int64_t)(v0 + rsub) * a.H + kc * 8;
-    uint32_t a_ok = 0;
+    const bf16_t* ga[4];
+    const bf16_t* gb[4];
 #pragma unroll
-    for (int c = 0; c < kLA / 32; ++c)
-      if (v0 + 32 * c + rsub < a.v_end) a_ok |= 1u << c;
-    const bf16_t* b_ptr[kLB / 32];
-#pragma unroll
-    for (int c = 0; c < kLB / 32; ++c) {
-      const int m = m0 + 32 * c + rsub;
-      b_ptr[c] = nullptr;
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * (4 * wave + q) + lrow;
+      const int c = lphys ^ swz_k(r);
+      // rows past the end read a valid row; their results are discarded
+      const int v = (v0 + r < a.v_end) ? v0 + r : a.v_begin;
+      ga[q] = a.W + (int64_t)v * a.H + 8 * c;
+      const int m = m0 + r;
+      int64_t row = 0;
       if (m < n_rows) {
-        const int64_t r = a.row_idx[m];
-        if (r >= 0 && r < a.n_tokens) b_ptr[c] = a.hidden + r * a.H + kc * 8;
+        row = a.row_idx[m];
+        if (row < 0 || row >= a.n_tokens) row = 0;
       }
+      gb[q] = a.hidden + row * a.H + 8 * c;
     }
-    uint32_t imask = 0, jmask = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (v0 + wa * 128 + 32 * i < a.v_end) imask |= 1u << i;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (m0 + wb * 64 + 32 * j < n_rows) jmask |= 1u << j;
-
-    uint4 ra[kLA / 32], rb[kLB / 32];
-    auto gload = [&](int k0) {
-#pragma unroll
-      for (int c = 0; c < kLA / 32; ++c)
-        ra[c] = ((a_ok >> c) & 1u)
-                    ? *reinterpret_cast<const uint4*>(a_ptr + (int64_t)c * 32 * a.H + k0)
-                    : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int c = 0; c < kLB / 32; ++c)
-        rb[c] = b_ptr[c] ? *reinterpret_cast<const uint4*>(b_ptr[c] + k0)
-                         : make_uint4(0, 0, 0, 0);
-    };
-    auto lstore = [&](int buf) {
-      bf16_t* as = lds + buf * (kLA + kLB) * kStride;
-      bf16_t* bs = as + kLA * kStride;
-#pragma unroll
-      for (int c = 0; c < kLA / 32; ++c)
-        *reinterpret_cast<uint4*>(as + (32 * c + rsub) * kStride + kc * 8) = ra[c];
-#pragma unroll
-      for (int c = 0; c < kLB / 32; ++c)
-        *reinterpret_cast<uint4*>(bs + (32 * c + rsub) * kStride + kc * 8) = rb[c];
-    };
-
     f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -201,18 +191,48 @@ __global__ void __launch_bounds__(kThreads, 1) logits_kernel(LogitsArgs a) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    auto issue = [&](char* stage, int k0) {
+      char* sa = stage + (4 * wave) * 1024;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        g2l(ga[q] + k0, sa + q * 1024);
+        g2l(gb[q] + k0, sa + kOpBytes + q * 1024);
+      }
+    };
+    auto compute = [&](const char* base) {
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int coff = ((2 * kk + khalf) ^ fx) * 16;
+        bf16x8 af[4], bfr[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8*>(base + b_off + j * 32 * kKRow + coff);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0,
+                                                                0);
+      }
+    };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      if (kt + 1 < KT) gload((kt + 1) * kBK);
-      const bf16_t* base = lds + (kt & 1) * (kLA + kLB) * kStride;
-      const bf16_t* as = base + (wa * 128 + (lane & 31)) * kStride + (lane >> 5) * 8;
-      const bf16_t* bs = base + (kLA + wb * 64 + (lane & 31)) * kStride + (lane >> 5) * 8;
-      mma_step<4, 2>(as, bs, acc, imask, jmask);
-      if (kt + 1 < KT) lstore((kt + 1) & 1);
+    __syncthreads();  // the previous tile is done with both stages
+    issue(smem0, 0);
+    // two K steps per trip so that each access names its stage statically
+    for (int kt = 0; kt < KT; kt += 2) {
+      wait_vmem();
       __syncthreads();
+      if (kt + 1 < KT) issue(smem1, (kt + 1) * kBK);
+      compute(smem0);
+      if (kt + 1 < KT) {
+        wait_vmem();
+        __syncthreads();
+        if (kt + 2 < KT) issue(smem0, (kt + 2) * kBK);
+        compute(smem1);
+      }
     }
 
     // ---- epilogue ---------------------------------------------------------
@@ -286,7 +306,7 @@ __global__ void __launch_bounds__(kThreads, 1) logits_kernel(LogitsArgs a) {
             if (mx != -INFINITY)
               s = p0.y * __builtin_amdgcn_exp2f(p0.x - mx) +
                   p1.y * __builtin_amdgcn_exp2f(p1.x - mx);
-            a.partial[(int64_t)((v0 - a.v_begin) / kLA) * a.max_rows + m] = make_float2(mx, s);
+            a.partial[(int64_t)((v0 - a.v_begin) / kTile) * a.max_rows + m] = make_float2(mx, s);
           }
         }
       }
@@ -295,7 +315,7 @@ __global__ void __launch_bounds__(kThreads, 1) logits_kernel(LogitsArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// dH += G W over one vocabulary chunk.
+// dH = G W over one vocabulary chunk, split along K into S slices.
 // --------------------------------------------------------------------------
 struct DhArgs {
   const bf16_t* G;
@@ -306,180 +326,160 @@ struct DhArgs {
   int v_end;
   const int32_t* n_rows;
   int max_rows;
-  float* dh;     // [max_rows][H] fp32
-  float* slots;  // [kGrid][kDA * kDB] split-tile partials
+  float* part;  // [kMaxSplit][max_rows][H] fp32, slice s in part + s * max_rows * H
   int accumulate;
 };
 
-// The 8x8 transpose of bf16 held as 8 rows of uint4 (row = v, 8 h each) into
-// 8 rows of uint4 (row = h, 8 v each).
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    uint32_t o[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t lo_row = reinterpret_cast<const uint32_t*>(&in[2 * q])[s >> 1];
-      const uint32_t hi_row = reinterpret_cast<const uint32_t*>(&in[2 * q + 1])[s >> 1];
-      o[q] = (s & 1) ? ((lo_row >> 16) | (hi_row & 0xFFFF0000u))
-                     : ((lo_row & 0xFFFFu) | (hi_row << 16));
+// Number of K-slices: the fewest (up to kMaxSplit) that keep the grid busy,
+// judged by the share of workgroup slots the tile x slice units fill.
+__host__ __device__ __forceinline__ int dh_splits(int64_t tiles, int grid, int ki) {
+  if (tiles <= 0) return 1;
+  int best = 1;
+  double best_eff = 0.0;
+  for (int s = 1; s <= kMaxSplit && s <= ki; ++s) {
+    const int64_t units = tiles * s;
+    const int64_t rounds = (units + grid - 1) / grid;
+    const double eff = (double)units / (double)(rounds * grid);
+    if (eff > best_eff + 0.02) {
+      best = s;
+      best_eff = eff;
     }
-    out[s] = make_uint4(o[0], o[1], o[2], o[3]);
   }
+  return best;
 }
 
-__device__ __forceinline__ void dh_tile(const DhArgs& a, bf16_t* lds, int n_rows, int n_mt,
-                                        int64_t tile, int k_beg, int k_end, float* out,
-                                        int64_t ld_out, bool to_slot) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wa = wave >> 1, wb = wave & 1;
-  const int mt = (int)(tile % n_mt), ht = (int)(tile / n_mt);
-  const int m0 = mt * kDA, h0 = ht * kDB;
-  const int kc = tid & 7, rsub = tid >> 3;
-  // A = G rows (K contiguous)
-  const bf16_t* a_ptr = a.G + (int64_t)(m0 + rsub) * a.ldg + kc * 8;
-  uint32_t a_ok = 0;
-#pragma unroll
-  for (int c = 0; c < kDA / 32; ++c)
-    if (m0 + 32 * c + rsub < n_rows) a_ok |= 1u << c;
-  // B = W^T: this thread loads an 8 (v) x 8 (h) block and transposes it
-  const int gv = lane & 7, gh = 8 * wave + (lane >> 3);
-  const bool h_ok = h0 + 8 * gh < a.H;
-  const bf16_t* b_ptr = a.W + (int64_t)(a.v_begin + 8 * gv) * a.H + h0 + 8 * gh;
-  uint32_t imask = 0, jmask = 0;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    if (m0 + wa * 64 + 32 * i < n_rows) imask |= 1u << i;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (h0 + wb * 128 + 32 * j < a.H) jmask |= 1u << j;
-
-  uint4 ra[kDA / 32], rb[8];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int c = 0; c < kDA / 32; ++c)
-      ra[c] = ((a_ok >> c) & 1u)
-                  ? *reinterpret_cast<const uint4*>(a_ptr + (int64_t)c * 32 * a.ldg + k0)
-                  : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const bool ok = h_ok && (a.v_begin + k0 + 8 * gv + r < a.v_end);
-      rb[r] = ok ? *reinterpret_cast<const uint4*>(b_ptr + (int64_t)(k0 + r) * a.H)
-                 : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&](int buf) {
-    bf16_t* as = lds + buf * (kDA + kDB) * kStride;
-    bf16_t* bs = as + kDA * kStride;
-#pragma unroll
-    for (int c = 0; c < kDA / 32; ++c)
-      *reinterpret_cast<uint4*>(as + (32 * c + rsub) * kStride + kc * 8) = ra[c];
-    uint4 tr[8];
-    transpose8x8(rb, tr);
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      *reinterpret_cast<uint4*>(bs + (8 * gh + s) * kStride + 8 * gv) = tr[s];
-  };
-
-  f32x16 acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  gload(k_beg * kBK);
-  lstore(0);
-  __syncthreads();
-  for (int kt = k_beg; kt < k_end; ++kt) {
-    const int buf = (kt - k_beg) & 1;
-    if (kt + 1 < k_end) gload((kt + 1) * kBK);
-    const bf16_t* base = lds + buf * (kDA + kDB) * kStride;
-    const bf16_t* as = base + (wa * 64 + (lane & 31)) * kStride + (lane >> 5) * 8;
-    const bf16_t* bs = base + (kDA + wb * 128 + (lane & 31)) * kStride + (lane >> 5) * 8;
-    mma_step<2, 4>(as, bs, acc, imask, jmask);
-    if (kt + 1 < k_end) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // acc element e of block (i, j) on lane l: row m0 + wa*64 + 32i + 8(e/4) +
-  // 4(l/32) + e%4, column h0 + wb*128 + 32j + l%32.
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int rl = wa * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int cl = wb * 128 + 32 * j + (lane & 31);
-        if (to_slot) {
-          out[(int64_t)rl * kDB + cl] = acc[i][j][e];
-        } else if (m0 + rl < n_rows && h0 + cl < a.H) {
-          float* p = out + (int64_t)(m0 + rl) * ld_out + h0 + cl;
-          *p = a.accumulate ? *p + acc[i][j][e] : acc[i][j][e];
-        }
-      }
-    }
-}
-
-__device__ __forceinline__ void dh_schedule(int n_rows, int H, int v_begin, int v_end,
-                                            int* n_mt, int64_t* T, int* KI, int64_t* full,
-                                            int* R, int* SB) {
-  *n_mt = (n_rows + kDA - 1) / kDA;
-  const int n_ht = (H + kDB - 1) / kDB;
-  *T = (int64_t)(*n_mt) * n_ht;
-  *KI = (v_end - v_begin + kBK - 1) / kBK;
-  *full = *T / gridDim.x;
-  *R = (int)(*T % gridDim.x);
-  *SB = *R ? (int)gridDim.x / *R : 0;
-  if (*SB > *KI) *SB = *KI;
-}
-
-__global__ void __launch_bounds__(kThreads, 1) dh_kernel(DhArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t lds[kLdsElems];
+// Tile of 256 scored rows (operand A, rows of G) by 256 hidden columns
+// (operand B, columns of W read through transpose loads), K = vocabulary.
+// Wave w owns rows 128 (w % 2) .. +127 and columns 64 (w / 2) .. +63.
+__global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem1[kStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wa = wave & 1, wb = wave >> 1;
   const int n_rows = min(*a.n_rows, a.max_rows);
-  int n_mt, KI, R, SB;
-  int64_t T, full;
-  dh_schedule(n_rows, a.H, a.v_begin, a.v_end, &n_mt, &T, &KI, &full, &R, &SB);
-  if (T == 0 || KI == 0) return;
-  const int lw = logical_block();
-  // whole tiles: every workgroup runs the same K range at the same time
-  for (int64_t r = 0; r < full; ++r)
-    dh_tile(a, lds, n_rows, n_mt, r * gridDim.x + lw, 0, KI, a.dh, a.H, false);
-  // leftover tiles, each split into SB K-slices
-  if (R && lw < R * SB) {
-    const int64_t tile = full * gridDim.x + lw / SB;
-    const int s = lw % SB;
-    const int kb = (int)((int64_t)KI * s / SB), ke = (int)((int64_t)KI * (s + 1) / SB);
-    dh_tile(a, lds, n_rows, n_mt, tile, kb, ke, a.slots + (int64_t)lw * kDA * kDB, kDB, true);
-  }
-}
-
-// Sums the K-slices of each leftover tile in slice order and adds them to dH.
-__global__ void __launch_bounds__(kThreads) dh_fixup_kernel(DhArgs a, int grid) {
-  const int n_rows = min(*a.n_rows, a.max_rows);
-  const int n_mt = (n_rows + kDA - 1) / kDA;
-  const int n_ht = (a.H + kDB - 1) / kDB;
+  const int n_mt = (n_rows + kTile - 1) / kTile;
+  const int n_ht = (a.H + kTile - 1) / kTile;
   const int64_t T = (int64_t)n_mt * n_ht;
   const int KI = (a.v_end - a.v_begin + kBK - 1) / kBK;
   if (T == 0 || KI == 0) return;
-  const int64_t full = T / grid;
-  const int R = (int)(T % grid);
-  int SB = R ? grid / R : 0;
-  if (SB > KI) SB = KI;
-  const int r = blockIdx.x;
-  if (r >= R) return;
-  const int64_t tile = full * grid + r;
-  const int mt = (int)(tile % n_mt), ht = (int)(tile / n_mt);
-  const int m0 = mt * kDA, h0 = ht * kDB;
-  for (int idx = threadIdx.x; idx < kDA * kDB; idx += kThreads) {
-    const int rl = idx / kDB, cl = idx % kDB;
-    if (m0 + rl >= n_rows || h0 + cl >= a.H) continue;
-    float s = 0.f;
-    for (int k = 0; k < SB; ++k) s += a.slots[(int64_t)(r * SB + k) * kDA * kDB + idx];
-    float* p = a.dh + (int64_t)(m0 + rl) * a.H + h0 + cl;
-    *p = a.accumulate ? *p + s : s;
+  const int S = dh_splits(T, gridDim.x, KI);
+
+  const int fx = swz_k(lane & 15), khalf = lane >> 5;
+  const int a_off = (wa * 128 + (lane & 31)) * kKRow;
+  // transpose-read roles: group g = lane / 16 covers K rows 8 (g / 2) .. +7 of
+  // a 16-deep slice and columns 16 (g % 2) .. +15 of a 32-column block
+  const int jl = lane & 15, grp = lane >> 4;
+  const int tr_row = 8 * (grp >> 1) + (jl >> 2);
+  int b_col_off[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = wb * 64 + 32 * j + 16 * (grp & 1) + 4 * (jl & 3);
+    b_col_off[j] = (((col >> 3) ^ swz_n(tr_row)) * 16) + ((col >> 2) & 1) * 8;
+  }
+  const int lrow = lane >> 3, lphys = lane & 7;       // K-major loads
+  const int nrow = lane >> 5, nphys = lane & 31;      // N-major loads
+
+  const int64_t units = T * S;
+  for (int64_t u = logical_block(); u < units; u += gridDim.x) {
+    const int s = (int)(u / T);
+    const int64_t tile = u % T;
+    const int mt = (int)(tile % n_mt), ht = (int)(tile / n_mt);
+    const int m0 = mt * kTile, h0 = ht * kTile;
+    const int kb = (int)((int64_t)KI * s / S), ke = (int)((int64_t)KI * (s + 1) / S);
+
+    const bf16_t* ga[4];
+    const bf16_t* gb[4];
+    int brow[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 8 * (4 * wave + q) + lrow;
+      const int c = lphys ^ swz_k(r);
+      const int m = (m0 + r < n_rows) ? m0 + r : 0;
+      ga[q] = a.G + (int64_t)m * a.ldg + 8 * c;
+      const int rn = 2 * (4 * wave + q) + nrow;
+      const int cn = nphys ^ swz_n(rn);
+      const int h = (h0 + 8 * cn < a.H) ? h0 + 8 * cn : 0;
+      gb[q] = a.W + h;
+      brow[q] = rn;
+    }
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    auto issue = [&](char* stage, int k0) {
+      char* sa = stage + (4 * wave) * 1024;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        g2l(ga[q] + k0, sa + q * 1024);
+        int v = a.v_begin + k0 + brow[q];
+        if (v >= a.v_end) v = a.v_begin;  // G is zero there
+        g2l(gb[q] + (int64_t)v * a.H, sa + kOpBytes + q * 1024);
+      }
+    };
+    auto compute = [&](const char* base) {
+      const char* bb = base + kOpBytes;
+#pragma unroll
+      for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int coff = ((2 * kk + khalf) ^ fx) * 16;
+        bf16x8 af[4], bfr[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
+        const char* brow_p = bb + (16 * kk + tr_row) * kNRow;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const shortx4 lo = ds_read_tr(brow_p + b_col_off[j]);
+          const shortx4 hi = ds_read_tr(brow_p + 4 * kNRow + b_col_off[j]);
+          const short v8 __attribute__((__vector_size__(16))) = {lo[0], lo[1], lo[2], lo[3],
+                                                                 hi[0], hi[1], hi[2], hi[3]};
+          bfr[j] = __builtin_bit_cast(bf16x8, v8);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0,
+                                                                0);
+      }
+    };
+
+    __syncthreads();
+    issue(smem0, kb * kBK);
+    for (int kt = kb; kt < ke; kt += 2) {
+      wait_vmem();
+      __syncthreads();
+      if (kt + 1 < ke) issue(smem1, (kt + 1) * kBK);
+      compute(smem0);
+      if (kt + 1 < ke) {
+        wait_vmem();
+        __syncthreads();
+        if (kt + 2 < ke) issue(smem0, (kt + 2) * kBK);
+        compute(smem1);
+      }
+    }
+
+    // acc element e of block (i, j) on lane l: row m0 + wa*128 + 32i + 8(e/4)
+    // + 4(l/32) + e%4, column h0 + wb*64 + 32j + l%32.
+    float* out = a.part + (int64_t)s * a.max_rows * a.H;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + wa * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (m >= n_rows) continue;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int h = h0 + wb * 64 + 32 * j + (lane & 31);
+          if (h < a.H) {
+            float* p = out + (int64_t)m * a.H + h;
+            *p = a.accumulate ? *p + acc[i][j][e] : acc[i][j][e];
+          }
+        }
+      }
   }
 }
 
@@ -564,18 +564,24 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return (bf16_t)x; }
 
-// d_hidden[row_idx[j]] = dH[j] for every scored row j.
+// d_hidden[row_idx[j]] = sum over the K-slices of dH[j], for every scored row.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
-scatter_kernel(const float* __restrict__ dh, int H, const int32_t* __restrict__ row_idx,
-               const int32_t* __restrict__ n_rows_ptr, int max_rows, int64_t n_tokens,
-               T* __restrict__ d_hidden) {
+scatter_kernel(const float* __restrict__ part, int H, int grid, int v_span,
+               const int32_t* __restrict__ row_idx, const int32_t* __restrict__ n_rows_ptr,
+               int max_rows, int64_t n_tokens, T* __restrict__ d_hidden) {
   const int n_rows = min(*n_rows_ptr, max_rows);
+  const int64_t tiles = (int64_t)((n_rows + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
+  const int S = dh_splits(tiles, grid, (v_span + kBK - 1) / kBK);
+  const int64_t slice = (int64_t)max_rows * H;
   for (int j = blockIdx.x; j < n_rows; j += gridDim.x) {
     const int64_t r = row_idx[j];
     if (r < 0 || r >= n_tokens) continue;
-    for (int h = threadIdx.x; h < H; h += kThreads)
-      d_hidden[r * H + h] = from_f32<T>(dh[(int64_t)j * H + h]);
+    for (int h = threadIdx.x; h < H; h += kThreads) {
+      float acc = 0.f;
+      for (int k = 0; k < S; ++k) acc += part[k * slice + (int64_t)j * H + h];
+      d_hidden[r * H + h] = from_f32<T>(acc);
+    }
   }
 }
 
@@ -666,27 +672,24 @@ f32_dh_kernel(F32Args a, float* __restrict__ d_hidden) {
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t partial, ztgt, lse, bsum, dh, slots, G, total;
-  int64_t vc;   // vocabulary chunk width of the gradient pass
-  int64_t ldg;  // row pitch of G in elements
+  size_t partial, ztgt, lse, bsum, part, G, total;
   int n_vt, n_bsum;
 };
 
 // Fixed part of the layout; G gets whatever follows.
 Layout fixed_layout(int64_t max_rows, int H, int V, int dtype, bool grad) {
   Layout L{};
-  const int tile = dtype == MDLM_BF16 ? kLA : kThreads;
-  L.n_vt = (V + tile - 1) / tile;
+  L.n_vt = (V + kTile - 1) / kTile;
   L.n_bsum = (int)((max_rows + kMergeRows - 1) / kMergeRows);
   size_t off = 0;
   L.partial = off; off = align_up(off + (size_t)L.n_vt * max_rows * sizeof(float2));
   L.ztgt = off;    off = align_up(off + (size_t)max_rows * sizeof(float));
   L.lse = off;     off = align_up(off + (size_t)max_rows * sizeof(float));
   L.bsum = off;    off = align_up(off + (size_t)std::max(L.n_bsum, 1) * sizeof(double));
-  L.dh = L.slots = L.G = off;
+  L.part = L.G = off;
   if (grad && dtype == MDLM_BF16) {
-    L.dh = off;    off = align_up(off + (size_t)max_rows * H * sizeof(float));
-    L.slots = off; off = align_up(off + (size_t)kGrid * kDA * kDB * sizeof(float));
+    L.part = off;
+    off = align_up(off + (size_t)kMaxSplit * max_rows * H * sizeof(float));
     L.G = off;
   } else if (grad) {
     L.G = off;
@@ -696,24 +699,17 @@ Layout fixed_layout(int64_t max_rows, int H, int V, int dtype, bool grad) {
   return L;
 }
 
-// The bf16 gradient chunk prefers G to stay near 192 MiB so that it and the
-// matching slice of W can be served from the 256 MiB Infinity Cache.
-constexpr size_t kPreferredGBytes = 192ull << 20;
-
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 }  // namespace
 
+// The preferred workspace holds G for the whole vocabulary, so the gradient
+// runs as one chunk; the minimum holds one 256-wide vocabulary chunk.
 size_t head_ce_workspace_bytes(int64_t max_rows, int32_t H, int32_t V, int32_t dtype,
                                bool minimal) {
   Layout L = fixed_layout(max_rows, H, V, dtype, true);
   if (dtype != MDLM_BF16 || max_rows == 0) return L.total;
-  const int64_t vfull = round_up(V, kLA);
-  int64_t vc = kLA;
-  if (!minimal) {
-    vc = (int64_t)(kPreferredGBytes / ((size_t)max_rows * sizeof(bf16_t))) / kLA * kLA;
-    vc = std::max<int64_t>(kLA, std::min(vc, vfull));
-  }
+  const int64_t vc = minimal ? kTile : round_up(V, kTile);
   return L.total + align_up((size_t)max_rows * vc * sizeof(bf16_t));
 }
 
@@ -769,7 +765,7 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     la.v_end = x.V;
     la.partial = partial;
     la.ztgt = ztgt;
-    logits_kernel<false><<<grid, kThreads, 0, stream>>>(la);
+    logits_kernel<false><<<grid, kGemmThreads, 0, stream>>>(la);
   } else {
     F32Args fa{};
     fa.W = reinterpret_cast<const float*>(x.W);
@@ -819,10 +815,9 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
 
   // bf16 gradient: vocabulary chunks sized by the workspace given
   const size_t g_room = x.workspace_bytes - L.total;
-  int64_t vc = (int64_t)(g_room / ((size_t)max_rows * sizeof(bf16_t))) / kLA * kLA;
-  vc = std::min<int64_t>(vc, round_up(x.V, kLA));
-  float* dh = reinterpret_cast<float*>(ws + L.dh);
-  float* slots = reinterpret_cast<float*>(ws + L.slots);
+  int64_t vc = (int64_t)(g_room / ((size_t)max_rows * sizeof(bf16_t))) / kTile * kTile;
+  vc = std::min<int64_t>(vc, round_up(x.V, kTile));
+  float* part = reinterpret_cast<float*>(ws + L.part);
   bf16_t* G = reinterpret_cast<bf16_t*>(ws + L.G);
 
   LogitsArgs la{};
@@ -849,25 +844,25 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   da.H = x.H;
   da.n_rows = x.n_rows;
   da.max_rows = (int)max_rows;
-  da.dh = dh;
-  da.slots = slots;
+  da.part = part;
 
   int chunk = 0;
   for (int64_t v0 = 0; v0 < x.V; v0 += vc, ++chunk) {
     const int v1 = (int)std::min<int64_t>(x.V, v0 + vc);
     la.v_begin = (int)v0;
     la.v_end = v1;
-    logits_kernel<true><<<grid, kThreads, 0, stream>>>(la);
+    logits_kernel<true><<<grid, kGemmThreads, 0, stream>>>(la);
     da.v_begin = (int)v0;
     da.v_end = v1;
     da.accumulate = chunk > 0;
-    dh_kernel<<<grid, kThreads, 0, stream>>>(da);
-    dh_fixup_kernel<<<grid, kThreads, 0, stream>>>(da, grid);
+    dh_kernel<<<grid, kGemmThreads, 0, stream>>>(da);
   }
-  if (x.dtype == MDLM_BF16)
-    scatter_kernel<bf16_t><<<(unsigned)std::min<int64_t>(max_rows, 65536), kThreads, 0, stream>>>(
-        dh, x.H, x.row_idx, x.n_rows, (int)max_rows, x.n_tokens,
-        reinterpret_cast<bf16_t*>(x.d_hidden));
+  // every chunk uses the same slice count (it depends on the chunk width only
+  // through the number of K steps, which is at least kMaxSplit unless the
+  // chunk is narrower than 512)
+  scatter_kernel<bf16_t><<<(unsigned)std::min<int64_t>(max_rows, 65536), kThreads, 0, stream>>>(
+      part, x.H, grid, (int)std::min<int64_t>(vc, x.V), x.row_idx, x.n_rows, (int)max_rows,
+      x.n_tokens, reinterpret_cast<bf16_t*>(x.d_hidden));
   return hipGetLastError();
 }
 
