@@ -51,6 +51,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--bandwidth-tokens", type=int, default=1 << 27,
                    help="tokens of the corruption/compaction bandwidth run (0 = skip)")
+    p.add_argument("--calibrate-copy", type=int, default=0,
+                   help="before timing, copy this many MiB device-to-device once, so "
+                        "counter runs can scale their byte counts by a known transfer")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles",
                                                           "head_ce_traffic.json"),
                    help="measured HBM traffic of the fused call, if current")
@@ -205,6 +208,14 @@ def main():
     wl = WL.make_workload(args.workload)
     log(f"generating workload {wl.name}: N={wl.n_tokens} H={wl.H} V={wl.V}")
     inp = WL.generate(wl)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {n} bytes done")
+        del src, dst
     log("timing steps")
     r = gpu_steps(args, inp, dev)
     K = args.steps

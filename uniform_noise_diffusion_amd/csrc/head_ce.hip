@@ -39,7 +39,17 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr int kThreads = 256;         // reduction and utility kernels
-constexpr int kGemmThreads = 512;     // MFMA kernels: 8 waves, two per SIMD
+#ifndef MDLM_GEMM_WAVES
+#define MDLM_GEMM_WAVES 8
+#endif
+// MFMA kernels: kWaves waves over a 256 x 256 tile.  Each wave owns 128 rows
+// of operand A and 256 / (kWaves / 2) rows of operand B (kNJ 32-row blocks).
+constexpr int kWaves = MDLM_GEMM_WAVES;
+constexpr int kGemmThreads = 64 * kWaves;
+constexpr int kNJ = 16 / kWaves;          // 32-row B blocks per wave
+constexpr int kWB = 32 * kNJ;             // B rows per wave
+constexpr int kLoads = 32 / kWaves;       // 1 KiB loads per operand per wave
+static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
 constexpr int kTile = 256;            // rows of each operand tile
 constexpr int kBK = 64;               // K elements per main-loop step
 constexpr int kKRow = kBK * 2;        // bytes per row of a K-major tile (128)
@@ -89,13 +99,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ int swz_k(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz_n(int r) { return (r & 3) << 2; }
 
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds + 16 * l (the LDS address must be uniform across the wave).
-__device__ __forceinline__ void g2l(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds((const MDLM_GLOBAL void*)g, (MDLM_LDS void*)lds, 16, 0, 0);
+// 16 bytes per lane from a buffer into LDS: lane l's bytes land at lds + 16 l.
+// Offsets past the resource's byte count read as zeros (the descriptor's
+// range check), so tiles that overhang an operand need no clamping.
+__device__ __forceinline__ void buf2l(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MDLM_LDS void*)lds, 16, voff, soff, 0, 0);
+}
+
+// Raw (unformatted) buffer descriptor over `bytes` bytes from `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t capped = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)capped,
+                                           0x00020000);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Keeps the scheduler from moving instructions across this point: used so the
+// next stage's loads are issued at the top of a K step (a full step ahead of
+// their use) and the step's MFMAs finish before the next wait.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short shortx4;
 
@@ -132,10 +156,35 @@ struct LogitsArgs {
   int64_t ldg;
 };
 
+// Software-pipelined MFMA block for one 64-deep K step of a wave's 128 x 128
+// tile: the fragments of 16-deep slice kk+1 are read from LDS while the 16
+// MFMAs of slice kk run.  `ra` reads the A fragments of a slice, `rb` the B
+// fragments.
+template <typename ReadA, typename ReadB>
+__device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB rb) {
+  bf16x8 af[2][4], bfr[2][kNJ];
+  ra(0, af[0]);
+  rb(0, bfr[0]);
+#pragma unroll
+  for (int kk = 0; kk < kBK / 16; ++kk) {
+    const int cur = kk & 1;
+    if (kk + 1 < kBK / 16) {
+      ra(kk + 1, af[cur ^ 1]);
+      rb(kk + 1, bfr[cur ^ 1]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
+                                                            0, 0, 0);
+  }
+}
+
 // Tile of 256 vocabulary rows (operand A, rows of W) by 256 scored rows
 // (operand B, rows of hidden gathered through row_idx), K = H.  Wave w owns
-// vocabulary rows 128 (w % 2) .. +127 and scored rows 64 (w / 2) .. +63: a
-// 4 x 2 grid of 32 x 32 MFMA blocks.
+// vocabulary rows 128 (w % 2) .. +127 and scored rows kWB (w / 2) .. +kWB-1:
+// a 4 x kNJ grid of 32 x 32 MFMA blocks.
 template <bool kGrad>
 __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
   // the two stages are separate objects so that the compiler can tell a
@@ -157,9 +206,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
   // fragment-read offsets (bytes within a stage)
   const int fx = swz_k(lane & 15), khalf = lane >> 5;
   const int a_off = (wa * 128 + (lane & 31)) * kKRow;
-  const int b_off = kOpBytes + (wb * 64 + (lane & 31)) * kKRow;
-  // direct-load roles: load q of this wave fills tile rows 8 (4 wave + q) ..
-  // +7; lane l supplies row 8 (4 wave + q) + l / 8 at physical chunk l % 8
+  const int b_off = kOpBytes + (wb * kWB + (lane & 31)) * kKRow;
+  // direct-load roles: load q (0..kLoads-1) of this wave fills tile rows
+  // 8 (kLoads wave + q) .. +7; lane l supplies row 8 (kLoads wave + q) + l / 8
+  // at physical chunk l % 8
   const int lrow = lane >> 3, lphys = lane & 7;
 
   for (int64_t t = logical_block(); t < n_tiles; t += gridDim.x) {
@@ -167,85 +217,102 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
     const int v0 = a.v_begin + vt * kTile;
     const int m0 = mt * kTile;
 
-    const bf16_t* ga[4];
-    const bf16_t* gb[4];
+    // A: rows v0.. of W, read as one buffer that ends at v_end (rows past it
+    // read as zeros).  Row r = 8 (kLoads wave + q) + l / 8 has r % 8 = l / 8
+    // and (r / 8) % 2 = q % 2, so its swizzled chunk depends on q only through
+    // q % 2: two lane offsets serve all loads, the rest is scalar.
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(a.W + (int64_t)v0 * a.H, (int64_t)(a.v_end - v0) * a.H * 2);
+    uint32_t a_voff[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 8 * (4 * wave + q) + lrow;
-      const int c = lphys ^ swz_k(r);
-      // rows past the end read a valid row; their results are discarded
-      const int v = (v0 + r < a.v_end) ? v0 + r : a.v_begin;
-      ga[q] = a.W + (int64_t)v * a.H + 8 * c;
+    for (int par = 0; par < 2; ++par)
+      a_voff[par] = (uint32_t)((lrow * a.H + 8 * (lphys ^ lrow ^ par)) * 2);
+    // B: gathered rows of hidden; rows past n_rows point past the buffer
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.hidden, a.n_tokens * a.H * 2);
+    uint32_t b_voff[kLoads];
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+      const int r = 8 * (kLoads * wave + q) + lrow;
       const int m = m0 + r;
-      int64_t row = 0;
+      int64_t row = -1;
       if (m < n_rows) {
         row = a.row_idx[m];
-        if (row < 0 || row >= a.n_tokens) row = 0;
+        if (row >= a.n_tokens) row = -1;
       }
-      gb[q] = a.hidden + row * a.H + 8 * c;
+      b_voff[q] = row < 0 ? 0xFFFFFFF0u
+                          : (uint32_t)((row * a.H + 8 * (lphys ^ swz_k(r))) * 2);
     }
-    f32x16 acc[4][2];
+    f32x16 acc[4][kNJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < kNJ; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     auto issue = [&](char* stage, int k0) {
-      char* sa = stage + (4 * wave) * 1024;
+      char* sa = stage + (kLoads * wave) * 1024;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        g2l(ga[q] + k0, sa + q * 1024);
-        g2l(gb[q] + k0, sa + kOpBytes + q * 1024);
+      for (int q = 0; q < kLoads; ++q) {
+        buf2l(ra, sa + q * 1024, a_voff[q & 1],
+              (uint32_t)((8 * (kLoads * wave + q) * a.H + k0) * 2));
+        buf2l(rb, sa + kOpBytes + q * 1024, b_voff[q], (uint32_t)(k0 * 2));
       }
     };
     auto compute = [&](const char* base) {
+      mma_k64(
+          acc,
+          [&](int kk, bf16x8(&f)[4]) {
+            const int coff = ((2 * kk + khalf) ^ fx) * 16;
 #pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int coff = ((2 * kk + khalf) ^ fx) * 16;
-        bf16x8 af[4], bfr[2];
+            for (int i = 0; i < 4; ++i)
+              f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
+          },
+          [&](int kk, bf16x8(&f)[kNJ]) {
+            const int coff = ((2 * kk + khalf) ^ fx) * 16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8*>(base + b_off + j * 32 * kKRow + coff);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0,
-                                                                0);
-      }
+            for (int j = 0; j < kNJ; ++j)
+              f[j] = *reinterpret_cast<const bf16x8*>(base + b_off + j * 32 * kKRow + coff);
+          });
     };
 
     __syncthreads();  // the previous tile is done with both stages
     issue(smem0, 0);
-    // two K steps per trip so that each access names its stage statically
-    for (int kt = 0; kt < KT; kt += 2) {
+    // two K steps per trip so that each access names its stage statically;
+    // an odd last step runs after the loop
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
       wait_vmem();
       __syncthreads();
-      if (kt + 1 < KT) issue(smem1, (kt + 1) * kBK);
+      issue(smem1, (kt + 1) * kBK);
+      sched_fence();
       compute(smem0);
-      if (kt + 1 < KT) {
-        wait_vmem();
-        __syncthreads();
-        if (kt + 2 < KT) issue(smem0, (kt + 2) * kBK);
-        compute(smem1);
-      }
+      sched_fence();
+      wait_vmem();
+      __syncthreads();
+      if (kt + 2 < KT) issue(smem0, (kt + 2) * kBK);
+      sched_fence();
+      compute(smem1);
+      sched_fence();
+    }
+    if (kt < KT) {
+      wait_vmem();
+      __syncthreads();
+      compute(smem0);
     }
 
     // ---- epilogue ---------------------------------------------------------
     // Accumulator element e of block (i, j) on lane l holds vocabulary entry
-    // v0 + wa*128 + 32i + 8(e/4) + 4(l/32) + e%4 for row m0 + wb*64 + 32j + l%32.
+    // v0 + wa*128 + 32i + 8(e/4) + 4(l/32) + e%4 for row m0 + wb*kWB + 32j + l%32.
     const int vl = v0 + wa * 128 + 4 * (lane >> 5);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = m0 + wb * 64 + 32 * j + (lane & 31);
+    for (int j = 0; j < kNJ; ++j) {
+      const int m = m0 + wb * kWB + 32 * j + (lane & 31);
       const bool mvalid = m < n_rows;
       const int tg = mvalid ? a.tgt[m] : -1;
       if (!kGrad) {
-        float mx = -INFINITY;
+        float sv[4][16];
+        float mx = -INFINITY, zt = 0.f;
+        bool hit = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -253,21 +320,22 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
             const int v = vl + 32 * i + 8 * (e >> 2) + (e & 3);
             float zc = acc[i][j][e], dc;
             if (capped) zc = softcap_fwd(zc, a.softcap, a.inv_softcap, &dc);
-            if (mvalid && v == tg) a.ztgt[m] = zc;
-            const float s = v < a.v_end ? zc * kLog2e : -INFINITY;
-            acc[i][j][e] = s;
-            mx = fmaxf(mx, s);
+            zt = (v == tg) ? zc : zt;
+            hit |= (v == tg);
+            sv[i][e] = v < a.v_end ? zc * kLog2e : -INFINITY;
+            mx = fmaxf(mx, sv[i][e]);
           }
+        if (mvalid && hit) a.ztgt[m] = zt;
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         float sum = 0.f;
         if (mx != -INFINITY) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(acc[i][j][e] - mx);
+            for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(sv[i][e] - mx);
         }
         sum += __shfl_xor(sum, 32, 64);
-        if (lane < 32) red[wa][wb * 64 + 32 * j + lane] = make_float2(mx, sum);
+        if (lane < 32) red[wa][wb * kWB + 32 * j + lane] = make_float2(mx, sum);
       } else if (mvalid) {
         const float lse2 = a.lse[m] * kLog2e;
         const float wm = a.w[m];
@@ -296,8 +364,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
       __syncthreads();
       if (wa == 0) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = wb * 64 + 32 * j + (lane & 31);
+        for (int j = 0; j < kNJ; ++j) {
+          const int col = wb * kWB + 32 * j + (lane & 31);
           const int m = m0 + col;
           if (lane < 32 && m < n_rows) {
             const float2 p0 = red[0][col], p1 = red[1][col];
@@ -350,7 +418,7 @@ __host__ __device__ __forceinline__ int dh_splits(int64_t tiles, int grid, int k
 
 // Tile of 256 scored rows (operand A, rows of G) by 256 hidden columns
 // (operand B, columns of W read through transpose loads), K = vocabulary.
-// Wave w owns rows 128 (w % 2) .. +127 and columns 64 (w / 2) .. +63.
+// Wave w owns rows 128 (w % 2) .. +127 and columns kWB (w / 2) .. +kWB-1.
 __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char smem1[kStageBytes];
@@ -371,10 +439,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
   // a 16-deep slice and columns 16 (g % 2) .. +15 of a 32-column block
   const int jl = lane & 15, grp = lane >> 4;
   const int tr_row = 8 * (grp >> 1) + (jl >> 2);
-  int b_col_off[2];
+  int b_col_off[kNJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = wb * 64 + 32 * j + 16 * (grp & 1) + 4 * (jl & 3);
+  for (int j = 0; j < kNJ; ++j) {
+    const int col = wb * kWB + 32 * j + 16 * (grp & 1) + 4 * (jl & 3);
     b_col_off[j] = (((col >> 3) ^ swz_n(tr_row)) * 16) + ((col >> 2) & 1) * 8;
   }
   const int lrow = lane >> 3, lphys = lane & 7;       // K-major loads
@@ -388,82 +456,88 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
     const int m0 = mt * kTile, h0 = ht * kTile;
     const int kb = (int)((int64_t)KI * s / S), ke = (int)((int64_t)KI * (s + 1) / S);
 
-    const bf16_t* ga[4];
-    const bf16_t* gb[4];
-    int brow[4];
+    // load q (0..kLoads-1): K-major rows 8 (kLoads wave + q) + l / 8 of G,
+    // N-major rows 2 (kLoads wave + q) + l / 32 of W.  Both swizzles depend on q only through
+    // q % 2, so two lane offsets per operand serve all loads.  G rows past
+    // n_rows and W rows past v_end read as zeros.
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(a.G + (int64_t)m0 * a.ldg, (int64_t)(n_rows - m0) * a.ldg * 2);
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(a.W + (int64_t)a.v_begin * a.H, (int64_t)(a.v_end - a.v_begin) * a.H * 2);
+    uint32_t a_voff[2], b_voff[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int r = 8 * (4 * wave + q) + lrow;
-      const int c = lphys ^ swz_k(r);
-      const int m = (m0 + r < n_rows) ? m0 + r : 0;
-      ga[q] = a.G + (int64_t)m * a.ldg + 8 * c;
-      const int rn = 2 * (4 * wave + q) + nrow;
-      const int cn = nphys ^ swz_n(rn);
-      const int h = (h0 + 8 * cn < a.H) ? h0 + 8 * cn : 0;
-      gb[q] = a.W + h;
-      brow[q] = rn;
+    for (int par = 0; par < 2; ++par) {
+      a_voff[par] = (uint32_t)((lrow * a.ldg + 8 * (lphys ^ lrow ^ par)) * 2);
+      const int cn = nphys ^ swz_n(2 * par + nrow);
+      // columns past H read the following row (finite values whose products
+      // land only in columns that are never stored)
+      b_voff[par] = (uint32_t)((nrow * a.H + h0 + 8 * cn) * 2);
     }
-    f32x16 acc[4][2];
+    f32x16 acc[4][kNJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < kNJ; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     auto issue = [&](char* stage, int k0) {
-      char* sa = stage + (4 * wave) * 1024;
+      char* sa = stage + (kLoads * wave) * 1024;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        g2l(ga[q] + k0, sa + q * 1024);
-        int v = a.v_begin + k0 + brow[q];
-        if (v >= a.v_end) v = a.v_begin;  // G is zero there
-        g2l(gb[q] + (int64_t)v * a.H, sa + kOpBytes + q * 1024);
+      for (int q = 0; q < kLoads; ++q) {
+        buf2l(ra, sa + q * 1024, a_voff[q & 1],
+              (uint32_t)((8 * (kLoads * wave + q) * a.ldg + k0) * 2));
+        buf2l(rb, sa + kOpBytes + q * 1024, b_voff[q & 1],
+              (uint32_t)((2 * (kLoads * wave + q) + k0) * a.H * 2));
       }
     };
     auto compute = [&](const char* base) {
       const char* bb = base + kOpBytes;
+      mma_k64(
+          acc,
+          [&](int kk, bf16x8(&f)[4]) {
+            const int coff = ((2 * kk + khalf) ^ fx) * 16;
 #pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
-        const int coff = ((2 * kk + khalf) ^ fx) * 16;
-        bf16x8 af[4], bfr[2];
+            for (int i = 0; i < 4; ++i)
+              f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
+          },
+          [&](int kk, bf16x8(&f)[kNJ]) {
+            const char* brow_p = bb + (16 * kk + tr_row) * kNRow;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
-        const char* brow_p = bb + (16 * kk + tr_row) * kNRow;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const shortx4 lo = ds_read_tr(brow_p + b_col_off[j]);
-          const shortx4 hi = ds_read_tr(brow_p + 4 * kNRow + b_col_off[j]);
-          const short v8 __attribute__((__vector_size__(16))) = {lo[0], lo[1], lo[2], lo[3],
-                                                                 hi[0], hi[1], hi[2], hi[3]};
-          bfr[j] = __builtin_bit_cast(bf16x8, v8);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0,
-                                                                0);
-      }
+            for (int j = 0; j < kNJ; ++j) {
+              const shortx4 lo = ds_read_tr(brow_p + b_col_off[j]);
+              const shortx4 hi = ds_read_tr(brow_p + 4 * kNRow + b_col_off[j]);
+              const short v8 __attribute__((__vector_size__(16))) = {
+                  lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              f[j] = __builtin_bit_cast(bf16x8, v8);
+            }
+          });
     };
 
     __syncthreads();
     issue(smem0, kb * kBK);
-    for (int kt = kb; kt < ke; kt += 2) {
+    int kt = kb;
+    for (; kt + 2 <= ke; kt += 2) {
       wait_vmem();
       __syncthreads();
-      if (kt + 1 < ke) issue(smem1, (kt + 1) * kBK);
+      issue(smem1, (kt + 1) * kBK);
+      sched_fence();
       compute(smem0);
-      if (kt + 1 < ke) {
-        wait_vmem();
-        __syncthreads();
-        if (kt + 2 < ke) issue(smem0, (kt + 2) * kBK);
-        compute(smem1);
-      }
+      sched_fence();
+      wait_vmem();
+      __syncthreads();
+      if (kt + 2 < ke) issue(smem0, (kt + 2) * kBK);
+      sched_fence();
+      compute(smem1);
+      sched_fence();
+    }
+    if (kt < ke) {
+      wait_vmem();
+      __syncthreads();
+      compute(smem0);
     }
 
     // acc element e of block (i, j) on lane l: row m0 + wa*128 + 32i + 8(e/4)
-    // + 4(l/32) + e%4, column h0 + wb*64 + 32j + l%32.
+    // + 4(l/32) + e%4, column h0 + wb*kWB + 32j + l%32.
     float* out = a.part + (int64_t)s * a.max_rows * a.H;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -472,8 +546,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
         const int m = m0 + wa * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (m >= n_rows) continue;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int h = h0 + wb * 64 + 32 * j + (lane & 31);
+        for (int j = 0; j < kNJ; ++j) {
+          const int h = h0 + wb * kWB + 32 * j + (lane & 31);
           if (h < a.H) {
             float* p = out + (int64_t)m * a.H + h;
             *p = a.accumulate ? *p + acc[i][j][e] : acc[i][j][e];
