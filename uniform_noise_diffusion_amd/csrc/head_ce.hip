@@ -160,7 +160,7 @@ struct LogitsArgs {
 // tile: the fragments of 16-deep slice kk+1 are read from LDS while the 16
 // MFMAs of slice kk run.  `ra` reads the A fragments of a slice, `rb` the B
 // fragments.
-template <typename ReadA, typename ReadB>
+template <int kReads, typename ReadA, typename ReadB>
 __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB rb) {
   bf16x8 af[2][4], bfr[2][kNJ];
   ra(0, af[0]);
@@ -179,6 +179,23 @@ __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB r
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
                                                             0, 0, 0);
   }
+  // Issue order for the scheduler: the first slice's reads, then for each
+  // slice but the last its MFMAs alternated one for one with the next slice's
+  // reads, then the last slice's MFMAs.  `kReads` counts LDS read
+  // instructions per slice (transpose reads count twice).
+  constexpr int kMfma = 4 * kNJ;
+  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+#pragma unroll
+  for (int kk = 0; kk + 1 < kBK / 16; ++kk) {
+#pragma unroll
+    for (int x = 0; x < kMfma; ++x) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (x < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int x = kMfma; x < kReads; ++x) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
 }
 
 // Tile of 256 vocabulary rows (operand A, rows of W) by 256 scored rows
@@ -259,7 +276,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
       }
     };
     auto compute = [&](const char* base) {
-      mma_k64(
+      mma_k64<4 + kNJ>(
           acc,
           [&](int kk, bf16x8(&f)[4]) {
             const int coff = ((2 * kk + khalf) ^ fx) * 16;
@@ -492,7 +509,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
     };
     auto compute = [&](const char* base) {
       const char* bb = base + kOpBytes;
-      mma_k64(
+      mma_k64<4 + 2 * kNJ>(
           acc,
           [&](int kk, bf16x8(&f)[4]) {
             const int coff = ((2 * kk + khalf) ^ fx) * 16;
