@@ -124,8 +124,9 @@ int mdlm_corrupt(const int32_t* x0, int64_t n_tokens,
                  int32_t* doc_counts, void* stream);
 
 /*
- * Workspace bytes that mdlm_compact_masked needs for n_tokens tokens
- * (per-tile scan state).  Returns 0 only for n_tokens <= 0.
+ * Workspace bytes that mdlm_compact_masked needs for n_tokens tokens (three
+ * 32-bit words per 4096-token tile: its count and its first and last
+ * document).  Returns 0 only for n_tokens <= 0.
  */
 size_t mdlm_compact_workspace_bytes(int64_t n_tokens);
 
@@ -151,8 +152,8 @@ size_t mdlm_compact_workspace_bytes(int64_t n_tokens);
  *   tgt         [n_tokens] int32 out.
  *   w           [n_tokens] float out.
  *   n_rows      [1] int32 out (device scalar).
- *   workspace   >= mdlm_compact_workspace_bytes(n_tokens) bytes, 256-byte
- *               aligned device memory; contents on entry are ignored.
+ *   workspace   >= mdlm_compact_workspace_bytes(n_tokens) bytes of device
+ *               memory, 4-byte aligned; contents on entry are ignored.
  * Returns MDLM_OK, MDLM_EINVAL, MDLM_EWORKSPACE or MDLM_EHIP.
  */
 int mdlm_compact_masked(const uint8_t* corrupted, const int32_t* x0,

@@ -51,11 +51,12 @@ def test_version(lib):
 
 
 def test_compact_workspace_sizes(lib):
+    # three 32-bit words per 4096-token tile
     assert B.mdlm_compact_workspace_bytes(0) == 0
-    assert B.mdlm_compact_workspace_bytes(1) == 256 + 8
-    assert B.mdlm_compact_workspace_bytes(4096) == 256 + 8
-    assert B.mdlm_compact_workspace_bytes(4097) == 256 + 16
-    assert B.mdlm_compact_workspace_bytes(1 << 27) == 256 + 8 * (1 << 15)
+    assert B.mdlm_compact_workspace_bytes(1) == 12
+    assert B.mdlm_compact_workspace_bytes(4096) == 12
+    assert B.mdlm_compact_workspace_bytes(4097) == 24
+    assert B.mdlm_compact_workspace_bytes(1 << 27) == 12 * (1 << 15)
 
 
 def test_head_workspace_sizes(lib):
@@ -164,11 +165,16 @@ def test_head_rejects_missing_or_small_workspace(lib):
 
 
 def test_compact_rejects_small_workspace(lib):
+    # placeholders are never dereferenced: the workspace check fails first
     fake = ctypes.c_void_p(1 << 20)
+    n = 1 << 20
+    need = B.mdlm_compact_workspace_bytes(n)
+    assert need == 12 * (n // 4096)
     kw = dict(corrupted=fake, x0=fake, cu=fake, p_doc=fake, row_idx=fake, tgt=fake, w=fake,
-              n_rows=fake)
+              n_rows=fake, n=n)
     assert compact_call(lib, **kw) == B.MDLM_EWORKSPACE
-    assert compact_call(lib, ws=fake, ws_bytes=10, **kw) == B.MDLM_EWORKSPACE
+    assert compact_call(lib, ws=fake, ws_bytes=need - 1, **kw) == B.MDLM_EWORKSPACE
+    assert "workspace" in B.mdlm_last_error()
 
 
 def test_error_is_cleared_by_next_call(lib):

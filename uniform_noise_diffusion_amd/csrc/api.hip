@@ -88,8 +88,8 @@ int mdlm_compact_masked(const uint8_t* corrupted, const int32_t* x0, int64_t n_t
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(MDLM_EWORKSPACE, "mdlm_compact_masked: workspace of %zu bytes, need %zu",
                 workspace_bytes, need);
-  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 8) != 0)
-    return fail(MDLM_EINVAL, "mdlm_compact_masked: workspace must be 8-byte aligned");
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 4) != 0)
+    return fail(MDLM_EINVAL, "mdlm_compact_masked: workspace must be 4-byte aligned");
   if (launch_compact(corrupted, x0, n_tokens, cu_seqlens, n_docs, p_doc, align, row_idx, tgt,
                      w, n_rows, workspace, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return check_launch("mdlm_compact_masked");

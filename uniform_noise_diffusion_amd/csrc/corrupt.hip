@@ -6,20 +6,21 @@
 // Axolotl diffusion docs, "Packed training" (documents in a packed stream stay
 // isolated, so each draws its own t).
 //
-// Layout: one thread owns 4 consecutive tokens, which is exactly the output of
-// one Philox call per stream, so each token costs a quarter of a call (two
-// quarters under uniform noise).  A block covers 1024 tokens; the documents it
-// touches are found once per block and per-document counts are gathered in LDS
-// before one global atomic per (block, document).
+// Layout: a block covers 4096 tokens in four rounds; in round j thread t owns
+// the 4 consecutive tokens starting at 4 (t + 256 j), exactly the output of one
+// Philox call per stream, and a wave's loads and stores are contiguous.  The
+// documents a block touches are found once by a wave-wide search and their
+// offsets cached in LDS; corrupted counts are summed per wave and document
+// before one LDS atomic, and one global atomic per (block, document).
 #include "mdlm_internal.h"
 
 namespace mdlm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTokPerThread = 4;
-constexpr int kTokPerBlock = kThreads * kTokPerThread;
-constexpr int kLdsDocs = 1024;
+constexpr int kRounds = 4;
+constexpr int kTokPerBlock = kThreads * 4 * kRounds;  // 4096
+constexpr int kLdsDocs = 2048;                        // documents cached per block
 
 __global__ void __launch_bounds__(kThreads)
 noise_level_kernel(int32_t n_docs, uint32_t k0, uint32_t k1, double eps,
@@ -41,6 +42,12 @@ __device__ __forceinline__ uint32_t threshold_of(double p) {
   return (uint32_t)ceil(p * 16777216.0);
 }
 
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
 template <bool kUniform, bool kVec>
 __global__ void __launch_bounds__(kThreads)
 corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restrict__ cu,
@@ -48,89 +55,123 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
                int32_t mask_id, uint32_t rand_vocab, int32_t* __restrict__ xt,
                uint8_t* __restrict__ corrupted, int32_t* __restrict__ doc_counts) {
   __shared__ int s_dlo, s_dhi;
+  __shared__ int32_t s_cu[kLdsDocs + 1];
   __shared__ int s_cnt[kLdsDocs];
 
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t blk0 = (int64_t)blockIdx.x * kTokPerBlock;
   const int64_t blk1 = min(blk0 + kTokPerBlock, n);
-  if (threadIdx.x == 0) s_dlo = find_doc(cu, 0, n_docs - 1, blk0);
-  if (threadIdx.x == 1) s_dhi = find_doc(cu, 0, n_docs - 1, blk1 - 1);
-  for (int i = threadIdx.x; i < kLdsDocs; i += kThreads) s_cnt[i] = 0;
+  if (wave == 0) {
+    const int d = wave_find_doc(cu, n_docs, blk0);
+    if (lane == 0) s_dlo = d;
+  } else if (wave == 1) {
+    const int d = wave_find_doc(cu, n_docs, blk1 - 1);
+    if (lane == 0) s_dhi = d;
+  }
   __syncthreads();
-  const int dlo = s_dlo, dhi = s_dhi;
-  const bool lds_counts = (dhi - dlo) < kLdsDocs;
+  const int dlo = s_dlo, nd = s_dhi - s_dlo + 1;
+  const bool cached = nd <= kLdsDocs;
+  if (cached) {
+    for (int i = tid; i <= nd; i += kThreads) s_cu[i] = cu[dlo + i];
+    for (int i = tid; i < nd; i += kThreads) s_cnt[i] = 0;
+  }
+  __syncthreads();
 
-  const int64_t g0 = blk0 + (int64_t)threadIdx.x * kTokPerThread;
-  if (g0 < n) {
-    const uint64_t q = (uint64_t)g0 >> 2;
-    const uint4 r1 = philox4x32_10(
-        make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagBernoulli), k0, k1);
-    uint4 r2 = make_uint4(0, 0, 0, 0);
-    if (kUniform)
-      r2 = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagReplace),
-                         k0, k1);
-    const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
-    const uint32_t w2[4] = {r2.x, r2.y, r2.z, r2.w};
-
-    int32_t in[4], out[4];
-    uint8_t flag[4];
-    const int cnt_here = (int)min<int64_t>(kTokPerThread, n - g0);
-    if (kVec && cnt_here == kTokPerThread) {
-      const int4 v = *reinterpret_cast<const int4*>(x0 + g0);
-      in[0] = v.x; in[1] = v.y; in[2] = v.z; in[3] = v.w;
-    } else {
+  for (int j = 0; j < kRounds; ++j) {
+    const int64_t g0 = blk0 + 4 * (int64_t)(tid + kThreads * j);
+    const bool active = g0 < n;
+    int dl[4] = {0, 0, 0, 0};  // local document index of each token (-1: none)
+    uint32_t flag_bits = 0;
+    if (active) {
+      const uint64_t q = (uint64_t)g0 >> 2;
+      const uint4 r1 = philox4x32_10(
+          make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagBernoulli), k0, k1);
+      uint4 r2 = make_uint4(0, 0, 0, 0);
+      if (kUniform)
+        r2 = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagReplace), k0,
+                           k1);
+      const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
+      const uint32_t w2[4] = {r2.x, r2.y, r2.z, r2.w};
+      const int cnt_here = (int)min<int64_t>(4, n - g0);
+      int32_t in[4];
+      if (kVec && cnt_here == 4) {
+        const int4 v = *reinterpret_cast<const int4*>(x0 + g0);
+        in[0] = v.x; in[1] = v.y; in[2] = v.z; in[3] = v.w;
+      } else {
 #pragma unroll
-      for (int k = 0; k < kTokPerThread; ++k) in[k] = k < cnt_here ? x0[g0 + k] : 0;
-    }
-
-    int d = find_doc(cu, dlo, dhi, g0);
-    int64_t d_end = cu[d + 1];
-    uint32_t thr = threshold_of(p_doc[d]);
-    int run = 0;  // corrupted tokens of document d seen so far by this thread
+        for (int k = 0; k < 4; ++k) in[k] = k < cnt_here ? x0[g0 + k] : 0;
+      }
+      // document of the first token, then walk forward
+      int d = cached ? lds_find_doc(s_cu, nd, g0) : find_doc(cu, dlo, s_dhi, g0) - dlo;
+      int64_t d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
+      uint32_t thr = threshold_of(p_doc[dlo + d]);
+      int32_t out[4];
 #pragma unroll
-    for (int k = 0; k < kTokPerThread; ++k) {
-      const int64_t g = g0 + k;
-      flag[k] = 0;
-      out[k] = in[k];
-      if (k < cnt_here) {
-        if (g >= d_end) {
-          if (run) {
-            if (lds_counts && d <= dhi) atomicAdd(&s_cnt[d - dlo], run);
-            else atomicAdd(&doc_counts[d], run);
-            run = 0;
+      for (int k = 0; k < 4; ++k) {
+        const int64_t g = g0 + k;
+        out[k] = in[k];
+        dl[k] = -1;
+        if (k < cnt_here) {
+          if (g >= d_end) {
+            do {
+              ++d;
+              d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
+            } while (g >= d_end && d < nd - 1);
+            thr = threshold_of(p_doc[dlo + d]);
           }
-          // (bounded by the last document even if cu_seqlens is malformed)
-          do { ++d; d_end = cu[d + 1]; } while (g >= d_end && d < n_docs - 1);
-          thr = threshold_of(p_doc[d]);
+          dl[k] = d;
+          if ((w1[k] >> 8) < thr) {
+            flag_bits |= 1u << (8 * k);
+            out[k] = kUniform ? (int32_t)(((uint64_t)w2[k] * rand_vocab) >> 32) : mask_id;
+          }
         }
-        if ((w1[k] >> 8) < thr) {
-          flag[k] = 1;
-          ++run;
-          if (kUniform)
-            out[k] = (int32_t)(((uint64_t)w2[k] * rand_vocab) >> 32);
-          else
-            out[k] = mask_id;
+      }
+      if (kVec && cnt_here == 4) {
+        *reinterpret_cast<int4*>(xt + g0) = make_int4(out[0], out[1], out[2], out[3]);
+        *reinterpret_cast<uint32_t*>(corrupted + g0) = flag_bits;
+      } else {
+        for (int k = 0; k < cnt_here; ++k) {
+          xt[g0 + k] = out[k];
+          corrupted[g0 + k] = (uint8_t)((flag_bits >> (8 * k)) & 1u);
         }
       }
     }
-    if (run) {
-      if (lds_counts && d <= dhi) atomicAdd(&s_cnt[d - dlo], run);
-      else atomicAdd(&doc_counts[d], run);
+    // per-document counts: tokens in the wave's first or last document are
+    // summed across the wave; any others (short documents) are added per lane
+    const int d_first = __shfl(active ? dl[0] : 0x7fffffff, 0, 64);
+    int last_local = -1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) last_local = max(last_local, dl[k]);
+    int d_last = last_local;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) d_last = max(d_last, __shfl_xor(d_last, off, 64));
+    int c_first = 0, c_last = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int bit = (flag_bits >> (8 * k)) & 1;
+      if (dl[k] == d_first) c_first += bit;
+      else if (dl[k] == d_last) c_last += bit;
+      else if (dl[k] >= 0 && bit) {
+        if (cached) atomicAdd(&s_cnt[dl[k]], 1);
+        else atomicAdd(&doc_counts[dlo + dl[k]], 1);
+      }
     }
-    if (kVec && cnt_here == kTokPerThread) {
-      *reinterpret_cast<int4*>(xt + g0) = make_int4(out[0], out[1], out[2], out[3]);
-      const uint32_t packed = (uint32_t)flag[0] | ((uint32_t)flag[1] << 8) |
-                              ((uint32_t)flag[2] << 16) | ((uint32_t)flag[3] << 24);
-      *reinterpret_cast<uint32_t*>(corrupted + g0) = packed;
-    } else {
-      for (int k = 0; k < cnt_here; ++k) {
-        xt[g0 + k] = out[k];
-        corrupted[g0 + k] = flag[k];
+    c_first = wave_sum(c_first);
+    c_last = wave_sum(c_last);
+    if (lane == 0) {
+      if (c_first && d_first >= 0 && d_first != 0x7fffffff) {
+        if (cached) atomicAdd(&s_cnt[d_first], c_first);
+        else atomicAdd(&doc_counts[dlo + d_first], c_first);
+      }
+      if (c_last && d_last >= 0) {
+        if (cached) atomicAdd(&s_cnt[d_last], c_last);
+        else atomicAdd(&doc_counts[dlo + d_last], c_last);
       }
     }
   }
-  if (lds_counts) {
+  if (cached) {
     __syncthreads();
-    for (int i = threadIdx.x; i <= dhi - dlo; i += kThreads)
+    for (int i = tid; i < nd; i += kThreads)
       if (s_cnt[i]) atomicAdd(&doc_counts[dlo + i], s_cnt[i]);
   }
 }
@@ -147,25 +188,21 @@ hipError_t launch_corrupt(const int32_t* x0, int64_t n, const int32_t* cu, int32
         n_docs, k0, k1, eps, p_doc, doc_counts);
   }
   if (n > 0) {
-    const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)xt % 16 == 0) &&
-                     ((uintptr_t)corrupted % 4 == 0);
     const unsigned grid = (unsigned)((n + kTokPerBlock - 1) / kTokPerBlock);
     const uint32_t rv = (uint32_t)rand_vocab;
+    const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)xt % 16 == 0) &&
+                     ((uintptr_t)corrupted % 4 == 0);
+#define MDLM_CORRUPT_LAUNCH(U, VEC)                                                      \
+  corrupt_kernel<U, VEC><<<grid, kThreads, 0, stream>>>(x0, n, cu, n_docs, k0, k1, p_doc, \
+                                                        mask_id, rv, xt, corrupted, doc_counts)
     if (noise == MDLM_NOISE_UNIFORM) {
-      if (vec)
-        corrupt_kernel<true, true><<<grid, kThreads, 0, stream>>>(
-            x0, n, cu, n_docs, k0, k1, p_doc, mask_id, rv, xt, corrupted, doc_counts);
-      else
-        corrupt_kernel<true, false><<<grid, kThreads, 0, stream>>>(
-            x0, n, cu, n_docs, k0, k1, p_doc, mask_id, rv, xt, corrupted, doc_counts);
+      if (vec) MDLM_CORRUPT_LAUNCH(true, true);
+      else MDLM_CORRUPT_LAUNCH(true, false);
     } else {
-      if (vec)
-        corrupt_kernel<false, true><<<grid, kThreads, 0, stream>>>(
-            x0, n, cu, n_docs, k0, k1, p_doc, mask_id, rv, xt, corrupted, doc_counts);
-      else
-        corrupt_kernel<false, false><<<grid, kThreads, 0, stream>>>(
-            x0, n, cu, n_docs, k0, k1, p_doc, mask_id, rv, xt, corrupted, doc_counts);
+      if (vec) MDLM_CORRUPT_LAUNCH(false, true);
+      else MDLM_CORRUPT_LAUNCH(false, false);
     }
+#undef MDLM_CORRUPT_LAUNCH
   }
   return hipGetLastError();
 }

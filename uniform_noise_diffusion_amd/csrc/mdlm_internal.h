@@ -61,6 +61,48 @@ __device__ __forceinline__ int find_doc(const int32_t* __restrict__ cu, int lo, 
   return a - 1;
 }
 
+// Document holding token g, found by one whole wave (every lane passes the
+// same g) with a 64-ary search: each round, 64 evenly spaced candidate
+// documents are tested at once and the range shrinks 64-fold, so 32,768
+// documents take three rounds of loads instead of fifteen.  Returns the same
+// value on every lane.
+__device__ __forceinline__ int wave_find_doc(const int32_t* __restrict__ cu, int n_docs,
+                                             int64_t g) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, hi = n_docs - 1;  // the answer lies in [lo, hi]
+  while (hi - lo + 1 > 64) {
+    const int64_t span = (int64_t)hi - lo + 1;
+    const int c = lo + (int)(span * lane / 64);
+    const uint64_t b = __ballot((int64_t)cu[c + 1] > g);
+    if (b == 0) {
+      lo = lo + (int)(span * 63 / 64) + 1;
+    } else {
+      const int f = __ffsll((unsigned long long)b) - 1;
+      const int cf = lo + (int)(span * f / 64);
+      if (f > 0) lo = lo + (int)(span * (f - 1) / 64) + 1;
+      hi = cf;
+    }
+  }
+  const int c = lo + lane;
+  const uint64_t b = __ballot(c <= hi && (int64_t)cu[c + 1] > g);
+  return lo + __ffsll((unsigned long long)b) - 1;
+}
+
+// Document of token g among documents [0, nd) of a block whose offsets
+// (cu[dlo] .. cu[dlo + nd]) are cached in LDS as s_cu[0 .. nd]; returns the
+// local index.
+__device__ __forceinline__ int lds_find_doc(const int32_t* s_cu, int nd, int64_t g) {
+  int a = 1, b = nd;  // first i in [1, nd] with s_cu[i] > g, minus one
+  while (a < b) {
+    const int mid = (a + b) >> 1;
+    if ((int64_t)s_cu[mid] > g)
+      b = mid;
+    else
+      a = mid + 1;
+  }
+  return a - 1;
+}
+
 // ---- launchers implemented in the kernel translation units ---------------
 hipError_t launch_corrupt(const int32_t* x0, int64_t n_tokens, const int32_t* cu,
                           int32_t n_docs, uint64_t seed, double eps, int32_t noise,
