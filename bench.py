@@ -165,7 +165,13 @@ def bandwidth(n_tokens, dev, reps=10):
 
 
 def cpu_baseline(inp, mean_rows, seconds):
-    """The fp64 oracle, as it stands, on a bounded sample of the workload."""
+    """The fp64 oracle, as it stands, on a bounded sample of the workload.
+
+    The oracle's head + CE call has a fixed cost per call (it converts every
+    chunk of W to fp64) plus a cost per scored row, so it is timed on a
+    doubling number of rows until a call takes about half the budget, and the
+    last two timings give the line a + b * rows that is evaluated at the
+    workload's mean scored-row count."""
     import oracle
     wl = inp.wl
     t0 = time.perf_counter()
@@ -173,24 +179,40 @@ def cpu_baseline(inp, mean_rows, seconds):
                                          wl.mask_id, wl.rand_vocab)
     rows, tgt, w = oracle.compact(corrupted, inp.x0, inp.cu_seqlens, p, wl.align)
     t_cc = time.perf_counter() - t0
-    # calibrate on a few rows, then size the sample to about `seconds`
-    t1 = time.perf_counter()
-    oracle.head_ce(inp.hidden, inp.W, rows[:4], tgt[:4], w[:4], wl.softcap)
-    per_row = (time.perf_counter() - t1) / 4
-    s = int(max(4, min(rows.shape[0], seconds / max(per_row, 1e-9))))
-    t2 = time.perf_counter()
-    oracle.head_ce(inp.hidden, inp.W, rows[:s], tgt[:s], w[:s], wl.softcap)
-    t_rows = time.perf_counter() - t2
-    est_step = t_cc + t_rows / s * mean_rows
+    m_all = rows.shape[0]
+    samples = []
+    s = 8
+    spent = 0.0
+    while True:
+        s = min(s, m_all)
+        t1 = time.perf_counter()
+        oracle.head_ce(inp.hidden, inp.W, rows[:s], tgt[:s], w[:s], wl.softcap)
+        dt = time.perf_counter() - t1
+        spent += dt
+        samples.append((s, dt))
+        if s >= m_all or dt > seconds / 2 or spent > seconds:
+            break
+        s *= 2
+    if len(samples) >= 2:
+        (s1, d1), (s2, d2) = samples[-2], samples[-1]
+        b = max((d2 - d1) / (s2 - s1), 0.0)
+        a = max(d2 - b * s2, 0.0)
+    else:
+        (s2, d2), = samples
+        a, b = 0.0, d2 / s2
+    est_step = t_cc + a + b * mean_rows
     try:
         from threadpoolctl import threadpool_info
         cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or os.cpu_count()
     except Exception:  # noqa: BLE001
         cores = os.cpu_count()
     return dict(value=wl.n_tokens / est_step, unit="tokens/s", cores=cores, kind="oracle",
-                sample=(f"oracle corrupt+compact over all {wl.n_tokens} tokens "
-                        f"({t_cc:.2f} s) plus fp64 head+CE fwd+bwd over {s} scored rows "
-                        f"({t_rows:.2f} s), scaled to {mean_rows:.0f} scored rows per step"))
+                seconds_per_step=est_step,
+                sample=(f"oracle corrupt+compact over all {wl.n_tokens} tokens ({t_cc:.2f} s); "
+                        f"fp64 head+CE fwd+bwd timed on {', '.join(str(x) for x, _ in samples)} "
+                        f"scored rows ({spent:.1f} s in all), per-call cost {a:.2f} s + "
+                        f"{b * 1e3:.1f} ms per row, evaluated at the {mean_rows:.0f} scored "
+                        f"rows of a mean step"))
 
 
 def main():
