@@ -30,6 +30,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace mdlm {
 namespace {
@@ -57,6 +58,11 @@ constexpr int kNRow = kTile * 2;      // bytes per row of an N-major tile (512)
 constexpr int kOpBytes = kTile * kKRow;       // one operand tile: 32 KiB
 constexpr int kStageBytes = 2 * kOpBytes;     // A + B: 64 KiB
 constexpr int kLdsBytes = 2 * kStageBytes;    // two stages: 128 KiB
+#ifndef MDLM_VMEM_EVERY
+#define MDLM_VMEM_EVERY 2
+#endif
+constexpr int kVmemEvery = MDLM_VMEM_EVERY;  // MFMAs per interleaved prefetch load
+static_assert(2 * kLoads * kVmemEvery <= 4 * (16 / kWaves) * (64 / 16), "loads fit in a step");
 constexpr int kMaxSplit = 8;          // K-splits of the dH product
 constexpr int kMergeRows = 4;         // rows per merge block (one per wave)
 constexpr int kGrid = 256;            // persistent grid: one workgroup per CU
@@ -114,11 +120,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
                                            0x00020000);
 }
 
+// Compile-time count of prefetch loads interleaved with a step's MFMAs.
+constexpr std::integral_constant<int, 2 * kLoads> kInterleave{};
+constexpr std::integral_constant<int, 0> kNoLoads{};
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Keeps the scheduler from moving instructions across this point: used so the
-// next stage's loads are issued at the top of a K step (a full step ahead of
-// their use) and the step's MFMAs finish before the next wait.
+// Keeps the scheduler from moving instructions across this point: used so a
+// step's MFMAs (and the loads interleaved with them) stay ahead of the next
+// wait.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short shortx4;
@@ -129,6 +139,33 @@ typedef __attribute__((__vector_size__(4 * sizeof(short)))) short shortx4;
 // that block, rows 0..3.
 __device__ __forceinline__ shortx4 ds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MDLM_LDS shortx4*)(p));
+}
+
+// Entry at offset dt (0 <= dt < 128, bit 2 clear) of a lane's 64 accumulator
+// entries, where entry e of block i sits at offset 32 i + 8 (e / 4) + e % 4:
+// a select tree on the bits of dt (six masks, 63 selects) rather than one
+// compare per entry.
+__device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
+
+__device__ __forceinline__ float pick_entry(const float (&sv)[4][16], int dt) {
+  // (selects on values, never on array elements: a conditional lvalue would
+  // select addresses and force the arrays into scratch memory)
+  const bool b0 = dt & 1, b1 = dt & 2, b3 = dt & 8, b4 = dt & 16, b5 = dt & 32, b6 = dt & 64;
+  float g[16];  // g[4 i + q]: entry 4 q + (dt % 4) of block i
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float x0 = sv[i][4 * q], x1 = sv[i][4 * q + 1];
+      const float x2 = sv[i][4 * q + 2], x3 = sv[i][4 * q + 3];
+      g[4 * i + q] = sel(b1, sel(b0, x3, x2), sel(b0, x1, x0));
+    }
+  float h8[8], h4[4];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) h8[k] = sel(b3, g[2 * k + 1], g[2 * k]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) h4[k] = sel(b4, h8[2 * k + 1], h8[2 * k]);
+  return sel(b6, sel(b5, h4[3], h4[2]), sel(b5, h4[1], h4[0]));
 }
 
 // --------------------------------------------------------------------------
@@ -150,17 +187,20 @@ struct LogitsArgs {
   int v_begin;  // vocabulary range of this launch
   int v_end;
   float2* partial;  // fwd: [ceil(V/kTile)][max_rows] (max, sum) in log2 units
-  float* ztgt;      // fwd: [max_rows] capped target logit
+  float* ztgt;      // [max_rows] capped target logit x log2(e) (fwd writes, grad reads)
   const float* lse; // grad: [max_rows]
   bf16_t* G;        // grad: [max_rows][ldg], column = v - v_begin
   int64_t ldg;
 };
 
-// Software-pipelined MFMA block for one 64-deep K step of a wave's 128 x 128
-// tile: the fragments of 16-deep slice kk+1 are read from LDS while the 16
-// MFMAs of slice kk run.  `ra` reads the A fragments of a slice, `rb` the B
-// fragments.
-template <int kReads, typename ReadA, typename ReadB>
+// Software-pipelined MFMA block for one 64-deep K step of a wave's tile: the
+// fragments of 16-deep slice kk+1 are read from LDS while the MFMAs of slice
+// kk run.  `ra` reads the A fragments of a slice, `rb` the B fragments.
+// kVmem global->LDS loads issued just before the call (the next stage's
+// prefetch) are spread over the step, one before every kVmemEvery-th MFMA:
+// issued together at the top of the step they stall the issuing waves (and
+// so the matrix pipes) until the memory pipeline has taken them.
+template <int kReads, int kVmem, typename ReadA, typename ReadB>
 __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB rb) {
   bf16x8 af[2][4], bfr[2][kNJ];
   ra(0, af[0]);
@@ -179,30 +219,34 @@ __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB r
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
                                                             0, 0, 0);
   }
-  // Issue order for the scheduler: the first slice's reads, then for each
-  // slice but the last its MFMAs alternated one for one with the next slice's
-  // reads, then the last slice's MFMAs.  `kReads` counts LDS read
-  // instructions per slice (transpose reads count twice).
+  // Issue order for the scheduler: the first slice's reads, then each slice's
+  // MFMAs alternated one for one with the next slice's reads (transpose reads
+  // count twice in `kReads`), with the loads interleaved as above.
   constexpr int kMfma = 4 * kNJ;
+  constexpr int kSlices = kBK / 16;
   __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
-  for (int kk = 0; kk + 1 < kBK / 16; ++kk) {
+  for (int kk = 0; kk < kSlices; ++kk) {
 #pragma unroll
     for (int x = 0; x < kMfma; ++x) {
+      const int gx = kk * kMfma + x;
+      if (kVmem > 0 && gx % kVmemEvery == 0 && gx / kVmemEvery < kVmem)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (x < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (kk + 1 < kSlices && x < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    if (kk + 1 < kSlices) {
 #pragma unroll
-    for (int x = kMfma; x < kReads; ++x) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int x = kMfma; x < kReads; ++x) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
 }
 
 // Tile of 256 vocabulary rows (operand A, rows of W) by 256 scored rows
 // (operand B, rows of hidden gathered through row_idx), K = H.  Wave w owns
 // vocabulary rows 128 (w % 2) .. +127 and scored rows kWB (w / 2) .. +kWB-1:
 // a 4 x kNJ grid of 32 x 32 MFMA blocks.
-template <bool kGrad>
+template <bool kGrad, bool kCap>
 __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
   // the two stages are separate objects so that the compiler can tell a
   // prefetch into one from reads of the other
@@ -218,7 +262,6 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
   const int n_vt = (a.v_end - a.v_begin + kTile - 1) / kTile;
   const int64_t n_tiles = (int64_t)n_mt * n_vt;
   const int KT = a.H / kBK;
-  const bool capped = a.softcap > 0.f;
 
   // fragment-read offsets (bytes within a stage)
   const int fx = swz_k(lane & 15), khalf = lane >> 5;
@@ -275,8 +318,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
         buf2l(rb, sa + kOpBytes + q * 1024, b_voff[q], (uint32_t)(k0 * 2));
       }
     };
-    auto compute = [&](const char* base) {
-      mma_k64<4 + kNJ>(
+    auto compute = [&](const char* base, auto vmem) {
+      mma_k64<4 + kNJ, decltype(vmem)::value>(
           acc,
           [&](int kk, bf16x8(&f)[4]) {
             const int coff = ((2 * kk + khalf) ^ fx) * 16;
@@ -295,88 +338,116 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
     __syncthreads();  // the previous tile is done with both stages
     issue(smem0, 0);
     // two K steps per trip so that each access names its stage statically;
-    // an odd last step runs after the loop
+    // an odd last step runs after the loop.  The prefetch into smem0 is
+    // unconditional so that it shares a basic block (and so a scheduling
+    // region) with the MFMAs it is interleaved with: on the last trip of an
+    // even KT it reads past K (in-range bytes or zeros), is never consumed,
+    // and the wait after the loop retires it before the stage is reused.
     int kt = 0;
     for (; kt + 2 <= KT; kt += 2) {
       wait_vmem();
       __syncthreads();
       issue(smem1, (kt + 1) * kBK);
-      sched_fence();
-      compute(smem0);
+      compute(smem0, kInterleave);
       sched_fence();
       wait_vmem();
       __syncthreads();
-      if (kt + 2 < KT) issue(smem0, (kt + 2) * kBK);
-      sched_fence();
-      compute(smem1);
+      issue(smem0, (kt + 2) * kBK);
+      compute(smem1, kInterleave);
       sched_fence();
     }
     if (kt < KT) {
       wait_vmem();
       __syncthreads();
-      compute(smem0);
+      compute(smem0, kNoLoads);
     }
+    wait_vmem();
 
     // ---- epilogue ---------------------------------------------------------
     // Accumulator element e of block (i, j) on lane l holds vocabulary entry
-    // v0 + wa*128 + 32i + 8(e/4) + 4(l/32) + e%4 for row m0 + wb*kWB + 32j + l%32.
+    // vl + 32i + 8(e/4) + e%4, vl = v0 + wa*128 + 4(l/32), for row
+    // m0 + wb*kWB + 32j + l%32.  A row's target sits in this lane's registers
+    // iff its offset dt from vl lies in [0, 128) with bit 2 clear.  Only the
+    // tile that straddles v_end masks entries past the vocabulary.
     const int vl = v0 + wa * 128 + 4 * (lane >> 5);
+    const int lim = a.v_end - vl;
+    auto epilogue = [&](auto full_tag) __attribute__((always_inline)) {
+      constexpr bool kFull = decltype(full_tag)::value;
 #pragma unroll
-    for (int j = 0; j < kNJ; ++j) {
-      const int m = m0 + wb * kWB + 32 * j + (lane & 31);
-      const bool mvalid = m < n_rows;
-      const int tg = mvalid ? a.tgt[m] : -1;
-      if (!kGrad) {
-        float sv[4][16];
-        float mx = -INFINITY, zt = 0.f;
-        bool hit = false;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int v = vl + 32 * i + 8 * (e >> 2) + (e & 3);
-            float zc = acc[i][j][e], dc;
-            if (capped) zc = softcap_fwd(zc, a.softcap, a.inv_softcap, &dc);
-            zt = (v == tg) ? zc : zt;
-            hit |= (v == tg);
-            sv[i][e] = v < a.v_end ? zc * kLog2e : -INFINITY;
-            mx = fmaxf(mx, sv[i][e]);
-          }
-        if (mvalid && hit) a.ztgt[m] = zt;
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        float sum = 0.f;
-        if (mx != -INFINITY) {
+      for (int j = 0; j < kNJ; ++j) {
+        const int m = m0 + wb * kWB + 32 * j + (lane & 31);
+        const bool mvalid = m < n_rows;
+        const int tg = mvalid ? a.tgt[m] : -1;
+        const int dt = tg - vl;
+        const bool holds_tgt = (unsigned)dt < 128u && (dt & 4) == 0;
+        if (!kGrad) {
+          float sv[4][16];
+          float mx = -INFINITY;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(sv[i][e] - mx);
-        }
-        sum += __shfl_xor(sum, 32, 64);
-        if (lane < 32) red[wa][wb * kWB + 32 * j + lane] = make_float2(mx, sum);
-      } else if (mvalid) {
-        const float lse2 = a.lse[m] * kLog2e;
-        const float wm = a.w[m];
-        bf16_t* grow = a.G + (int64_t)m * a.ldg - a.v_begin;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float g[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int v = vl + 32 * i + 8 * q + r;
-              float zc = acc[i][j][4 * q + r], dc = 1.f;
-              if (capped) zc = softcap_fwd(zc, a.softcap, a.inv_softcap, &dc);
-              float p = __builtin_amdgcn_exp2f(zc * kLog2e - lse2);
-              if (v == tg) p -= 1.f;
-              g[r] = v < a.v_end ? p * dc * wm : 0.f;
+            for (int e = 0; e < 16; ++e) {
+              const int off = 32 * i + 8 * (e >> 2) + (e & 3);
+              float zc = acc[i][j][e], dc;
+              if (kCap) zc = softcap_fwd(zc, a.softcap, a.inv_softcap, &dc);
+              float sc = zc * kLog2e;
+              if (!kFull) sc = off < lim ? sc : -INFINITY;
+              sv[i][e] = sc;
+              mx = fmaxf(mx, sc);
             }
-            const int v = vl + 32 * i + 8 * q;
-            *reinterpret_cast<uint2*>(grow + v) =
-                make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
+          // (the target is never past the vocabulary, so never masked)
+          if (mvalid && holds_tgt) a.ztgt[m] = pick_entry(sv, dt);
+          mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          float sum = 0.f;
+          if (mx != -INFINITY) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(sv[i][e] - mx);
           }
+          sum += __shfl_xor(sum, 32, 64);
+          if (lane < 32) red[wa][wb * kWB + 32 * j + lane] = make_float2(mx, sum);
+        } else if (mvalid) {
+          // G = w p cap' everywhere, then the target entry is rewritten with
+          // w (p - 1) cap' from the capped target logit the forward pass kept
+          // (the same tile product)
+          const float lse2 = a.lse[m] * kLog2e;
+          const float wm = a.w[m];
+          bf16_t* grow = a.G + (int64_t)m * a.ldg - a.v_begin;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float g[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int off = 32 * i + 8 * q + r;
+                float zc = acc[i][j][4 * q + r], dc = 1.f;
+                if (kCap) zc = softcap_fwd(zc, a.softcap, a.inv_softcap, &dc);
+                const float p = __builtin_amdgcn_exp2f(zc * kLog2e - lse2);
+                g[r] = kCap ? p * dc * wm : p * wm;
+                if (!kFull) g[r] = off < lim ? g[r] : 0.f;
+              }
+              *reinterpret_cast<uint2*>(grow + vl + 32 * i + 8 * q) =
+                  make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
+            }
+          if (holds_tgt) {
+            const float zt2 = a.ztgt[m];
+            float dc = 1.f;
+            if (kCap) {
+              const float th = zt2 * kLn2 * a.inv_softcap;
+              dc = 1.f - th * th;
+            }
+            const float p = __builtin_amdgcn_exp2f(zt2 - lse2);
+            grow[tg] = (bf16_t)((p - 1.f) * dc * wm);
+          }
+        }
       }
-    }
+    };
+    if (v0 + kTile <= a.v_end)
+      epilogue(std::true_type{});
+    else
+      epilogue(std::false_type{});
     if (!kGrad) {
       __syncthreads();
       if (wa == 0) {
@@ -507,9 +578,9 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
               (uint32_t)((2 * (kLoads * wave + q) + k0) * a.H * 2));
       }
     };
-    auto compute = [&](const char* base) {
+    auto compute = [&](const char* base, auto vmem) {
       const char* bb = base + kOpBytes;
-      mma_k64<4 + 2 * kNJ>(
+      mma_k64<4 + 2 * kNJ, decltype(vmem)::value>(
           acc,
           [&](int kk, bf16x8(&f)[4]) {
             const int coff = ((2 * kk + khalf) ^ fx) * 16;
@@ -532,26 +603,27 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
 
     __syncthreads();
     issue(smem0, kb * kBK);
+    // same pipeline as the logits tiles (unconditional last prefetch, retired
+    // by the wait after the loop)
     int kt = kb;
     for (; kt + 2 <= ke; kt += 2) {
       wait_vmem();
       __syncthreads();
       issue(smem1, (kt + 1) * kBK);
-      sched_fence();
-      compute(smem0);
+      compute(smem0, kInterleave);
       sched_fence();
       wait_vmem();
       __syncthreads();
-      if (kt + 2 < ke) issue(smem0, (kt + 2) * kBK);
-      sched_fence();
-      compute(smem1);
+      issue(smem0, (kt + 2) * kBK);
+      compute(smem1, kInterleave);
       sched_fence();
     }
     if (kt < ke) {
       wait_vmem();
       __syncthreads();
-      compute(smem0);
+      compute(smem0, kNoLoads);
     }
+    wait_vmem();
 
     // acc element e of block (i, j) on lane l: row m0 + wa*128 + 32i + 8(e/4)
     // + 4(l/32) + e%4, column h0 + wb*kWB + 32j + l%32.
@@ -605,9 +677,11 @@ merge_kernel(const float2* __restrict__ partial, int n_vt, int max_rows,
         s = s * __builtin_amdgcn_exp2f(mx - nm) + os * __builtin_amdgcn_exp2f(om - nm);
       mx = nm;
     }
-    const float lse = (mx + __log2f(s)) * kLn2;
+    const float lse2 = mx + __log2f(s);
+    const float lse = lse2 * kLn2;
     const int tg = tgt[j];
-    const float ce = (tg >= 0 && tg < V) ? lse - ztgt[j] : NAN;
+    // ztgt holds the capped target logit in log2 units
+    const float ce = (tg >= 0 && tg < V) ? (lse2 - ztgt[j]) * kLn2 : NAN;
     if (lane == 0) {
       lse_out[j] = lse;
       if (row_ce) row_ce[j] = ce;
@@ -718,7 +792,7 @@ __global__ void __launch_bounds__(kThreads) f32_logits_kernel(F32Args a) {
   if (a.softcap > 0.f) z = softcap_fwd(z, a.softcap, a.inv_softcap, &dc);
   const int tg = a.tgt[m];
   if (!kGrad) {
-    if (vok && v == tg) a.ztgt[m] = z;
+    if (vok && v == tg) a.ztgt[m] = z * kLog2e;
     const float s = vok ? z * kLog2e : -INFINITY;
     float mx = s;
     for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
@@ -856,7 +930,10 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     la.v_end = x.V;
     la.partial = partial;
     la.ztgt = ztgt;
-    logits_kernel<false><<<grid, kGemmThreads, 0, stream>>>(la);
+    if (x.softcap > 0.f)
+      logits_kernel<false, true><<<grid, kGemmThreads, 0, stream>>>(la);
+    else
+      logits_kernel<false, false><<<grid, kGemmThreads, 0, stream>>>(la);
   } else {
     F32Args fa{};
     fa.W = reinterpret_cast<const float*>(x.W);
@@ -925,6 +1002,7 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   la.softcap = x.softcap;
   la.inv_softcap = inv_cap;
   la.lse = lse;
+  la.ztgt = ztgt;
   la.G = G;
   la.ldg = vc;
 
@@ -942,7 +1020,10 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     const int v1 = (int)std::min<int64_t>(x.V, v0 + vc);
     la.v_begin = (int)v0;
     la.v_end = v1;
-    logits_kernel<true><<<grid, kGemmThreads, 0, stream>>>(la);
+    if (x.softcap > 0.f)
+      logits_kernel<true, true><<<grid, kGemmThreads, 0, stream>>>(la);
+    else
+      logits_kernel<true, false><<<grid, kGemmThreads, 0, stream>>>(la);
     da.v_begin = (int)v0;
     da.v_end = v1;
     da.accumulate = chunk > 0;
