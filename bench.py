@@ -124,17 +124,24 @@ def gpu_steps(args, inp, dev):
     return dict(total_ms=total_ms, wall_s=wall, head_ms=head_ms, rows=rows, align=align)
 
 
-def bandwidth(n_tokens, dev, reps=10):
-    """Corruption and compaction at a bandwidth-sized stream: 2^27 tokens in
-    documents of 4,096 (32,768 documents)."""
+def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
+    """Corruption and compaction at a bandwidth-sized stream of 2^27 tokens:
+    documents of 4,096 tokens (32,768 documents), or lognormal lengths with
+    arithmetic mean ``doc_mean`` (sigma 1, clipped to [16, 4096])."""
     import torch
+    import workloads as WL
     from uniform_noise_diffusion_amd.pipeline import MdlmLossStep
-    L = 4096
-    n = n_tokens // L * L
-    n_docs = n // L
+    if doc_mean is None:
+        L = 4096
+        n = n_tokens // L * L
+        cu = torch.arange(0, n + 1, L, dtype=torch.int32, device=dev)
+    else:
+        n = n_tokens
+        cu = torch.from_numpy(
+            WL.lognormal_stream_offsets(5000 + doc_mean, doc_mean, n).astype(np.int32)).to(dev)
+    n_docs = cu.numel() - 1
     g = torch.Generator(device=dev).manual_seed(0)
     x0 = torch.randint(0, 126336, (n,), dtype=torch.int32, device=dev, generator=g)
-    cu = torch.arange(0, n + 1, L, dtype=torch.int32, device=dev)
     step = MdlmLossStep(n, n_docs, 64, 64, device=dev, head_workspace_bytes=0, want_grad=False)
     for i in range(2):
         step.corrupt(x0, cu, i, 1e-3, 0, 126336, 126464)
@@ -157,7 +164,8 @@ def bandwidth(n_tokens, dev, reps=10):
     # scored row, the target (4 B) and writes row, target and weight (12 B)
     b_cor = 9.0 * n
     b_cmp = 1.0 * n + 16.0 * m
-    return dict(n_tokens=n, scored_rows=m,
+    return dict(docs="4096 each" if doc_mean is None else f"lognormal mean {doc_mean}",
+                n_tokens=n, n_docs=n_docs, scored_rows=m,
                 corrupt_us=t_cor * 1e6, corrupt_GBs=b_cor / t_cor / 1e9,
                 corrupt_frac=b_cor / t_cor / 1e9 / PEAK_HBM_GBS,
                 compact_us=t_cmp * 1e6, compact_GBs=b_cmp / t_cmp / 1e9,
@@ -277,6 +285,8 @@ def main():
     if args.bandwidth_tokens:
         log("timing corruption/compaction bandwidth")
         out["corrupt_compact_hbm"] = bandwidth(args.bandwidth_tokens, dev)
+        out["corrupt_compact_hbm_lognormal296"] = bandwidth(args.bandwidth_tokens, dev,
+                                                            doc_mean=296)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(inp, rows.mean(), args.cpu_seconds)

@@ -124,9 +124,10 @@ int mdlm_corrupt(const int32_t* x0, int64_t n_tokens,
                  int32_t* doc_counts, void* stream);
 
 /*
- * Workspace bytes that mdlm_compact_masked needs for n_tokens tokens (three
- * 32-bit words per 4096-token tile: its count and its first and last
- * document).  Returns 0 only for n_tokens <= 0.
+ * Workspace bytes that mdlm_compact_masked needs for n_tokens tokens: three
+ * 32-bit words per 4096-token tile (its count and its first and last
+ * document) plus one per group of 1024 tiles (the group's total).  Returns 0
+ * only for n_tokens <= 0.
  */
 size_t mdlm_compact_workspace_bytes(int64_t n_tokens);
 

@@ -50,13 +50,20 @@ def test_version(lib):
     assert B.mdlm_version() >> 16 == 1
 
 
+def compact_ws(n):
+    # three 32-bit words per 4096-token tile, one per group of 1024 tiles
+    tiles = -(-n // 4096)
+    return 4 * (3 * tiles + -(-tiles // 1024))
+
+
 def test_compact_workspace_sizes(lib):
-    # three 32-bit words per 4096-token tile
     assert B.mdlm_compact_workspace_bytes(0) == 0
-    assert B.mdlm_compact_workspace_bytes(1) == 12
-    assert B.mdlm_compact_workspace_bytes(4096) == 12
-    assert B.mdlm_compact_workspace_bytes(4097) == 24
-    assert B.mdlm_compact_workspace_bytes(1 << 27) == 12 * (1 << 15)
+    assert B.mdlm_compact_workspace_bytes(1) == 16
+    assert B.mdlm_compact_workspace_bytes(4096) == 16
+    assert B.mdlm_compact_workspace_bytes(4097) == 28
+    assert B.mdlm_compact_workspace_bytes(1024 * 4096) == 4 * (3 * 1024 + 1)
+    assert B.mdlm_compact_workspace_bytes(1024 * 4096 + 1) == 4 * (3 * 1025 + 2)
+    assert B.mdlm_compact_workspace_bytes(1 << 27) == compact_ws(1 << 27) == 4 * (3 * 32768 + 32)
 
 
 def test_head_workspace_sizes(lib):
@@ -169,7 +176,7 @@ def test_compact_rejects_small_workspace(lib):
     fake = ctypes.c_void_p(1 << 20)
     n = 1 << 20
     need = B.mdlm_compact_workspace_bytes(n)
-    assert need == 12 * (n // 4096)
+    assert need == compact_ws(n)
     kw = dict(corrupted=fake, x0=fake, cu=fake, p_doc=fake, row_idx=fake, tgt=fake, w=fake,
               n_rows=fake, n=n)
     assert compact_call(lib, **kw) == B.MDLM_EWORKSPACE

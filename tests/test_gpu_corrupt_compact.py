@@ -90,6 +90,20 @@ def test_corrupt_compact_bit_exact_workloads(k, align):
         _check(inp.x0, inp.cu_seqlens, seed, wl.eps, wl.noise, wl.mask_id, wl.rand_vocab, align)
 
 
+@pytest.mark.parametrize("align", [oracle.ALIGNED, oracle.SHIFTED])
+def test_compaction_across_scan_groups(align):
+    """1,025 full tiles and a ragged one (two groups of the offset scan), with
+    lognormal documents of mean 296 plus a run of 3-token documents: every
+    output is compared with the oracle."""
+    rng = np.random.default_rng(31)
+    n = 1025 * 4096 + 1234
+    cu = WL.lognormal_stream_offsets(77, 296, n)
+    short = np.arange(cu[100], cu[100] + 3 * 400, 3)
+    cu = np.unique(np.concatenate([cu, short])).astype(np.int32)
+    x0 = rng.integers(0, 126000, size=n).astype(np.int32)
+    _check(x0, cu, 4242, 1e-3, oracle.NOISE_ABSORB, 126336, 126464, align)
+
+
 def test_empty_stream():
     x0 = np.zeros(0, dtype=np.int32)
     cu = np.zeros(2, dtype=np.int32)

@@ -11,16 +11,18 @@
 //   1. tile_docs_kernel: one thread per document records, for every 4096-token
 //      tile whose first or last token the document holds, that document --
 //      each tile learns the range of documents it touches without a search;
-//   2. count_kernel: each block counts the scored tokens of one tile (1 byte
-//      per token read);
-//   3. scan_kernel: one block turns the per-tile counts into exclusive
-//      offsets in place and writes the total to n_rows;
-//   4. scatter_kernel: each block re-reads its tile in four 1024-token rounds,
-//      ranks each round's scored tokens with a block scan, stages (row,
-//      target, weight) in LDS and writes them at its offset with coalesced
-//      stores.
-// A tile's document offsets are cached in LDS when it touches at most 2048
-// documents.
+//   2. count_kernel: one wave per tile counts its scored tokens (1 byte per
+//      token read, four 16-byte loads in flight per lane);
+//   3. group_scan_kernel: each block scans 1024 tile counts into offsets
+//      within the group (in place) and writes the group's total;
+//   4. scatter_kernel: each block adds the totals of the groups before its own
+//      to its offset, re-reads its tile in four 1024-token rounds, ranks each
+//      round's scored tokens with ballots, stages (row, target, weight) in a
+//      double-buffered LDS area and writes them with coalesced stores.
+// A tile's document offsets and weights are cached in LDS when it touches at
+// most 1024 documents; a wave whose 256 tokens of a round touch at most four
+// documents finds each token's document by comparisons with wave-uniform
+// boundaries instead of a search.
 #include "mdlm_internal.h"
 
 #include <algorithm>
@@ -30,25 +32,41 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTokPerThread = 16;
-constexpr int kTile = kThreads * kTokPerThread;  // 4096 tokens
-constexpr int kLdsDocs = 2048;                   // documents cached per tile
-constexpr int kScanThreads = 1024;
+constexpr int kTile = 4096;          // tokens per tile
+#ifndef MDLM_COMPACT_LDS_DOCS
+#define MDLM_COMPACT_LDS_DOCS 1024
+#endif
+constexpr int kLdsDocs = MDLM_COMPACT_LDS_DOCS;  // documents cached per tile
+constexpr int kGroup = 1024;         // tiles per scan group (one block)
+constexpr int kRoundTok = kThreads * 4;  // tokens per scatter round: 1024
+#ifndef MDLM_SCATTER_BUFS
+#define MDLM_SCATTER_BUFS 1
+#endif
+// staging buffers: two drop the barrier that protects reuse, at the cost of
+// LDS (and so of resident blocks)
+constexpr int kBufs = MDLM_SCATTER_BUFS;
 
 __global__ void set_int_kernel(int32_t* p, int32_t v) { *p = v; }
 
-// The 16 mask bytes of this thread's tokens [g0, g0 + cnt).
-__device__ __forceinline__ void load_mask(const uint8_t* __restrict__ corrupted, int64_t g0,
-                                          int cnt, uint8_t (&m)[kTokPerThread]) {
-  if (cnt == kTokPerThread && ((uintptr_t)(corrupted + g0) % 16 == 0)) {
-    const uint4 v = *reinterpret_cast<const uint4*>(corrupted + g0);
-    const uint32_t words[4] = {v.x, v.y, v.z, v.w};
+__device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
-    for (int k = 0; k < kTokPerThread; ++k) m[k] = (words[k >> 2] >> (8 * (k & 3))) & 0xff;
-  } else {
-#pragma unroll
-    for (int k = 0; k < kTokPerThread; ++k) m[k] = k < cnt ? corrupted[g0 + k] : 0;
-  }
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Number of nonzero bytes of w: bit 0 of each byte becomes the OR of that
+// byte's bits (shifts that only move bits down within a byte's low nibble).
+__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
+  uint32_t x = w | (w >> 4);
+  x |= x >> 2;
+  x |= x >> 1;
+  return __popc(x & 0x01010101u);
+}
+
+// Set bits of b at lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t b) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
 }
 
 // For each tile k, the documents holding its first token (tile_lo[k]) and its
@@ -72,221 +90,239 @@ tile_docs_kernel(const int32_t* __restrict__ cu, int32_t n_docs, int64_t n,
   }
 }
 
-// Loads the tile's document range and caches the documents' offsets in s_cu
-// when there are at most kLdsDocs of them.  Returns whether they were cached.
-// Contains one barrier.
-__device__ __forceinline__ bool tile_docs(const int32_t* __restrict__ cu, int32_t n_docs,
-                                          const int32_t* __restrict__ tile_lo,
-                                          const int32_t* __restrict__ tile_hi, int* dlo_out,
-                                          int* dhi_out, int32_t* s_cu) {
-  // (clamped so that even offsets that break the preconditions stay in range)
-  const int dlo = min(max(tile_lo[blockIdx.x], 0), n_docs - 1);
-  const int dhi = min(max(tile_hi[blockIdx.x], dlo), n_docs - 1);
-  const int nd = dhi - dlo + 1;
-  const bool cached = nd <= kLdsDocs;
-  if (cached)
-    for (int i = threadIdx.x; i <= nd; i += kThreads) s_cu[i] = cu[dlo + i];
-  __syncthreads();
-  *dlo_out = dlo;
-  *dhi_out = dhi;
-  return cached;
+// Document range [dlo, dhi] of tile t (clamped so that even offsets that
+// break the preconditions stay in range).
+__device__ __forceinline__ void tile_range(const int32_t* __restrict__ tile_lo,
+                                           const int32_t* __restrict__ tile_hi, int32_t n_docs,
+                                           int64_t t, int* dlo, int* dhi) {
+  *dlo = min(max(tile_lo[t], 0), n_docs - 1);
+  *dhi = min(max(tile_hi[t], *dlo), n_docs - 1);
 }
 
+// One wave per tile: the number of scored tokens of the tile.
 template <bool kShifted>
 __global__ void __launch_bounds__(kThreads)
 count_kernel(const uint8_t* __restrict__ corrupted, int64_t n, const int32_t* __restrict__ cu,
              int32_t n_docs, const int32_t* __restrict__ tile_lo, const int32_t* __restrict__ tile_hi,
-             int32_t* __restrict__ tile_counts) {
-  __shared__ int32_t s_cu[kLdsDocs + 1];
-  __shared__ int s_sum[kWaves];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * kTile;
-  const int64_t t1 = min(t0 + kTile, n);
-  const int64_t g0 = t0 + (int64_t)tid * kTokPerThread;
+             int64_t n_tiles, int32_t* __restrict__ tile_counts) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (t >= n_tiles) return;
+  const int64_t t0 = t * kTile, t1 = min(t0 + kTile, n);
   int cnt = 0;
-  if (g0 < n) {
-    uint8_t m[kTokPerThread];
-    load_mask(corrupted, g0, (int)min<int64_t>(kTokPerThread, n - g0), m);
+  if (t1 - t0 == kTile && ((uintptr_t)corrupted % 16) == 0) {
+    uint4 v[4];
 #pragma unroll
-    for (int k = 0; k < kTokPerThread; ++k) cnt += m[k] != 0;
+    for (int i = 0; i < 4; ++i)
+      v[i] = *reinterpret_cast<const uint4*>(corrupted + t0 + 1024 * i + 16 * lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      cnt += nonzero_bytes(v[i].x) + nonzero_bytes(v[i].y) + nonzero_bytes(v[i].z) +
+             nonzero_bytes(v[i].w);
+  } else {
+    for (int64_t g = t0 + lane; g < t1; g += 64) cnt += corrupted[g] != 0;
   }
   if (kShifted) {
     // a corrupted first token of a (non-empty) document is not scored
     int dlo, dhi;
-    const bool cached = tile_docs(cu, n_docs, tile_lo, tile_hi, &dlo, &dhi, s_cu);
-    const int nd = dhi - dlo + 1;
-    for (int i = tid; i < nd; i += kThreads) {
-      const int64_t beg = cached ? s_cu[i] : cu[dlo + i];
-      const int64_t end = cached ? s_cu[i + 1] : cu[dlo + i + 1];
+    tile_range(tile_lo, tile_hi, n_docs, t, &dlo, &dhi);
+    for (int i = dlo + lane; i <= dhi; i += 64) {
+      const int64_t beg = cu[i], end = cu[i + 1];
       if (beg < end && beg >= t0 && beg < t1 && corrupted[beg]) --cnt;
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off, 64);
-  if (lane == 0) s_sum[wave] = cnt;
-  __syncthreads();
-  if (tid == 0) {
-    int t = 0;
-    for (int i = 0; i < kWaves; ++i) t += s_sum[i];
-    tile_counts[blockIdx.x] = t;
-  }
+  cnt = wave_sum(cnt);
+  if (lane == 0) tile_counts[t] = cnt;
 }
 
-// Exclusive scan of the per-tile counts in place (one block; each thread
-// takes a run of consecutive counts per pass), total -> n_rows.
-constexpr int kScanRun = 32;
-__global__ void __launch_bounds__(kScanThreads)
-scan_kernel(int32_t* __restrict__ tile_counts, int64_t n_tiles, int32_t* __restrict__ n_rows) {
-  __shared__ int64_t s_wave[kScanThreads / 64];
-  __shared__ int64_t s_carry;
+// Per group of 1024 tiles: counts -> exclusive offsets within the group (in
+// place) and the group's total.
+__global__ void __launch_bounds__(kGroup)
+group_scan_kernel(int32_t* __restrict__ tile_counts, int64_t n_tiles,
+                  int32_t* __restrict__ group_sums) {
+  __shared__ int s_wave[kGroup / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) s_carry = 0;
-  __syncthreads();
-  for (int64_t base = 0; base < n_tiles; base += (int64_t)kScanThreads * kScanRun) {
-    const int64_t i0 = base + (int64_t)tid * kScanRun;
-    int32_t v[kScanRun];
-    int64_t run = 0;
+  const int64_t i = (int64_t)blockIdx.x * kGroup + tid;
+  const int v = i < n_tiles ? tile_counts[i] : 0;
+  int incl = v;
 #pragma unroll
-    for (int k = 0; k < kScanRun; ++k) {
-      v[k] = i0 + k < n_tiles ? tile_counts[i0 + k] : 0;
-      run += v[k];
-    }
-    int64_t incl = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int64_t y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    if (lane == 63) s_wave[wave] = incl;
-    __syncthreads();
-    int64_t before = s_carry, total = 0;
-    for (int wv = 0; wv < kScanThreads / 64; ++wv) {
-      if (wv < wave) before += s_wave[wv];
-      total += s_wave[wv];
-    }
-    int64_t acc = before + incl - run;
-#pragma unroll
-    for (int k = 0; k < kScanRun; ++k) {
-      if (i0 + k < n_tiles) tile_counts[i0 + k] = (int32_t)acc;
-      acc += v[k];
-    }
-    __syncthreads();
-    if (tid == 0) s_carry += total;
-    __syncthreads();
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
   }
-  if (tid == 0) *n_rows = (int32_t)s_carry;
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kGroup / 64; ++w) {
+    const int x = s_wave[w];
+    if (w < wave) before += x;
+    total += x;
+  }
+  if (i < n_tiles) tile_counts[i] = before + incl - v;
+  if (tid == 0) group_sums[blockIdx.x] = total;
+}
+
+// Weight 1 / (p N) of a document, in fp64 then rounded once to fp32.
+__device__ __forceinline__ float doc_weight(double p, int64_t n) {
+  return (float)(1.0 / (p * (double)n));
 }
 
 // Scatter: four rounds per tile; in round j thread t owns the 4 consecutive
-// tokens at 1024 j + 4 t, so every load is contiguous across the wave.  Each
-// round ranks its scored tokens with a block scan, stages them in LDS and
-// writes them at the tile offset plus the rounds before it.
-constexpr int kRoundTok = kThreads * 4;  // 1024
+// tokens at 1024 j + 4 t, so every load is contiguous across the wave.
 template <bool kShifted, bool kVec>
 __global__ void __launch_bounds__(kThreads)
 scatter_kernel(const uint8_t* __restrict__ corrupted, const int32_t* __restrict__ x0, int64_t n,
                const int32_t* __restrict__ cu, int32_t n_docs,
                const int32_t* __restrict__ tile_lo, const int32_t* __restrict__ tile_hi,
-               const double* __restrict__ p_doc,
-               const int32_t* __restrict__ tile_offsets, int32_t* __restrict__ row_idx,
-               int32_t* __restrict__ tgt, float* __restrict__ w) {
-  __shared__ int s_wave_sum[kWaves];
+               const double* __restrict__ p_doc, const int32_t* __restrict__ tile_offsets,
+               const int32_t* __restrict__ group_sums, int32_t n_groups,
+               int32_t* __restrict__ row_idx, int32_t* __restrict__ tgt, float* __restrict__ w,
+               int32_t* __restrict__ n_rows) {
   __shared__ int32_t s_cu[kLdsDocs + 1];
-  __shared__ int32_t s_row[kRoundTok];
-  __shared__ int32_t s_tgt[kRoundTok];
-  __shared__ float s_w[kRoundTok];
+  __shared__ float s_wd[kLdsDocs];
+  __shared__ int s_wsum[kBufs][kWaves];
+  __shared__ int32_t s_row[kBufs][kRoundTok];
+  __shared__ int32_t s_tgt[kBufs][kRoundTok];
+  __shared__ float s_w[kBufs][kRoundTok];
+  __shared__ int s_base;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t0 = (int64_t)blockIdx.x * kTile;
+  const int64_t tile = blockIdx.x;
+  const int64_t t0 = tile * kTile;
   int dlo, dhi;
-  const bool cached = tile_docs(cu, n_docs, tile_lo, tile_hi, &dlo, &dhi, s_cu);
+  tile_range(tile_lo, tile_hi, n_docs, tile, &dlo, &dhi);
   const int nd = dhi - dlo + 1;
-  int64_t out = tile_offsets[blockIdx.x];
+  const bool cached = nd <= kLdsDocs;
+  if (cached) {
+    for (int i = tid; i <= nd; i += kThreads) s_cu[i] = cu[dlo + i];
+    for (int i = tid; i < nd; i += kThreads) s_wd[i] = doc_weight(p_doc[dlo + i], n);
+  }
+  const int grp = (int)(tile / kGroup);
+  if (wave == 0) {
+    // this tile's offset: its place in its group plus the groups before it
+    int b = 0;
+    for (int g = lane; g < grp; g += 64) b += group_sums[g];
+    b = wave_sum(b);
+    if (lane == 0) s_base = b + tile_offsets[tile];
+  } else if (wave == 1 && tile == 0) {
+    int tot = 0;
+    for (int g = lane; g < n_groups; g += 64) tot += group_sums[g];
+    tot = wave_sum(tot);
+    if (lane == 0) *n_rows = tot;
+  }
+  __syncthreads();
+  int64_t out = s_base;
 
   for (int j = 0; j < kTile / kRoundTok; ++j) {
+    const int buf = j % kBufs;
     const int64_t g0 = t0 + (int64_t)kRoundTok * j + 4 * tid;
+    const int64_t gw = t0 + (int64_t)kRoundTok * j + 256 * wave;
     uint32_t sel = 0;
     int32_t vals[4] = {0, 0, 0, 0};
     float wts[4] = {0.f, 0.f, 0.f, 0.f};
-    if (g0 < n) {
-      const int cnt_here = (int)min<int64_t>(4, n - g0);
-      uint8_t m[4];
-      if (kVec && cnt_here == 4) {
-        const uint32_t mv = *reinterpret_cast<const uint32_t*>(corrupted + g0);
-        const int4 xv = *reinterpret_cast<const int4*>(x0 + g0);
+    uint32_t mv = 0;  // mask byte k in bits 8k..8k+7
+    const int cnt_here = g0 < n ? (int)min<int64_t>(4, n - g0) : 0;
+    if (kVec && cnt_here == 4) {
+      mv = *reinterpret_cast<const uint32_t*>(corrupted + g0);
+      const int4 xv = *reinterpret_cast<const int4*>(x0 + g0);
+      vals[0] = xv.x; vals[1] = xv.y; vals[2] = xv.z; vals[3] = xv.w;
+    } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) m[k] = (mv >> (8 * k)) & 0xff;
-        vals[0] = xv.x; vals[1] = xv.y; vals[2] = xv.z; vals[3] = xv.w;
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          m[k] = k < cnt_here ? corrupted[g0 + k] : 0;
-          vals[k] = k < cnt_here ? x0[g0 + k] : 0;
+      for (int k = 0; k < 4; ++k)
+        if (k < cnt_here) {
+          mv |= (uint32_t)(corrupted[g0 + k] != 0) << (8 * k);
+          vals[k] = x0[g0 + k];
         }
-      }
-      if (m[0] | m[1] | m[2] | m[3]) {
-        int d = cached ? lds_find_doc(s_cu, nd, g0) : find_doc(cu, dlo, dhi, g0) - dlo;
-        int64_t d_beg = cached ? s_cu[d] : cu[dlo + d];
-        int64_t d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
-        float wd = (float)(1.0 / (p_doc[dlo + d] * (double)n));
+    }
+    bool done = false;
+    if (kVec && cached && gw + 256 <= n) {
+      // wave-uniform: the round's 256 tokens of this wave touch local
+      // documents dw .. dw + span
+      const int dw = lds_find_doc(s_cu, nd, gw);
+      const int span = lds_find_doc(s_cu, nd, gw + 255) - dw;
+      if (span <= 3) {
+        const int64_t b0 = s_cu[dw], b1 = s_cu[dw + 1];
+        const int64_t b2 = span >= 2 ? (int64_t)s_cu[dw + 2] : INT64_MAX;
+        const int64_t b3 = span >= 3 ? (int64_t)s_cu[dw + 3] : INT64_MAX;
+        const float w0 = s_wd[dw], w1 = s_wd[dw + min(span, 1)];
+        const float w2 = s_wd[dw + min(span, 2)], w3 = s_wd[dw + span];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int64_t g = g0 + k;
-          if (k < cnt_here && m[k]) {
-            if (g >= d_end) {
-              // (bounded by the last document even if cu_seqlens is malformed)
-              do {
-                ++d;
-                d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
-              } while (g >= d_end && d < nd - 1);
-              d_beg = cached ? s_cu[d] : cu[dlo + d];
-              wd = (float)(1.0 / (p_doc[dlo + d] * (double)n));
-            }
-            if (!kShifted || g != d_beg) {
-              sel |= 1u << k;
-              wts[k] = wd;
-            }
+          const int idx = (int)(g >= b1) + (int)(g >= b2) + (int)(g >= b3);
+          const int64_t beg = idx == 0 ? b0 : idx == 1 ? b1 : idx == 2 ? b2 : b3;
+          const float wk = idx == 0 ? w0 : idx == 1 ? w1 : idx == 2 ? w2 : w3;
+          if (((mv >> (8 * k)) & 0xffu) && (!kShifted || g != beg)) {
+            sel |= 1u << k;
+            wts[k] = wk;
+          }
+        }
+        done = true;
+      }
+    }
+    if (!done && mv != 0) {
+      int d = cached ? lds_find_doc(s_cu, nd, g0) : find_doc(cu, dlo, dhi, g0) - dlo;
+      int64_t d_beg = cached ? s_cu[d] : cu[dlo + d];
+      int64_t d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
+      float wd = cached ? s_wd[d] : doc_weight(p_doc[dlo + d], n);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t g = g0 + k;
+        if (k < cnt_here && ((mv >> (8 * k)) & 0xffu)) {
+          if (g >= d_end) {
+            // (bounded by the last document even if cu_seqlens is malformed)
+            do {
+              ++d;
+              d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
+            } while (g >= d_end && d < nd - 1);
+            d_beg = cached ? s_cu[d] : cu[dlo + d];
+            wd = cached ? s_wd[d] : doc_weight(p_doc[dlo + d], n);
+          }
+          if (!kShifted || g != d_beg) {
+            sel |= 1u << k;
+            wts[k] = wd;
           }
         }
       }
     }
-    const int cnt = __popc(sel);
 
-    // block-exclusive scan of the per-thread counts
-    int incl = cnt;
+    // rank: selected tokens of lower lanes in the wave, then lower waves
+    int below = 0, wave_total = 0;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
+    for (int k = 0; k < 4; ++k) {
+      const uint64_t b = __ballot((sel >> k) & 1u);
+      below += lanes_below(b);
+      wave_total += __popcll(b);
     }
-    if (lane == 63) s_wave_sum[wave] = incl;
+    if (lane == 0) s_wsum[buf][wave] = wave_total;
     __syncthreads();
-    int wave_off = 0, round_total = 0;
+    int pos = below, round_total = 0;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) {
-      const int v = s_wave_sum[i];
-      if (i < wave) wave_off += v;
+      const int v = s_wsum[buf][i];
+      if (i < wave) pos += v;
       round_total += v;
     }
-    int pos = wave_off + incl - cnt;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (sel & (1u << k)) {
         const int64_t g = g0 + k;
-        s_row[pos] = (int32_t)(kShifted ? g - 1 : g);
-        s_tgt[pos] = vals[k];
-        s_w[pos] = wts[k];
+        s_row[buf][pos] = (int32_t)(kShifted ? g - 1 : g);
+        s_tgt[buf][pos] = vals[k];
+        s_w[buf][pos] = wts[k];
         ++pos;
       }
     }
     __syncthreads();
     for (int i = tid; i < round_total; i += kThreads) {
-      row_idx[out + i] = s_row[i];
-      tgt[out + i] = s_tgt[i];
-      w[out + i] = s_w[i];
+      row_idx[out + i] = s_row[buf][i];
+      tgt[out + i] = s_tgt[buf][i];
+      w[out + i] = s_w[buf][i];
     }
     out += round_total;
-    __syncthreads();  // staging and wave sums are reused by the next round
+    // with one buffer, the next round's staging must wait for this copy
+    if (kBufs == 1) __syncthreads();
   }
 }
 
@@ -295,7 +331,9 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const int32_t* __restrict_
 size_t compact_workspace_bytes(int64_t n_tokens) {
   if (n_tokens <= 0) return 0;
   const int64_t tiles = (n_tokens + kTile - 1) / kTile;
-  return 3 * (size_t)tiles * sizeof(int32_t);  // counts, first and last document
+  const int64_t groups = (tiles + kGroup - 1) / kGroup;
+  // counts, first and last document per tile; one total per group
+  return (3 * (size_t)tiles + (size_t)groups) * sizeof(int32_t);
 }
 
 hipError_t launch_compact(const uint8_t* corrupted, const int32_t* x0, int64_t n,
@@ -307,34 +345,35 @@ hipError_t launch_compact(const uint8_t* corrupted, const int32_t* x0, int64_t n
     return hipGetLastError();
   }
   const int64_t tiles = (n + kTile - 1) / kTile;
+  const int64_t groups = (tiles + kGroup - 1) / kGroup;
   int32_t* counts = reinterpret_cast<int32_t*>(workspace);
   int32_t* tile_lo = counts + tiles;
   int32_t* tile_hi = tile_lo + tiles;
-  const unsigned grid = (unsigned)tiles;
+  int32_t* group_sums = tile_hi + tiles;
   tile_docs_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(cu, n_docs, n,
                                                                                 tile_lo, tile_hi);
+  const unsigned count_grid = (unsigned)((tiles + kWaves - 1) / kWaves);
+  const bool shifted = align == MDLM_SHIFTED;
+  if (shifted)
+    count_kernel<true><<<count_grid, kThreads, 0, stream>>>(corrupted, n, cu, n_docs, tile_lo,
+                                                            tile_hi, tiles, counts);
+  else
+    count_kernel<false><<<count_grid, kThreads, 0, stream>>>(corrupted, n, cu, n_docs, tile_lo,
+                                                             tile_hi, tiles, counts);
+  group_scan_kernel<<<(unsigned)groups, kGroup, 0, stream>>>(counts, tiles, group_sums);
   const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)corrupted % 4 == 0);
-  if (align == MDLM_SHIFTED) {
-    count_kernel<true><<<grid, kThreads, 0, stream>>>(corrupted, n, cu, n_docs, tile_lo, tile_hi,
-                                                      counts);
-    scan_kernel<<<1, kScanThreads, 0, stream>>>(counts, tiles, n_rows);
-    if (vec)
-      scatter_kernel<true, true><<<grid, kThreads, 0, stream>>>(
-          corrupted, x0, n, cu, n_docs, tile_lo, tile_hi, p_doc, counts, row_idx, tgt, w);
-    else
-      scatter_kernel<true, false><<<grid, kThreads, 0, stream>>>(
-          corrupted, x0, n, cu, n_docs, tile_lo, tile_hi, p_doc, counts, row_idx, tgt, w);
+#define MDLM_SCATTER_LAUNCH(SH, VEC)                                                           \
+  scatter_kernel<SH, VEC><<<(unsigned)tiles, kThreads, 0, stream>>>(                           \
+      corrupted, x0, n, cu, n_docs, tile_lo, tile_hi, p_doc, counts, group_sums, (int32_t)groups, \
+      row_idx, tgt, w, n_rows)
+  if (shifted) {
+    if (vec) MDLM_SCATTER_LAUNCH(true, true);
+    else MDLM_SCATTER_LAUNCH(true, false);
   } else {
-    count_kernel<false><<<grid, kThreads, 0, stream>>>(corrupted, n, cu, n_docs, tile_lo,
-                                                       tile_hi, counts);
-    scan_kernel<<<1, kScanThreads, 0, stream>>>(counts, tiles, n_rows);
-    if (vec)
-      scatter_kernel<false, true><<<grid, kThreads, 0, stream>>>(
-          corrupted, x0, n, cu, n_docs, tile_lo, tile_hi, p_doc, counts, row_idx, tgt, w);
-    else
-      scatter_kernel<false, false><<<grid, kThreads, 0, stream>>>(
-          corrupted, x0, n, cu, n_docs, tile_lo, tile_hi, p_doc, counts, row_idx, tgt, w);
+    if (vec) MDLM_SCATTER_LAUNCH(false, true);
+    else MDLM_SCATTER_LAUNCH(false, false);
   }
+#undef MDLM_SCATTER_LAUNCH
   return hipGetLastError();
 }
 

@@ -10,17 +10,22 @@
 // the 4 consecutive tokens starting at 4 (t + 256 j), exactly the output of one
 // Philox call per stream, and a wave's loads and stores are contiguous.  The
 // documents a block touches are found once by a wave-wide search and their
-// offsets cached in LDS; corrupted counts are summed per wave and document
-// before one LDS atomic, and one global atomic per (block, document).
+// offsets and thresholds cached in LDS; corrupted counts are summed per wave
+// and document before one LDS atomic, and one global atomic per (block,
+// document).  A wave whose 256 tokens share a document takes a branch-free
+// path (the kernel is bound by instruction issue, not by memory, otherwise).
 #include "mdlm_internal.h"
 
 namespace mdlm {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRounds = 4;
-constexpr int kTokPerBlock = kThreads * 4 * kRounds;  // 4096
-constexpr int kLdsDocs = 2048;                        // documents cached per block
+#ifndef MDLM_CORRUPT_ROUNDS
+#define MDLM_CORRUPT_ROUNDS 4
+#endif
+constexpr int kRounds = MDLM_CORRUPT_ROUNDS;
+constexpr int kTokPerBlock = kThreads * 4 * kRounds;  // 4096 by default
+constexpr int kLdsDocs = 1024;                        // documents cached per block
 
 __global__ void __launch_bounds__(kThreads)
 noise_level_kernel(int32_t n_docs, uint32_t k0, uint32_t k1, double eps,
@@ -48,6 +53,50 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
+// Four consecutive tokens g0..g0+3 (g0 a multiple of 4), loaded as v, with
+// Bernoulli thresholds t0..t3: writes xt and the mask bytes and returns the
+// four corruption flags as bits 0, 8, 16, 24.
+template <bool kUniform>
+__device__ __forceinline__ uint32_t corrupt4_core(int4 v, int64_t g0, uint32_t t0, uint32_t t1,
+                                                  uint32_t t2, uint32_t t3, uint32_t k0,
+                                                  uint32_t k1, int32_t mask_id,
+                                                  uint32_t rand_vocab, int32_t* __restrict__ xt,
+                                                  uint8_t* __restrict__ corrupted) {
+  const uint64_t q = (uint64_t)g0 >> 2;
+  const uint4 r1 =
+      philox4x32_10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagBernoulli), k0, k1);
+  uint4 r2 = make_uint4(0, 0, 0, 0);
+  if (kUniform)
+    r2 = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagReplace), k0, k1);
+  const bool c0 = (r1.x >> 8) < t0, c1 = (r1.y >> 8) < t1;
+  const bool c2 = (r1.z >> 8) < t2, c3 = (r1.w >> 8) < t3;
+  auto repl = [&](uint32_t w2) {
+    return kUniform ? (int32_t)(((uint64_t)w2 * rand_vocab) >> 32) : mask_id;
+  };
+  *reinterpret_cast<int4*>(xt + g0) =
+      make_int4(c0 ? repl(r2.x) : v.x, c1 ? repl(r2.y) : v.y, c2 ? repl(r2.z) : v.z,
+                c3 ? repl(r2.w) : v.w);
+  const uint32_t bits =
+      (uint32_t)c0 | ((uint32_t)c1 << 8) | ((uint32_t)c2 << 16) | ((uint32_t)c3 << 24);
+  *reinterpret_cast<uint32_t*>(corrupted + g0) = bits;
+  return bits;
+}
+
+// corrupt4_core for four tokens of one document (threshold thr); returns the
+// wave's corrupted count (every lane of the wave must call it).
+template <bool kUniform>
+__device__ __forceinline__ int corrupt4(int4 v, int64_t g0, uint32_t thr, uint32_t k0,
+                                        uint32_t k1, int32_t mask_id, uint32_t rand_vocab,
+                                        int32_t* __restrict__ xt,
+                                        uint8_t* __restrict__ corrupted) {
+  const uint32_t bits = corrupt4_core<kUniform>(v, g0, thr, thr, thr, thr, k0, k1, mask_id,
+                                                rand_vocab, xt, corrupted);
+  int c = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c += __popcll(__ballot((bits >> (8 * k)) & 1u));
+  return c;
+}
+
 template <bool kUniform, bool kVec>
 __global__ void __launch_bounds__(kThreads)
 corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restrict__ cu,
@@ -57,6 +106,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
   __shared__ int s_dlo, s_dhi;
   __shared__ int32_t s_cu[kLdsDocs + 1];
   __shared__ int s_cnt[kLdsDocs];
+  __shared__ uint32_t s_thr[kLdsDocs];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t blk0 = (int64_t)blockIdx.x * kTokPerBlock;
@@ -73,12 +123,78 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
   const bool cached = nd <= kLdsDocs;
   if (cached) {
     for (int i = tid; i <= nd; i += kThreads) s_cu[i] = cu[dlo + i];
-    for (int i = tid; i < nd; i += kThreads) s_cnt[i] = 0;
+    for (int i = tid; i < nd; i += kThreads) {
+      s_cnt[i] = 0;
+      s_thr[i] = threshold_of(p_doc[dlo + i]);
+    }
   }
   __syncthreads();
+  // Bernoulli threshold of local document d (from LDS when cached)
+  auto thr_of = [&](int d) { return cached ? s_thr[d] : threshold_of(p_doc[dlo + d]); };
+
+  // Whole block in one document: all four rounds' loads are issued first.
+  if (kVec && cached && nd == 1 && blk1 - blk0 == kTokPerBlock) {
+    int4 v[kRounds];
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j)
+      v[j] = *reinterpret_cast<const int4*>(x0 + blk0 + 4 * (int64_t)(tid + kThreads * j));
+    const uint32_t thr = s_thr[0];
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j)
+      c += corrupt4<kUniform>(v[j], blk0 + 4 * (int64_t)(tid + kThreads * j), thr, k0, k1,
+                              mask_id, rand_vocab, xt, corrupted);
+    if (lane == 0 && c) atomicAdd(&doc_counts[dlo], c);
+    return;
+  }
 
   for (int j = 0; j < kRounds; ++j) {
     const int64_t g0 = blk0 + 4 * (int64_t)(tid + kThreads * j);
+    // Fast paths for a wave whose 256 tokens all exist (wave-uniform tests):
+    // all in one document (one threshold, ballot counts), or spread over at
+    // most four documents (per-token document index from three wave-uniform
+    // boundaries, ballot counts per document).  Neither walks or branches
+    // per token.
+    const int64_t gw = blk0 + 4 * (int64_t)(64 * wave + kThreads * j);
+    if (kVec && cached && gw + 256 <= n) {
+      const int dw = lds_find_doc(s_cu, nd, gw);
+      const int4 v = *reinterpret_cast<const int4*>(x0 + g0);
+      if (gw + 256 <= (int64_t)s_cu[dw + 1]) {
+        const int c = corrupt4<kUniform>(v, g0, s_thr[dw], k0, k1, mask_id, rand_vocab, xt,
+                                         corrupted);
+        if (lane == 0 && c) atomicAdd(&s_cnt[dw], c);
+        continue;
+      }
+      const int span = lds_find_doc(s_cu, nd, gw + 255) - dw;
+      if (span <= 3) {
+        // start of local documents dw+1..dw+3 (past the span: never reached)
+        const int64_t b1 = s_cu[dw + 1];
+        const int64_t b2 = span >= 2 ? (int64_t)s_cu[dw + 2] : INT64_MAX;
+        const int64_t b3 = span >= 3 ? (int64_t)s_cu[dw + 3] : INT64_MAX;
+        const uint32_t th0 = s_thr[dw], th1 = s_thr[dw + 1];
+        const uint32_t th2 = s_thr[dw + min(span, 2)], th3 = s_thr[dw + span];
+        int idx[4];
+        uint32_t tk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int64_t g = g0 + k;
+          idx[k] = (int)(g >= b1) + (int)(g >= b2) + (int)(g >= b3);
+          tk[k] = idx[k] == 0 ? th0 : idx[k] == 1 ? th1 : idx[k] == 2 ? th2 : th3;
+        }
+        const uint32_t bits = corrupt4_core<kUniform>(v, g0, tk[0], tk[1], tk[2], tk[3], k0, k1,
+                                                      mask_id, rand_vocab, xt, corrupted);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i > span) break;
+          int c = 0;
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            c += __popcll(__ballot(((bits >> (8 * k)) & 1u) && idx[k] == i));
+          if (lane == 0 && c) atomicAdd(&s_cnt[dw + i], c);
+        }
+        continue;
+      }
+    }
     const bool active = g0 < n;
     int dl[4] = {0, 0, 0, 0};  // local document index of each token (-1: none)
     uint32_t flag_bits = 0;
@@ -104,7 +220,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
       // document of the first token, then walk forward
       int d = cached ? lds_find_doc(s_cu, nd, g0) : find_doc(cu, dlo, s_dhi, g0) - dlo;
       int64_t d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
-      uint32_t thr = threshold_of(p_doc[dlo + d]);
+      uint32_t thr = thr_of(d);
       int32_t out[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -117,7 +233,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
               ++d;
               d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
             } while (g >= d_end && d < nd - 1);
-            thr = threshold_of(p_doc[dlo + d]);
+            thr = thr_of(d);
           }
           dl[k] = d;
           if ((w1[k] >> 8) < thr) {
@@ -136,36 +252,50 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
         }
       }
     }
-    // per-document counts: tokens in the wave's first or last document are
-    // summed across the wave; any others (short documents) are added per lane
-    const int d_first = __shfl(active ? dl[0] : 0x7fffffff, 0, 64);
-    int last_local = -1;
+    // Per-document counts.  Active lanes form a prefix of the wave and their
+    // documents rise with the lane.  When the wave's tokens lie in one
+    // document, ballots count its corrupted tokens; otherwise tokens in the
+    // wave's first or last document are summed across the wave and any others
+    // (short documents) are added per lane.
+    const uint64_t act = __ballot(active);
+    if (act != 0) {
+      int last_local = -1;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) last_local = max(last_local, dl[k]);
-    int d_last = last_local;
+      for (int k = 0; k < 4; ++k) last_local = max(last_local, dl[k]);
+      const int d_first = __shfl(dl[0], 0, 64);
+      const int d_last = __shfl(last_local, 63 - __clzll((long long)act), 64);
+      if (d_first == d_last) {
+        int c = 0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) d_last = max(d_last, __shfl_xor(d_last, off, 64));
-    int c_first = 0, c_last = 0;
+        for (int k = 0; k < 4; ++k) c += __popcll(__ballot((flag_bits >> (8 * k)) & 1u));
+        if (lane == 0 && c) {
+          if (cached) atomicAdd(&s_cnt[d_first], c);
+          else atomicAdd(&doc_counts[dlo + d_first], c);
+        }
+      } else {
+        int c_first = 0, c_last = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int bit = (flag_bits >> (8 * k)) & 1;
-      if (dl[k] == d_first) c_first += bit;
-      else if (dl[k] == d_last) c_last += bit;
-      else if (dl[k] >= 0 && bit) {
-        if (cached) atomicAdd(&s_cnt[dl[k]], 1);
-        else atomicAdd(&doc_counts[dlo + dl[k]], 1);
-      }
-    }
-    c_first = wave_sum(c_first);
-    c_last = wave_sum(c_last);
-    if (lane == 0) {
-      if (c_first && d_first >= 0 && d_first != 0x7fffffff) {
-        if (cached) atomicAdd(&s_cnt[d_first], c_first);
-        else atomicAdd(&doc_counts[dlo + d_first], c_first);
-      }
-      if (c_last && d_last >= 0) {
-        if (cached) atomicAdd(&s_cnt[d_last], c_last);
-        else atomicAdd(&doc_counts[dlo + d_last], c_last);
+        for (int k = 0; k < 4; ++k) {
+          const int bit = (flag_bits >> (8 * k)) & 1;
+          if (dl[k] == d_first) c_first += bit;
+          else if (dl[k] == d_last) c_last += bit;
+          else if (dl[k] >= 0 && bit) {
+            if (cached) atomicAdd(&s_cnt[dl[k]], 1);
+            else atomicAdd(&doc_counts[dlo + dl[k]], 1);
+          }
+        }
+        c_first = wave_sum(c_first);
+        c_last = wave_sum(c_last);
+        if (lane == 0) {
+          if (c_first) {
+            if (cached) atomicAdd(&s_cnt[d_first], c_first);
+            else atomicAdd(&doc_counts[dlo + d_first], c_first);
+          }
+          if (c_last) {
+            if (cached) atomicAdd(&s_cnt[d_last], c_last);
+            else atomicAdd(&doc_counts[dlo + d_last], c_last);
+          }
+        }
       }
     }
   }

@@ -78,6 +78,27 @@ def lognormal_lengths(rng, mean, total=None, count=None, lo=16, hi=4096):
     return out
 
 
+def lognormal_stream_offsets(seed, mean, total, lo=16, hi=4096):
+    """Document offsets (cu_seqlens, int64) of a ``total``-token stream whose
+    lengths are lognormal with arithmetic mean ``mean`` and sigma 1, rounded
+    and clipped to [lo, hi], the last one trimmed so the lengths sum to
+    ``total``.  Vectorised, for bandwidth-sized streams."""
+    rng = np.random.default_rng(seed)
+    mu = math.log(mean) - 0.5
+    chunks, s = [], 0
+    while s < total:
+        x = np.clip(np.rint(rng.lognormal(mu, 1.0, size=max(1024, 2 * total // mean))), lo, hi)
+        x = x.astype(np.int64)
+        chunks.append(x)
+        s += int(x.sum())
+    lengths = np.concatenate(chunks)
+    c = np.cumsum(lengths)
+    k = int(np.searchsorted(c, total))
+    lengths = lengths[:k + 1].copy()
+    lengths[-1] -= int(c[k] - total)
+    return np.concatenate([[0], np.cumsum(lengths)])
+
+
 def make_workload(k):
     """The five named workloads, by index 1..5."""
     rng = np.random.default_rng(1000 + k)
