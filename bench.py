@@ -48,12 +48,15 @@ def parse():
     p.add_argument("--workload", type=int, default=2)
     p.add_argument("--align", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-achievable", action="store_true",
+                   help="skip the achievable-peak probes (copy, MFMA loop, library GEMM)")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--bandwidth-tokens", type=int, default=1 << 27,
                    help="tokens of the corruption/compaction bandwidth run (0 = skip)")
     p.add_argument("--calibrate-copy", type=int, default=0,
-                   help="before timing, copy this many MiB device-to-device once, so "
-                        "counter runs can scale their byte counts by a known transfer")
+                   help="before timing, copy this many MiB once with the probe library's "
+                        "copy kernel, so counter runs can scale their byte counts by a "
+                        "known transfer")
     p.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles",
                                                           "head_ce_traffic.json"),
                    help="measured HBM traffic of the fused call, if current")
@@ -172,6 +175,56 @@ def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
                 compact_frac=b_cmp / t_cmp / 1e9 / PEAK_HBM_GBS)
 
 
+def achievable(dev, gemm_shape=None):
+    """Measured achievable peaks on this GPU, beside the datasheet ones: the
+    one-pass streaming copy and the MFMA issue loop of libmdlm_probe.so, and
+    (context only) a library bf16 GEMM of the forward logits' shape."""
+    import torch
+    from uniform_noise_diffusion_amd import probe
+    n = 2 << 30
+    a = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    probe.copy(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        probe.copy(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(4 * cus * 8, dtype=torch.float32, device=dev)
+    probe.mfma(out, 4 * cus, 2000)
+    torch.cuda.synchronize()
+    e0.record()
+    fl = probe.mfma(out, 4 * cus, 20000)
+    e1.record()
+    torch.cuda.synchronize()
+    mfma_tf = fl / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    res = dict(copy_GBs=copy_gbs, mfma_bf16_tflops=mfma_tf,
+               how=("copy: 2 GiB, one 16-byte element per thread, mean of 5; mfma: "
+                    f"{4 * cus} workgroups x 8 waves, 8 independent 32x32x16 bf16 MFMA chains "
+                    "per wave from registers (no memory traffic)"))
+    if gemm_shape is not None:
+        V, H, M = gemm_shape
+        A = torch.randn(V, H, device=dev).to(torch.bfloat16)
+        B = torch.randn(M, H, device=dev).to(torch.bfloat16)
+        C = A @ B.t().contiguous()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            C = A @ B.t().contiguous()
+        e1.record()
+        torch.cuda.synchronize()
+        res["library_gemm_tflops"] = 2.0 * V * H * M * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        res["library_gemm"] = (f"torch.matmul (hipBLASLt) bf16 [{V} x {H}] x [{H} x {M}], the "
+                               "forward logits' shape, output written; context, not a target")
+        del A, B, C
+    return res
+
+
 def cpu_baseline(inp, mean_rows, seconds):
     """The fp64 oracle, as it stands, on a bounded sample of the workload.
 
@@ -239,10 +292,13 @@ def main():
     log(f"generating workload {wl.name}: N={wl.n_tokens} H={wl.H} V={wl.V}")
     inp = WL.generate(wl)
     if args.calibrate_copy:
+        # one dispatch of the probe library's copy kernel over a known byte
+        # count, for scaling counter runs
+        from uniform_noise_diffusion_amd import probe
         n = args.calibrate_copy << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        probe.copy(src, dst)
         torch.cuda.synchronize()
         log(f"calibration copy of {n} bytes done")
         del src, dst
@@ -282,11 +338,22 @@ def main():
                            softcap=wl.softcap, eps=wl.eps, seeds=f"0..{K - 1}",
                            mean_scored_rows=float(rows.mean()), parallelism="none (1 GPU)"),
                roofline=roofline)
+    if not args.no_achievable:
+        log("measuring achievable peaks")
+        ach = achievable(dev, (wl.V, wl.H, int(round(rows.mean()))))
+        out["achievable"] = ach
+        roofline["frac_of_achievable"] = achieved / ach["mfma_bf16_tflops"]
+        roofline["executed_frac_of_achievable"] = executed / ach["mfma_bf16_tflops"]
     if args.bandwidth_tokens:
         log("timing corruption/compaction bandwidth")
         out["corrupt_compact_hbm"] = bandwidth(args.bandwidth_tokens, dev)
         out["corrupt_compact_hbm_lognormal296"] = bandwidth(args.bandwidth_tokens, dev,
                                                             doc_mean=296)
+        if "achievable" in out:
+            for k in ("corrupt_compact_hbm", "corrupt_compact_hbm_lognormal296"):
+                for op in ("corrupt", "compact"):
+                    out[k][f"{op}_frac_of_achievable_copy"] = (
+                        out[k][f"{op}_GBs"] / out["achievable"]["copy_GBs"])
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(inp, rows.mean(), args.cpu_seconds)

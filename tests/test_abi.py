@@ -193,6 +193,23 @@ def test_error_is_cleared_by_next_call(lib):
     assert "alignment" in B.mdlm_last_error()
 
 
+def test_probe_library_exports_its_header():
+    from uniform_noise_diffusion_amd import probe
+    if not os.path.exists(probe.PROBE_LIB_PATH):
+        pytest.skip("libmdlm_probe.so not built")
+    text = open(os.path.join(ROOT, "include", "mdlm_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(mdlm_\w+)\s*\(", text)))
+    assert set(names) == set(probe.EXPORTED)
+    lib = probe.load()
+    for n in names:
+        assert hasattr(lib, n), n
+    # invalid launch shapes are refused before anything is enqueued
+    assert lib.mdlm_probe_mfma(None, 0, 1, None) != 0
+    assert lib.mdlm_probe_mfma(None, 1, 0, None) != 0
+    assert lib.mdlm_probe_copy(None, None, 0, None) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))

@@ -1,7 +1,9 @@
-"""Builds libmdlm.so, the HIP library behind include/mdlm.h, for gfx950.
+"""Builds the HIP libraries for gfx950: libmdlm.so (include/mdlm.h, the loss
+path) and libmdlm_probe.so (include/mdlm_probe.h, the achievable-peak
+measurement kernels).
 
-Run as ``python -m uniform_noise_diffusion_amd.build``.  The library is built
-in-tree next to this file.  Always recompiles.
+Run as ``python -m uniform_noise_diffusion_amd.build``.  The libraries are
+built in-tree next to this file.  Always recompiles.
 """
 
 import os
@@ -15,6 +17,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmdlm.so")
 SOURCES = ["api.hip", "corrupt.hip", "compact.hip", "head_ce.hip"]
+PROBE_LIB_PATH = os.path.join(PKG_DIR, "libmdlm_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = os.environ.get("MDLM_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -33,9 +37,9 @@ def hipcc():
     return path
 
 
-def build(verbose=False):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+def _compile(sources, out, verbose):
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -46,8 +50,14 @@ def build(verbose=False):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose=False):
+    """Compiles both libraries; returns the loss-path library's path."""
+    _compile(PROBE_SOURCES, PROBE_LIB_PATH, verbose)
+    return _compile(SOURCES, LIB_PATH, verbose)
 
 
 if __name__ == "__main__":
