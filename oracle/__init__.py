@@ -31,7 +31,12 @@ from .mdlm import (  # noqa: F401
     noise_levels,
     corrupt,
     compact,
+    compact_rows,
+    WEIGHT_INV_P,
+    WEIGHT_MEAN,
+    WEIGHT_EXAMPLE_MEAN_CLIPPED,
     head_ce,
+    head_ce_weight_grad,
     head_ce_rows,
     mdlm_loss,
 )

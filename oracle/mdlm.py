@@ -162,6 +162,85 @@ def compact(corrupted, x0, cu_seqlens, p_doc, align):
             np.asarray(ws, dtype=np.float64))
 
 
+WEIGHT_INV_P = 0           # 1 / (p_b N), the LLaDA objective
+WEIGHT_MEAN = 1            # 1 / M: unweighted mean over the scored rows
+WEIGHT_EXAMPLE_MEAN_CLIPPED = 2  # min(1 / (1 - p_b), clip), example mean
+
+
+def compact_rows(x0, cu_seqlens, align, corrupted=None, eligible=None, p_doc=None,
+                 weighting=WEIGHT_INV_P, scale=1.0, clip=None):
+    """Scored rows, targets and weights for the loss variants.
+
+    A token g of document b is scored when it is corrupted (every token when
+    ``corrupted`` is None), eligible for the loss (every token when
+    ``eligible`` is None) and, with shifted logits, not the document's first
+    token.  It gives (row g or g-1, target x0[g]) as in ``compact``.
+
+    Weights (fp64, rounded once to fp32 by the library):
+      * WEIGHT_INV_P: scale / (p_b N), N the call's token count ([LLaDA]
+        Objective row, as in ``compact``).
+      * WEIGHT_MEAN: scale / M, M the number of scored rows.  With
+        corrupted=None, shifted logits and scale = lambda this is
+        lambda * (plain causal next-token CE over the clean sequence), the
+        encoder AR term of [Gemma] Finetuning notes; with a mask it is the
+        unweighted mean CE over the corrupted tokens.
+      * WEIGHT_EXAMPLE_MEAN_CLIPPED: scale * min(1 / (1 - p_b), clip) /
+        (n_b * B): the per-example mean of the scored CE weighted by the
+        clipped inverse of one minus the example's rate, averaged over the B
+        examples that have at least one scored row ([Axolotl] objective
+        options: inv_one_minus_t with example_mean, capped by
+        rhine_weight_clip).  The example's corruption rate p_b plays the
+        role of t: under uniform noise the rate is drawn directly as
+        t ~ U(eps, 1) ([Gemma] Finetuning notes).
+        Order of evaluation: a = 1 / (1 - p_b); a = min(a, clip);
+        w = scale * a / (n_b * B).
+
+    Eligibility ([Axolotl] "Packed training": tokens outside the loss, such
+    as prompt tokens, are excluded) applies to the target token g.
+
+    Returns (row_idx int64[M], tgt int64[M], w float64[M]).
+    """
+    x0 = np.asarray(x0, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    n = x0.shape[0]
+    rows, tgts, docs = [], [], []
+    for b in range(cu.shape[0] - 1):
+        for g in range(cu[b], cu[b + 1]):
+            if corrupted is not None and not corrupted[g]:
+                continue
+            if eligible is not None and not eligible[g]:
+                continue
+            if align == SHIFTED:
+                if g == cu[b]:
+                    continue
+                rows.append(g - 1)
+            else:
+                rows.append(g)
+            tgts.append(x0[g])
+            docs.append(b)
+    m = len(rows)
+    ws = []
+    if weighting == WEIGHT_INV_P:
+        p_doc = np.asarray(p_doc, dtype=np.float64)
+        ws = [scale / (p_doc[b] * float(n)) for b in docs]
+    elif weighting == WEIGHT_MEAN:
+        ws = [scale / float(m) for _ in docs]
+    elif weighting == WEIGHT_EXAMPLE_MEAN_CLIPPED:
+        p_doc = np.asarray(p_doc, dtype=np.float64)
+        per_doc = {}
+        for b in docs:
+            per_doc[b] = per_doc.get(b, 0) + 1
+        n_examples = float(len(per_doc))
+        for b in docs:
+            a = 1.0 / (1.0 - p_doc[b])
+            a = min(a, clip)
+            ws.append(scale * a / (float(per_doc[b]) * n_examples))
+    else:
+        raise ValueError(f"unknown weighting {weighting}")
+    return (np.asarray(rows, dtype=np.int64), np.asarray(tgts, dtype=np.int64),
+            np.asarray(ws, dtype=np.float64))
+
+
 def _capped_logits(rows_h, w_chunk, softcap):
     """Logits of the plain linear head, z = h W^T (no bias: [Axolotl]
     "Adapters, merging and inference" requires a plain linear output head),
@@ -239,6 +318,31 @@ def head_ce(hidden, W, row_idx, tgt, w, softcap=0.0, want_grad=True, chunk=8192)
         d_rows += (w[:, None] * prob * dcap) @ wc
     d_hidden[row_idx] = d_rows
     return loss, ce, d_hidden
+
+
+def head_ce_weight_grad(hidden, W, row_idx, tgt, w, softcap=0.0, chunk=8192):
+    """Gradient of loss = sum_j w_j CE_j with respect to the head W, for a
+    head that is trained (the frozen-head case of [LLaDA] forms none):
+        dW_v = sum_j w_j (softmax(zhat_j)_v - [v = tgt_j]) zhat'_jv h_row_j.
+    Returns float64[V, H]."""
+    hidden = np.asarray(hidden)
+    row_idx = np.asarray(row_idx, dtype=np.int64)
+    tgt = np.asarray(tgt, dtype=np.int64)
+    w = np.asarray(w, dtype=np.float64)
+    W = np.asarray(W)
+    dW = np.zeros(W.shape, dtype=np.float64)
+    if row_idx.size == 0:
+        return dW
+    _, lse = head_ce_rows(hidden, W, row_idx, tgt, softcap, chunk)
+    rows_h = hidden[row_idx].astype(np.float64)
+    for v0 in range(0, W.shape[0], chunk):
+        v1 = min(v0 + chunk, W.shape[0])
+        zc, dcap = _capped_logits(rows_h, W[v0:v1].astype(np.float64), softcap)
+        prob = np.exp(zc - lse[:, None])
+        hit = np.flatnonzero((tgt >= v0) & (tgt < v1))
+        prob[hit, tgt[hit] - v0] -= 1.0
+        dW[v0:v1] = (w[:, None] * prob * dcap).T @ rows_h
+    return dW
 
 
 def mdlm_loss(x0, cu_seqlens, hidden, W, seed, eps, noise, mask_id, rand_vocab,
