@@ -123,6 +123,13 @@ int mdlm_corrupt(const int32_t* x0, int64_t n_tokens,
                  int32_t* xt, uint8_t* corrupted, double* p_doc,
                  int32_t* doc_counts, void* stream);
 
+/* Row weightings of mdlm_compact_rows. */
+enum {
+  MDLM_WEIGHT_INV_P = 0,                 /* scale / (p_doc[b] * n_tokens)        */
+  MDLM_WEIGHT_MEAN = 1,                  /* scale / M, M = rows listed           */
+  MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED = 2   /* scale * min(1/(1-p_b), clip) / (n_b B) */
+};
+
 /*
  * Workspace bytes that mdlm_compact_masked needs for n_tokens tokens: three
  * 32-bit words per 4096-token tile (its count and its first and last
@@ -163,6 +170,62 @@ int mdlm_compact_masked(const uint8_t* corrupted, const int32_t* x0,
                         int32_t* row_idx, int32_t* tgt, float* w,
                         int32_t* n_rows, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes that mdlm_compact_rows needs: those of
+ * mdlm_compact_workspace_bytes plus, for MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED,
+ * one 32-bit word per document and one more.  Returns 0 for n_tokens <= 0
+ * or an invalid n_docs or weighting.
+ */
+size_t mdlm_compact_rows_workspace_bytes(int64_t n_tokens, int32_t n_docs,
+                                         int32_t weighting);
+
+/*
+ * mdlm_compact_rows -- the scored-row list of mdlm_compact_masked, generalised
+ * to the loss variants: every token (causal next-token CE), an eligibility
+ * mask, and other weightings.
+ *
+ * Defined by: diffusiongemma card, "Finetuning notes" (total = diffusion CE +
+ * encoder_loss_weight * encoder AR CE, the AR term a plain causal next-token
+ * CE over the clean sequence; the rate t ~ U(eps, 1) drawn per example);
+ * Axolotl docs, objective options (inv_one_minus_t time weighting with
+ * example_mean reduction, 1/(1-t) capped by rhine_weight_clip) and "Packed
+ * training" (tokens outside the loss are excluded).
+ *
+ * Token g of document b is scored when corrupted[g] != 0 (every token if
+ * corrupted is NULL), eligible[g] != 0 (every token if eligible is NULL)
+ * and, with MDLM_SHIFTED, g != cu_seqlens[b].  Rows and targets are as for
+ * mdlm_compact_masked, in ascending g.  With M the number of rows, n_b the
+ * rows of document b and B the number of documents with n_b > 0, each row of
+ * document b has weight, evaluated in fp64 and rounded once to fp32:
+ *   MDLM_WEIGHT_INV_P                 scale / (p_doc[b] * n_tokens)
+ *   MDLM_WEIGHT_MEAN                  scale / M
+ *   MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED  a = 1 / (1 - p_doc[b]); a = min(a, clip);
+ *                                     scale * a / (n_b * B)
+ * (corrupted = NULL, MDLM_SHIFTED, MDLM_WEIGHT_MEAN and scale = lambda give
+ * the rows of lambda times the causal next-token CE; under uniform noise
+ * p_doc[b] is the example's rate t.)
+ *
+ *   corrupted   [n_tokens] uint8 or NULL.
+ *   eligible    [n_tokens] uint8 or NULL.
+ *   x0, n_tokens, cu_seqlens, n_docs, align, row_idx, tgt, w, n_rows:
+ *               as for mdlm_compact_masked.
+ *   p_doc       [n_docs] double; may be NULL for MDLM_WEIGHT_MEAN.
+ *   weighting   an MDLM_WEIGHT_* value.
+ *   weight_scale  finite.
+ *   weight_clip   > 0 (+inf: no cap); read by the clipped mode only.
+ *   workspace   >= mdlm_compact_rows_workspace_bytes(n_tokens, n_docs,
+ *               weighting) bytes of device memory, 4-byte aligned.
+ * Returns MDLM_OK, MDLM_EINVAL, MDLM_EWORKSPACE or MDLM_EHIP.
+ */
+int mdlm_compact_rows(const uint8_t* corrupted, const uint8_t* eligible,
+                      const int32_t* x0, int64_t n_tokens,
+                      const int32_t* cu_seqlens, int32_t n_docs,
+                      const double* p_doc, int32_t align, int32_t weighting,
+                      double weight_scale, double weight_clip,
+                      int32_t* row_idx, int32_t* tgt, float* w,
+                      int32_t* n_rows, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes that mdlm_fused_head_ce_fwd_bwd needs for up to max_rows

@@ -184,6 +184,54 @@ def test_compact_rejects_small_workspace(lib):
     assert "workspace" in B.mdlm_last_error()
 
 
+def rows_call(lib, **kw):
+    a = dict(corrupted=NULL, eligible=NULL, x0=NULL, n=16, cu=NULL, n_docs=1, p_doc=NULL,
+             align=0, weighting=1, scale=1.0, clip=10.0, row_idx=NULL, tgt=NULL, w=NULL,
+             n_rows=NULL, ws=NULL, ws_bytes=0, stream=NULL)
+    a.update(kw)
+    return lib.mdlm_compact_rows(a["corrupted"], a["eligible"], a["x0"], a["n"], a["cu"],
+                                 a["n_docs"], a["p_doc"], a["align"], a["weighting"],
+                                 a["scale"], a["clip"], a["row_idx"], a["tgt"], a["w"],
+                                 a["n_rows"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(n=-1), B.MDLM_EINVAL, "n_tokens < 0"),
+    (dict(n_docs=0), B.MDLM_EINVAL, "n_docs"),
+    (dict(align=3), B.MDLM_EINVAL, "alignment"),
+    (dict(weighting=3), B.MDLM_EINVAL, "weighting"),
+    (dict(weighting=-1), B.MDLM_EINVAL, "weighting"),
+    (dict(scale=float("nan")), B.MDLM_EINVAL, "weight_scale"),
+    (dict(scale=float("inf")), B.MDLM_EINVAL, "weight_scale"),
+    (dict(weighting=2, clip=0.0), B.MDLM_EINVAL, "weight_clip"),
+    (dict(weighting=2, clip=float("nan")), B.MDLM_EINVAL, "weight_clip"),
+    (dict(), B.MDLM_EINVAL, "null n_rows"),
+])
+def test_compact_rows_rejects_bad_arguments(lib, kw, code, msg):
+    assert rows_call(lib, **kw) == code
+    assert msg in B.mdlm_last_error()
+
+
+def test_compact_rows_pointer_and_workspace_checks(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    n = 1 << 20
+    kw = dict(x0=fake, cu=fake, row_idx=fake, tgt=fake, w=fake, n_rows=fake, n=n, n_docs=9)
+    # the mean weighting needs no p_doc and no mask; others need p_doc
+    assert rows_call(lib, **kw) == B.MDLM_EWORKSPACE
+    assert rows_call(lib, weighting=0, **kw) == B.MDLM_EINVAL
+    assert "null pointer" in B.mdlm_last_error()
+    need = B.mdlm_compact_rows_workspace_bytes(n, 9, 2)
+    assert need == compact_ws(n) + 4 * (9 + 1)
+    assert B.mdlm_compact_rows_workspace_bytes(n, 9, 1) == compact_ws(n)
+    assert B.mdlm_compact_rows_workspace_bytes(n, 9, 7) == 0
+    assert B.mdlm_compact_rows_workspace_bytes(n, -1, 1) == 0
+    assert rows_call(lib, weighting=2, p_doc=fake, ws=fake, ws_bytes=need - 1,
+                     **kw) == B.MDLM_EWORKSPACE
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert rows_call(lib, weighting=2, p_doc=fake, ws=odd, ws_bytes=need, **kw) == B.MDLM_EINVAL
+    assert "4-byte aligned" in B.mdlm_last_error()
+
+
 def test_error_is_cleared_by_next_call(lib):
     assert corrupt_call(lib, eps=0.0) == B.MDLM_EINVAL
     assert B.mdlm_last_error() != ""

@@ -26,11 +26,16 @@ MDLM_ALIGNED = 0
 MDLM_SHIFTED = 1
 MDLM_F32 = 0
 MDLM_BF16 = 1
+MDLM_WEIGHT_INV_P = 0
+MDLM_WEIGHT_MEAN = 1
+MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED = 2
 
 EXPORTED = (
     "mdlm_corrupt",
     "mdlm_compact_workspace_bytes",
     "mdlm_compact_masked",
+    "mdlm_compact_rows_workspace_bytes",
+    "mdlm_compact_rows",
     "mdlm_head_ce_workspace_bytes",
     "mdlm_head_ce_workspace_min_bytes",
     "mdlm_fused_head_ce_fwd_bwd",
@@ -66,6 +71,11 @@ def load():
     lib.mdlm_compact_workspace_bytes.restype = sz
     lib.mdlm_compact_masked.argtypes = [vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.mdlm_compact_masked.restype = ctypes.c_int
+    lib.mdlm_compact_rows_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.mdlm_compact_rows_workspace_bytes.restype = sz
+    lib.mdlm_compact_rows.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, i32, f64, f64, vp, vp,
+                                      vp, vp, vp, sz, vp]
+    lib.mdlm_compact_rows.restype = ctypes.c_int
     lib.mdlm_head_ce_workspace_bytes.argtypes = [i64, i32, i32, i32]
     lib.mdlm_head_ce_workspace_bytes.restype = sz
     lib.mdlm_head_ce_workspace_min_bytes.argtypes = [i64, i32, i32, i32]
@@ -152,6 +162,33 @@ def mdlm_compact_masked(corrupted, x0, cu_seqlens, p_doc, align, row_idx, tgt, w
                                       cu_seqlens.numel() - 1, _ptr(p_doc), int(align),
                                       _ptr(row_idx), _ptr(tgt), _ptr(w), _ptr(n_rows),
                                       _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mdlm_compact_rows_workspace_bytes(n_tokens, n_docs, weighting):
+    return load().mdlm_compact_rows_workspace_bytes(int(n_tokens), int(n_docs), int(weighting))
+
+
+def mdlm_compact_rows(corrupted, eligible, x0, cu_seqlens, p_doc, align, weighting,
+                      weight_scale, weight_clip, row_idx, tgt, w, n_rows, workspace,
+                      stream=None):
+    """See mdlm_compact_rows in include/mdlm.h.  `corrupted`, `eligible` and
+    `p_doc` may be None; `workspace` is a uint8 tensor."""
+    _need(corrupted, torch.uint8, "corrupted")
+    _need(eligible, torch.uint8, "eligible")
+    _need(x0, torch.int32, "x0")
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    _need(p_doc, torch.float64, "p_doc")
+    _need(row_idx, torch.int32, "row_idx")
+    _need(tgt, torch.int32, "tgt")
+    _need(w, torch.float32, "w")
+    _need(n_rows, torch.int32, "n_rows")
+    _need(workspace, torch.uint8, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(load().mdlm_compact_rows(
+        _ptr(corrupted), _ptr(eligible), _ptr(x0), x0.numel(), _ptr(cu_seqlens),
+        cu_seqlens.numel() - 1, _ptr(p_doc), int(align), int(weighting), float(weight_scale),
+        float(weight_clip), _ptr(row_idx), _ptr(tgt), _ptr(w), _ptr(n_rows), _ptr(workspace),
+        ws_bytes, _stream(stream)))
 
 
 def dtype_code(t):

@@ -65,7 +65,51 @@ int mdlm_corrupt(const int32_t* x0, int64_t n_tokens, const int32_t* cu_seqlens,
 }
 
 size_t mdlm_compact_workspace_bytes(int64_t n_tokens) {
-  return compact_workspace_bytes(n_tokens);
+  return compact_workspace_bytes(n_tokens, 0, MDLM_WEIGHT_INV_P);
+}
+
+size_t mdlm_compact_rows_workspace_bytes(int64_t n_tokens, int32_t n_docs, int32_t weighting) {
+  if (n_docs < 0 || weighting < MDLM_WEIGHT_INV_P || weighting > MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED)
+    return 0;
+  return compact_workspace_bytes(n_tokens, n_docs, weighting);
+}
+
+// Shared checks and launch of both compaction entry points.
+static int compact_common(const char* fn, bool need_mask, const uint8_t* corrupted,
+                          const uint8_t* eligible,
+                          const int32_t* x0, int64_t n_tokens, const int32_t* cu_seqlens,
+                          int32_t n_docs, const double* p_doc, int32_t align, int32_t weighting,
+                          double scale, double clip, int32_t* row_idx, int32_t* tgt, float* w,
+                          int32_t* n_rows, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (n_tokens < 0) return fail(MDLM_EINVAL, "%s: n_tokens < 0", fn);
+  if (n_tokens > INT32_MAX)
+    return fail(MDLM_EUNSUPPORTED, "%s: n_tokens must be below 2^31", fn);
+  if (n_docs < 0 || (n_docs == 0 && n_tokens > 0))
+    return fail(MDLM_EINVAL, "%s: bad n_docs %d", fn, n_docs);
+  if (align != MDLM_ALIGNED && align != MDLM_SHIFTED)
+    return fail(MDLM_EINVAL, "%s: unknown alignment %d", fn, align);
+  if (weighting < MDLM_WEIGHT_INV_P || weighting > MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED)
+    return fail(MDLM_EINVAL, "%s: unknown weighting %d", fn, weighting);
+  if (!isfinite(scale)) return fail(MDLM_EINVAL, "%s: weight_scale must be finite", fn);
+  if (weighting == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED && !(clip > 0.0))
+    return fail(MDLM_EINVAL, "%s: weight_clip must be > 0", fn);
+  if (!n_rows) return fail(MDLM_EINVAL, "%s: null n_rows", fn);
+  const bool need_p = weighting != MDLM_WEIGHT_MEAN;
+  if (n_tokens > 0 && (!x0 || !cu_seqlens || !row_idx || !tgt || !w || (need_p && !p_doc) ||
+                       (need_mask && !corrupted)))
+    return fail(MDLM_EINVAL, "%s: null pointer", fn);
+  const size_t need = compact_workspace_bytes(n_tokens, n_docs, weighting);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MDLM_EWORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes,
+                need);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 4) != 0)
+    return fail(MDLM_EINVAL, "%s: workspace must be 4-byte aligned", fn);
+  if (launch_compact(corrupted, eligible, x0, n_tokens, cu_seqlens, n_docs, p_doc, align,
+                     weighting, scale, clip, row_idx, tgt, w, n_rows, workspace,
+                     reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return check_launch(fn);
+  return MDLM_OK;
 }
 
 int mdlm_compact_masked(const uint8_t* corrupted, const int32_t* x0, int64_t n_tokens,
@@ -74,26 +118,21 @@ int mdlm_compact_masked(const uint8_t* corrupted, const int32_t* x0, int64_t n_t
                         int32_t* n_rows, void* workspace, size_t workspace_bytes,
                         void* stream) {
   clear_error();
-  if (n_tokens < 0) return fail(MDLM_EINVAL, "mdlm_compact_masked: n_tokens < 0");
-  if (n_tokens > INT32_MAX)
-    return fail(MDLM_EUNSUPPORTED, "mdlm_compact_masked: n_tokens must be below 2^31");
-  if (n_docs < 0 || (n_docs == 0 && n_tokens > 0))
-    return fail(MDLM_EINVAL, "mdlm_compact_masked: bad n_docs %d", n_docs);
-  if (align != MDLM_ALIGNED && align != MDLM_SHIFTED)
-    return fail(MDLM_EINVAL, "mdlm_compact_masked: unknown alignment %d", align);
-  if (!n_rows) return fail(MDLM_EINVAL, "mdlm_compact_masked: null n_rows");
-  if (n_tokens > 0 && (!corrupted || !x0 || !cu_seqlens || !p_doc || !row_idx || !tgt || !w))
-    return fail(MDLM_EINVAL, "mdlm_compact_masked: null pointer");
-  const size_t need = compact_workspace_bytes(n_tokens);
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(MDLM_EWORKSPACE, "mdlm_compact_masked: workspace of %zu bytes, need %zu",
-                workspace_bytes, need);
-  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 4) != 0)
-    return fail(MDLM_EINVAL, "mdlm_compact_masked: workspace must be 4-byte aligned");
-  if (launch_compact(corrupted, x0, n_tokens, cu_seqlens, n_docs, p_doc, align, row_idx, tgt,
-                     w, n_rows, workspace, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
-    return check_launch("mdlm_compact_masked");
-  return MDLM_OK;
+  return compact_common("mdlm_compact_masked", true, corrupted, nullptr, x0, n_tokens, cu_seqlens,
+                        n_docs, p_doc, align, MDLM_WEIGHT_INV_P, 1.0, 0.0, row_idx, tgt, w,
+                        n_rows, workspace, workspace_bytes, stream);
+}
+
+int mdlm_compact_rows(const uint8_t* corrupted, const uint8_t* eligible, const int32_t* x0,
+                      int64_t n_tokens, const int32_t* cu_seqlens, int32_t n_docs,
+                      const double* p_doc, int32_t align, int32_t weighting,
+                      double weight_scale, double weight_clip, int32_t* row_idx, int32_t* tgt,
+                      float* w, int32_t* n_rows, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  clear_error();
+  return compact_common("mdlm_compact_rows", false, corrupted, eligible, x0, n_tokens, cu_seqlens,
+                        n_docs, p_doc, align, weighting, weight_scale, weight_clip, row_idx, tgt,
+                        w, n_rows, workspace, workspace_bytes, stream);
 }
 
 static bool head_sizes_ok(int64_t max_rows, int32_t H, int32_t V, int32_t dtype) {

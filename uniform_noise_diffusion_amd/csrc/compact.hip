@@ -54,13 +54,56 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
-// Number of nonzero bytes of w: bit 0 of each byte becomes the OR of that
-// byte's bits (shifts that only move bits down within a byte's low nibble).
-__device__ __forceinline__ int nonzero_bytes(uint32_t w) {
+// Bit 8k set iff byte k of w is nonzero: bit 0 of each byte becomes the OR
+// of that byte's bits (shifts that only move bits down within a byte's low
+// nibble).
+__device__ __forceinline__ uint32_t nonzero_flags(uint32_t w) {
   uint32_t x = w | (w >> 4);
   x |= x >> 2;
   x |= x >> 1;
-  return __popc(x & 0x01010101u);
+  return x & 0x01010101u;
+}
+
+// Which tokens are scored before the alignment rule: corrupted (every token
+// when the mask is absent) and eligible (every token when absent).
+struct RowMasks {
+  const uint8_t* corrupted;
+  const uint8_t* eligible;
+  __device__ __forceinline__ bool at(int64_t g) const {
+    return (!corrupted || corrupted[g]) && (!eligible || eligible[g]);
+  }
+  // flags (bit 8k) of the 4 tokens at g (4-byte aligned, all in range)
+  __device__ __forceinline__ uint32_t word(int64_t g) const {
+    uint32_t f = 0x01010101u;
+    if (corrupted) f &= nonzero_flags(*reinterpret_cast<const uint32_t*>(corrupted + g));
+    if (eligible) f &= nonzero_flags(*reinterpret_cast<const uint32_t*>(eligible + g));
+    return f;
+  }
+};
+
+// How rows are weighted (see mdlm_compact_rows).
+struct WeightArgs {
+  int32_t mode;
+  double scale, clip;
+  const double* p_doc;
+  int64_t n;                   // tokens in the call
+  const int32_t* doc_rows;     // example-mean mode: scored rows per document
+  const int32_t* n_examples;   // example-mean mode: documents with a scored row
+};
+
+// Weight of the rows of document b, in fp64 rounded once to fp32.
+__device__ __forceinline__ float doc_weight(const WeightArgs& a, int b, int64_t total_rows,
+                                            int32_t n_examples) {
+#pragma clang fp contract(off)
+  if (a.mode == MDLM_WEIGHT_MEAN) return (float)(a.scale / (double)total_rows);
+  if (a.mode == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED) {
+    const int32_t nb = a.doc_rows[b];
+    if (nb <= 0) return 0.f;  // (no row of such a document is ever written)
+    double x = 1.0 / (1.0 - a.p_doc[b]);
+    x = fmin(x, a.clip);
+    return (float)(a.scale * x / ((double)nb * (double)n_examples));
+  }
+  return (float)(a.scale / (a.p_doc[b] * (double)a.n));
 }
 
 // Set bits of b at lanes below this one.
@@ -102,37 +145,80 @@ __device__ __forceinline__ void tile_range(const int32_t* __restrict__ tile_lo,
 // One wave per tile: the number of scored tokens of the tile.
 template <bool kShifted>
 __global__ void __launch_bounds__(kThreads)
-count_kernel(const uint8_t* __restrict__ corrupted, int64_t n, const int32_t* __restrict__ cu,
-             int32_t n_docs, const int32_t* __restrict__ tile_lo, const int32_t* __restrict__ tile_hi,
+count_kernel(RowMasks mk, int64_t n, const int32_t* __restrict__ cu, int32_t n_docs,
+             const int32_t* __restrict__ tile_lo, const int32_t* __restrict__ tile_hi,
              int64_t n_tiles, int32_t* __restrict__ tile_counts) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (t >= n_tiles) return;
   const int64_t t0 = t * kTile, t1 = min(t0 + kTile, n);
   int cnt = 0;
-  if (t1 - t0 == kTile && ((uintptr_t)corrupted % 16) == 0) {
-    uint4 v[4];
+  const bool aligned = ((uintptr_t)mk.corrupted % 16) == 0 && ((uintptr_t)mk.eligible % 16) == 0;
+  if (t1 - t0 == kTile && aligned) {
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    uint4 c[4], e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t off = t0 + 1024 * i + 16 * lane;
+      c[i] = mk.corrupted ? *reinterpret_cast<const uint4*>(mk.corrupted + off) : zero;
+      e[i] = mk.eligible ? *reinterpret_cast<const uint4*>(mk.eligible + off) : zero;
+    }
+    // flags of one 4-byte word of each mask (an absent mask flags every byte)
+    auto flags = [&](uint32_t cw, uint32_t ew) {
+      return (mk.corrupted ? nonzero_flags(cw) : 0x01010101u) &
+             (mk.eligible ? nonzero_flags(ew) : 0x01010101u);
+    };
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      v[i] = *reinterpret_cast<const uint4*>(corrupted + t0 + 1024 * i + 16 * lane);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      cnt += nonzero_bytes(v[i].x) + nonzero_bytes(v[i].y) + nonzero_bytes(v[i].z) +
-             nonzero_bytes(v[i].w);
+      cnt += __popc(flags(c[i].x, e[i].x)) + __popc(flags(c[i].y, e[i].y)) +
+             __popc(flags(c[i].z, e[i].z)) + __popc(flags(c[i].w, e[i].w));
   } else {
-    for (int64_t g = t0 + lane; g < t1; g += 64) cnt += corrupted[g] != 0;
+    for (int64_t g = t0 + lane; g < t1; g += 64) cnt += mk.at(g);
   }
   if (kShifted) {
-    // a corrupted first token of a (non-empty) document is not scored
+    // a scored first token of a (non-empty) document has no row
     int dlo, dhi;
     tile_range(tile_lo, tile_hi, n_docs, t, &dlo, &dhi);
     for (int i = dlo + lane; i <= dhi; i += 64) {
       const int64_t beg = cu[i], end = cu[i + 1];
-      if (beg < end && beg >= t0 && beg < t1 && corrupted[beg]) --cnt;
+      if (beg < end && beg >= t0 && beg < t1 && mk.at(beg)) --cnt;
     }
   }
   cnt = wave_sum(cnt);
   if (lane == 0) tile_counts[t] = cnt;
+}
+
+// Example-mean weighting, pass 1: one wave per document counts its scored
+// rows.
+template <bool kShifted>
+__global__ void __launch_bounds__(kThreads)
+doc_rows_kernel(RowMasks mk, int64_t n, const int32_t* __restrict__ cu, int32_t n_docs,
+                int32_t* __restrict__ doc_rows) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (b >= n_docs) return;
+  const int64_t beg = cu[b], end = min<int64_t>(cu[b + 1], n);
+  int cnt = 0;
+  for (int64_t g = beg + (kShifted ? 1 : 0) + lane; g < end; g += 64) cnt += mk.at(g);
+  cnt = wave_sum(cnt);
+  if (lane == 0) doc_rows[b] = cnt;
+}
+
+// Example-mean weighting, pass 2: the number of documents with a scored row.
+__global__ void __launch_bounds__(1024)
+examples_kernel(const int32_t* __restrict__ doc_rows, int32_t n_docs,
+                int32_t* __restrict__ n_examples) {
+  __shared__ int s_part[1024 / 64];
+  int c = 0;
+  for (int b = threadIdx.x; b < n_docs; b += 1024) c += doc_rows[b] > 0;
+  c = wave_sum(c);
+  if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int i = 0; i < 1024 / 64; ++i) t += s_part[i];
+    *n_examples = t;
+  }
 }
 
 // Per group of 1024 tiles: counts -> exclusive offsets within the group (in
@@ -163,19 +249,14 @@ group_scan_kernel(int32_t* __restrict__ tile_counts, int64_t n_tiles,
   if (tid == 0) group_sums[blockIdx.x] = total;
 }
 
-// Weight 1 / (p N) of a document, in fp64 then rounded once to fp32.
-__device__ __forceinline__ float doc_weight(double p, int64_t n) {
-  return (float)(1.0 / (p * (double)n));
-}
-
 // Scatter: four rounds per tile; in round j thread t owns the 4 consecutive
 // tokens at 1024 j + 4 t, so every load is contiguous across the wave.
 template <bool kShifted, bool kVec>
 __global__ void __launch_bounds__(kThreads)
-scatter_kernel(const uint8_t* __restrict__ corrupted, const int32_t* __restrict__ x0, int64_t n,
+scatter_kernel(RowMasks mk, const int32_t* __restrict__ x0, int64_t n,
                const int32_t* __restrict__ cu, int32_t n_docs,
                const int32_t* __restrict__ tile_lo, const int32_t* __restrict__ tile_hi,
-               const double* __restrict__ p_doc, const int32_t* __restrict__ tile_offsets,
+               WeightArgs wa, const int32_t* __restrict__ tile_offsets,
                const int32_t* __restrict__ group_sums, int32_t n_groups,
                int32_t* __restrict__ row_idx, int32_t* __restrict__ tgt, float* __restrict__ w,
                int32_t* __restrict__ n_rows) {
@@ -185,7 +266,7 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const int32_t* __restrict_
   __shared__ int32_t s_row[kBufs][kRoundTok];
   __shared__ int32_t s_tgt[kBufs][kRoundTok];
   __shared__ float s_w[kBufs][kRoundTok];
-  __shared__ int s_base;
+  __shared__ int s_base, s_total;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tile = blockIdx.x;
@@ -194,10 +275,8 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const int32_t* __restrict_
   tile_range(tile_lo, tile_hi, n_docs, tile, &dlo, &dhi);
   const int nd = dhi - dlo + 1;
   const bool cached = nd <= kLdsDocs;
-  if (cached) {
+  if (cached)
     for (int i = tid; i <= nd; i += kThreads) s_cu[i] = cu[dlo + i];
-    for (int i = tid; i < nd; i += kThreads) s_wd[i] = doc_weight(p_doc[dlo + i], n);
-  }
   const int grp = (int)(tile / kGroup);
   if (wave == 0) {
     // this tile's offset: its place in its group plus the groups before it
@@ -205,12 +284,23 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const int32_t* __restrict_
     for (int g = lane; g < grp; g += 64) b += group_sums[g];
     b = wave_sum(b);
     if (lane == 0) s_base = b + tile_offsets[tile];
-  } else if (wave == 1 && tile == 0) {
+  } else if (wave == 1 && (tile == 0 || wa.mode == MDLM_WEIGHT_MEAN)) {
+    // the total row count (the mean weighting divides by it)
     int tot = 0;
     for (int g = lane; g < n_groups; g += 64) tot += group_sums[g];
     tot = wave_sum(tot);
-    if (lane == 0) *n_rows = tot;
+    if (lane == 0) {
+      s_total = tot;
+      if (tile == 0) *n_rows = tot;
+    }
   }
+  __syncthreads();
+  const int64_t total_rows = wa.mode == MDLM_WEIGHT_MEAN ? s_total : 0;
+  const int32_t n_examples =
+      wa.mode == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED ? *wa.n_examples : 0;
+  if (cached)
+    for (int i = tid; i < nd; i += kThreads)
+      s_wd[i] = doc_weight(wa, dlo + i, total_rows, n_examples);
   __syncthreads();
   int64_t out = s_base;
 
@@ -221,17 +311,17 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const int32_t* __restrict_
     uint32_t sel = 0;
     int32_t vals[4] = {0, 0, 0, 0};
     float wts[4] = {0.f, 0.f, 0.f, 0.f};
-    uint32_t mv = 0;  // mask byte k in bits 8k..8k+7
+    uint32_t mv = 0;  // bit 8k: token g0 + k is corrupted and eligible
     const int cnt_here = g0 < n ? (int)min<int64_t>(4, n - g0) : 0;
     if (kVec && cnt_here == 4) {
-      mv = *reinterpret_cast<const uint32_t*>(corrupted + g0);
+      mv = mk.word(g0);
       const int4 xv = *reinterpret_cast<const int4*>(x0 + g0);
       vals[0] = xv.x; vals[1] = xv.y; vals[2] = xv.z; vals[3] = xv.w;
     } else {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (k < cnt_here) {
-          mv |= (uint32_t)(corrupted[g0 + k] != 0) << (8 * k);
+          mv |= (uint32_t)mk.at(g0 + k) << (8 * k);
           vals[k] = x0[g0 + k];
         }
     }
@@ -265,7 +355,7 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const int32_t* __restrict_
       int d = cached ? lds_find_doc(s_cu, nd, g0) : find_doc(cu, dlo, dhi, g0) - dlo;
       int64_t d_beg = cached ? s_cu[d] : cu[dlo + d];
       int64_t d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
-      float wd = cached ? s_wd[d] : doc_weight(p_doc[dlo + d], n);
+      float wd = cached ? s_wd[d] : doc_weight(wa, dlo + d, total_rows, n_examples);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int64_t g = g0 + k;
@@ -277,7 +367,7 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const int32_t* __restrict_
               d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
             } while (g >= d_end && d < nd - 1);
             d_beg = cached ? s_cu[d] : cu[dlo + d];
-            wd = cached ? s_wd[d] : doc_weight(p_doc[dlo + d], n);
+            wd = cached ? s_wd[d] : doc_weight(wa, dlo + d, total_rows, n_examples);
           }
           if (!kShifted || g != d_beg) {
             sel |= 1u << k;
@@ -328,18 +418,22 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const int32_t* __restrict_
 
 }  // namespace
 
-size_t compact_workspace_bytes(int64_t n_tokens) {
+size_t compact_workspace_bytes(int64_t n_tokens, int32_t n_docs, int32_t weighting) {
   if (n_tokens <= 0) return 0;
   const int64_t tiles = (n_tokens + kTile - 1) / kTile;
   const int64_t groups = (tiles + kGroup - 1) / kGroup;
-  // counts, first and last document per tile; one total per group
-  return (3 * (size_t)tiles + (size_t)groups) * sizeof(int32_t);
+  // counts, first and last document per tile; one total per group; for the
+  // example-mean weighting, scored rows per document and the example count
+  size_t words = 3 * (size_t)tiles + (size_t)groups;
+  if (weighting == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED) words += (size_t)std::max(n_docs, 0) + 1;
+  return words * sizeof(int32_t);
 }
 
-hipError_t launch_compact(const uint8_t* corrupted, const int32_t* x0, int64_t n,
-                          const int32_t* cu, int32_t n_docs, const double* p_doc,
-                          int32_t align, int32_t* row_idx, int32_t* tgt, float* w,
-                          int32_t* n_rows, void* workspace, hipStream_t stream) {
+hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, const int32_t* x0,
+                          int64_t n, const int32_t* cu, int32_t n_docs, const double* p_doc,
+                          int32_t align, int32_t weighting, double scale, double clip,
+                          int32_t* row_idx, int32_t* tgt, float* w, int32_t* n_rows,
+                          void* workspace, hipStream_t stream) {
   if (n <= 0) {
     set_int_kernel<<<1, 1, 0, stream>>>(n_rows, 0);
     return hipGetLastError();
@@ -350,22 +444,37 @@ hipError_t launch_compact(const uint8_t* corrupted, const int32_t* x0, int64_t n
   int32_t* tile_lo = counts + tiles;
   int32_t* tile_hi = tile_lo + tiles;
   int32_t* group_sums = tile_hi + tiles;
+  const RowMasks mk{corrupted, eligible};
+  WeightArgs wa{weighting, scale, clip, p_doc, n, nullptr, nullptr};
+  const bool shifted = align == MDLM_SHIFTED;
+  if (weighting == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED) {
+    int32_t* doc_rows = group_sums + groups;
+    int32_t* n_examples = doc_rows + n_docs;
+    const unsigned g = (unsigned)((n_docs + kWaves - 1) / kWaves);
+    if (shifted)
+      doc_rows_kernel<true><<<g, kThreads, 0, stream>>>(mk, n, cu, n_docs, doc_rows);
+    else
+      doc_rows_kernel<false><<<g, kThreads, 0, stream>>>(mk, n, cu, n_docs, doc_rows);
+    examples_kernel<<<1, 1024, 0, stream>>>(doc_rows, n_docs, n_examples);
+    wa.doc_rows = doc_rows;
+    wa.n_examples = n_examples;
+  }
   tile_docs_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(cu, n_docs, n,
                                                                                 tile_lo, tile_hi);
   const unsigned count_grid = (unsigned)((tiles + kWaves - 1) / kWaves);
-  const bool shifted = align == MDLM_SHIFTED;
   if (shifted)
-    count_kernel<true><<<count_grid, kThreads, 0, stream>>>(corrupted, n, cu, n_docs, tile_lo,
-                                                            tile_hi, tiles, counts);
+    count_kernel<true><<<count_grid, kThreads, 0, stream>>>(mk, n, cu, n_docs, tile_lo, tile_hi,
+                                                            tiles, counts);
   else
-    count_kernel<false><<<count_grid, kThreads, 0, stream>>>(corrupted, n, cu, n_docs, tile_lo,
-                                                             tile_hi, tiles, counts);
+    count_kernel<false><<<count_grid, kThreads, 0, stream>>>(mk, n, cu, n_docs, tile_lo, tile_hi,
+                                                             tiles, counts);
   group_scan_kernel<<<(unsigned)groups, kGroup, 0, stream>>>(counts, tiles, group_sums);
-  const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)corrupted % 4 == 0);
+  const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)corrupted % 4 == 0) &&
+                   ((uintptr_t)eligible % 4 == 0);
 #define MDLM_SCATTER_LAUNCH(SH, VEC)                                                           \
   scatter_kernel<SH, VEC><<<(unsigned)tiles, kThreads, 0, stream>>>(                           \
-      corrupted, x0, n, cu, n_docs, tile_lo, tile_hi, p_doc, counts, group_sums, (int32_t)groups, \
-      row_idx, tgt, w, n_rows)
+      mk, x0, n, cu, n_docs, tile_lo, tile_hi, wa, counts, group_sums, (int32_t)groups, row_idx, \
+      tgt, w, n_rows)
   if (shifted) {
     if (vec) MDLM_SCATTER_LAUNCH(true, true);
     else MDLM_SCATTER_LAUNCH(true, false);

@@ -111,10 +111,11 @@ hipError_t launch_corrupt(const int32_t* x0, int64_t n_tokens, const int32_t* cu
                           uint8_t* corrupted, double* p_doc, int32_t* doc_counts,
                           hipStream_t stream);
 
-size_t compact_workspace_bytes(int64_t n_tokens);
-hipError_t launch_compact(const uint8_t* corrupted, const int32_t* x0, int64_t n_tokens,
-                          const int32_t* cu, int32_t n_docs, const double* p_doc,
-                          int32_t align, int32_t* row_idx, int32_t* tgt, float* w,
+size_t compact_workspace_bytes(int64_t n_tokens, int32_t n_docs, int32_t weighting);
+hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, const int32_t* x0,
+                          int64_t n_tokens, const int32_t* cu, int32_t n_docs,
+                          const double* p_doc, int32_t align, int32_t weighting, double scale,
+                          double clip, int32_t* row_idx, int32_t* tgt, float* w,
                           int32_t* n_rows, void* workspace, hipStream_t stream);
 
 struct HeadCeArgs {

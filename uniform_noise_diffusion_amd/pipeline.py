@@ -32,6 +32,7 @@ class MdlmLossStep:
         self.n_rows = torch.empty(1, **i32)
         self.compact_ws = torch.empty(max(B.mdlm_compact_workspace_bytes(n_tokens), 1),
                                       dtype=torch.uint8, device=dev)
+        self.rows_ws = None
         self.loss = torch.empty(1, dtype=torch.float32, device=dev)
         self.row_ce = torch.empty(max(n_tokens, 1), dtype=torch.float32, device=dev)
         self.d_hidden = (torch.empty((n_tokens, H), dtype=dtype, device=dev)
@@ -48,6 +49,19 @@ class MdlmLossStep:
     def compact(self, x0, cu_seqlens, align, stream=None):
         B.mdlm_compact_masked(self.corrupted, x0, cu_seqlens, self.p_doc, align, self.row_idx,
                               self.tgt, self.w, self.n_rows, self.compact_ws, stream)
+
+    def compact_rows(self, x0, cu_seqlens, align, weighting, weight_scale=1.0,
+                     weight_clip=float("inf"), corrupted=True, eligible=None, stream=None):
+        """mdlm_compact_rows into this step's row buffers: `corrupted` True uses
+        the mask of the last corrupt() call, None scores every token;
+        `eligible` is an optional uint8 mask."""
+        need = B.mdlm_compact_rows_workspace_bytes(self.n_tokens, self.n_docs, weighting)
+        if self.rows_ws is None or self.rows_ws.numel() < need:
+            self.rows_ws = torch.empty(max(need, 1), dtype=torch.uint8, device=self.xt.device)
+        mask = self.corrupted if corrupted is True else corrupted
+        B.mdlm_compact_rows(mask, eligible, x0, cu_seqlens, self.p_doc, align, weighting,
+                            weight_scale, weight_clip, self.row_idx, self.tgt, self.w,
+                            self.n_rows, self.rows_ws, stream)
 
     def head_ce(self, hidden, W, softcap, stream=None, want_grad=True, row_ce=True):
         B.mdlm_fused_head_ce_fwd_bwd(hidden, W, self.row_idx, self.tgt, self.w, self.n_rows,
