@@ -290,6 +290,45 @@ int mdlm_fused_head_ce_fwd_bwd(const void* hidden, const void* W, int32_t dtype,
                                float* row_ce, void* d_hidden, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/*
+ * Workspace bytes of mdlm_fused_head_ce_fwd_bwd_dw: those of the bf16
+ * mdlm_head_ce_workspace_bytes / _min_bytes plus room for the gathered
+ * scored rows (max_rows * H bf16).  Returns 0 for invalid sizes.
+ */
+size_t mdlm_head_ce_dw_workspace_bytes(int64_t max_rows, int32_t H, int32_t V);
+size_t mdlm_head_ce_dw_workspace_min_bytes(int64_t max_rows, int32_t H, int32_t V);
+
+/*
+ * mdlm_fused_head_ce_fwd_bwd_dw -- mdlm_fused_head_ce_fwd_bwd for a head that
+ * is trained: the same loss, row_ce and d_hidden, plus the gradient of the
+ * loss with respect to W.
+ *
+ * Defined by: Axolotl docs, "Adapters, merging and inference" (the plain
+ * linear head whose gradient this is); LLaDA-8B-MDLM-LoRA card, Training
+ * table (the frozen-head case, where no such gradient is formed).
+ *
+ *   dW[v] = sum_j w[j] * (softmax(zhat_j)[v] - [v == tgt[j]]) * zhat'_jv * h_j
+ * (the same per-logit factor as d_hidden, rounded to bf16, times the bf16
+ * hidden rows; products accumulated in fp32).
+ *
+ *   hidden, W   bf16 only (the element type is implied).
+ *   d_hidden    [n_tokens, H] bf16 out, or NULL (only dW is wanted).
+ *   dW          [V, H] float out, 16-byte aligned; overwritten (zero when no
+ *               row is scored).
+ *   workspace   >= mdlm_head_ce_dw_workspace_min_bytes(max_rows, H, V).
+ *   other arguments as for mdlm_fused_head_ce_fwd_bwd.
+ * Returns MDLM_OK, MDLM_EINVAL, MDLM_EUNSUPPORTED, MDLM_EWORKSPACE or
+ * MDLM_EHIP.
+ */
+int mdlm_fused_head_ce_fwd_bwd_dw(const void* hidden, const void* W,
+                                  int64_t n_tokens, int32_t H, int32_t V,
+                                  const int32_t* row_idx, const int32_t* tgt,
+                                  const float* w, const int32_t* n_rows,
+                                  int64_t max_rows, float softcap, float* loss,
+                                  float* row_ce, void* d_hidden, float* dW,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 /* Message describing the last failure on the calling thread ("" if none).
  * Valid until the next library call on that thread. */
 const char* mdlm_last_error(void);

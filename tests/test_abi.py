@@ -258,6 +258,33 @@ def test_probe_library_exports_its_header():
     assert lib.mdlm_probe_copy(None, None, 0, None) == 0
 
 
+def test_dw_entry_point_checks(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    a = dict(hidden=fake, W=fake, n=64, H=128, V=1000, row_idx=fake, tgt=fake, w=fake,
+             n_rows=fake, max_rows=32, softcap=0.0, loss=fake, row_ce=None, d_hidden=None,
+             dW=fake, ws=None, ws_bytes=0)
+
+    def call(**kw):
+        b = dict(a)
+        b.update(kw)
+        return lib.mdlm_fused_head_ce_fwd_bwd_dw(
+            b["hidden"], b["W"], b["n"], b["H"], b["V"], b["row_idx"], b["tgt"], b["w"],
+            b["n_rows"], b["max_rows"], b["softcap"], b["loss"], b["row_ce"], b["d_hidden"],
+            b["dW"], b["ws"], b["ws_bytes"], None)
+
+    assert call(dW=None) == B.MDLM_EINVAL and "null dW" in B.mdlm_last_error()
+    assert call(dW=ctypes.c_void_p((1 << 20) + 4)) == B.MDLM_EINVAL
+    assert "dW must be 16-byte aligned" in B.mdlm_last_error()
+    assert call(H=96) == B.MDLM_EUNSUPPORTED
+    assert call() == B.MDLM_EWORKSPACE
+    need = B.mdlm_head_ce_dw_workspace_min_bytes(32, 128, 1000)
+    # the gathered rows (32 x 128 bf16) on top of the plain call's workspace
+    assert need >= B.mdlm_head_ce_workspace_min_bytes(32, 128, 1000, B.MDLM_BF16) + 32 * 128 * 2
+    assert call(ws=fake, ws_bytes=need - 1) == B.MDLM_EWORKSPACE
+    assert (B.mdlm_head_ce_dw_workspace_bytes(32, 128, 1000) >= need > 0)
+    assert B.mdlm_head_ce_dw_workspace_bytes(-1, 128, 1000) == 0
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))

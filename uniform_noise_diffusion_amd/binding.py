@@ -39,6 +39,9 @@ EXPORTED = (
     "mdlm_head_ce_workspace_bytes",
     "mdlm_head_ce_workspace_min_bytes",
     "mdlm_fused_head_ce_fwd_bwd",
+    "mdlm_head_ce_dw_workspace_bytes",
+    "mdlm_head_ce_dw_workspace_min_bytes",
+    "mdlm_fused_head_ce_fwd_bwd_dw",
     "mdlm_last_error",
     "mdlm_version",
 )
@@ -83,6 +86,13 @@ def load():
     lib.mdlm_fused_head_ce_fwd_bwd.argtypes = [vp, vp, i32, i64, i32, i32, vp, vp, vp, vp, i64,
                                                f32, vp, vp, vp, vp, sz, vp]
     lib.mdlm_fused_head_ce_fwd_bwd.restype = ctypes.c_int
+    lib.mdlm_head_ce_dw_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.mdlm_head_ce_dw_workspace_bytes.restype = sz
+    lib.mdlm_head_ce_dw_workspace_min_bytes.argtypes = [i64, i32, i32]
+    lib.mdlm_head_ce_dw_workspace_min_bytes.restype = sz
+    lib.mdlm_fused_head_ce_fwd_bwd_dw.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp, i64,
+                                                  f32, vp, vp, vp, vp, vp, sz, vp]
+    lib.mdlm_fused_head_ce_fwd_bwd_dw.restype = ctypes.c_int
     lib.mdlm_last_error.argtypes = []
     lib.mdlm_last_error.restype = ctypes.c_char_p
     lib.mdlm_version.argtypes = []
@@ -232,4 +242,42 @@ def mdlm_fused_head_ce_fwd_bwd(hidden, W, row_idx, tgt, w, n_rows, max_rows, sof
     _check(load().mdlm_fused_head_ce_fwd_bwd(
         _ptr(hidden), _ptr(W), dt, n_tokens, H, V, _ptr(row_idx), _ptr(tgt), _ptr(w),
         _ptr(n_rows), int(max_rows), float(softcap), _ptr(loss), _ptr(row_ce), _ptr(d_hidden),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mdlm_head_ce_dw_workspace_bytes(max_rows, H, V):
+    return load().mdlm_head_ce_dw_workspace_bytes(int(max_rows), int(H), int(V))
+
+
+def mdlm_head_ce_dw_workspace_min_bytes(max_rows, H, V):
+    return load().mdlm_head_ce_dw_workspace_min_bytes(int(max_rows), int(H), int(V))
+
+
+def mdlm_fused_head_ce_fwd_bwd_dw(hidden, W, row_idx, tgt, w, n_rows, max_rows, softcap, loss,
+                                  row_ce, d_hidden, dW, workspace, stream=None):
+    """See mdlm_fused_head_ce_fwd_bwd_dw in include/mdlm.h (bf16 only).
+    `d_hidden` and `row_ce` may be None; `dW` is a float32 [V, H] tensor."""
+    if hidden.dtype != torch.bfloat16:
+        raise TypeError("mdlm_fused_head_ce_fwd_bwd_dw takes bf16 hidden and W")
+    _need(hidden, torch.bfloat16, "hidden")
+    _need(W, torch.bfloat16, "W")
+    _need(row_idx, torch.int32, "row_idx")
+    _need(tgt, torch.int32, "tgt")
+    _need(w, torch.float32, "w")
+    _need(n_rows, torch.int32, "n_rows")
+    _need(loss, torch.float32, "loss")
+    _need(row_ce, torch.float32, "row_ce")
+    _need(d_hidden, torch.bfloat16, "d_hidden")
+    _need(dW, torch.float32, "dW")
+    _need(workspace, torch.uint8, "workspace")
+    n_tokens, H = hidden.shape
+    V = W.shape[0]
+    if W.shape[1] != H or dW is None or tuple(dW.shape) != (V, H):
+        raise ValueError("W and dW must be [V, H] with the hidden size of `hidden`")
+    if d_hidden is not None and tuple(d_hidden.shape) != tuple(hidden.shape):
+        raise ValueError("d_hidden must have the shape of hidden")
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(load().mdlm_fused_head_ce_fwd_bwd_dw(
+        _ptr(hidden), _ptr(W), n_tokens, H, V, _ptr(row_idx), _ptr(tgt), _ptr(w), _ptr(n_rows),
+        int(max_rows), float(softcap), _ptr(loss), _ptr(row_ce), _ptr(d_hidden), _ptr(dW),
         _ptr(workspace), ws_bytes, _stream(stream)))

@@ -142,23 +142,32 @@ static bool head_sizes_ok(int64_t max_rows, int32_t H, int32_t V, int32_t dtype)
 
 size_t mdlm_head_ce_workspace_bytes(int64_t max_rows, int32_t H, int32_t V, int32_t dtype) {
   if (!head_sizes_ok(max_rows, H, V, dtype)) return 0;
-  return head_ce_workspace_bytes(max_rows, H, V, dtype, false);
+  return head_ce_workspace_bytes(max_rows, H, V, dtype, false, false);
 }
 
 size_t mdlm_head_ce_workspace_min_bytes(int64_t max_rows, int32_t H, int32_t V,
                                         int32_t dtype) {
   if (!head_sizes_ok(max_rows, H, V, dtype)) return 0;
-  return head_ce_workspace_bytes(max_rows, H, V, dtype, true);
+  return head_ce_workspace_bytes(max_rows, H, V, dtype, true, false);
 }
 
-int mdlm_fused_head_ce_fwd_bwd(const void* hidden, const void* W, int32_t dtype,
-                               int64_t n_tokens, int32_t H, int32_t V,
-                               const int32_t* row_idx, const int32_t* tgt, const float* w,
-                               const int32_t* n_rows, int64_t max_rows, float softcap,
-                               float* loss, float* row_ce, void* d_hidden, void* workspace,
-                               size_t workspace_bytes, void* stream) {
-  clear_error();
-  const char* fn = "mdlm_fused_head_ce_fwd_bwd";
+size_t mdlm_head_ce_dw_workspace_bytes(int64_t max_rows, int32_t H, int32_t V) {
+  if (!head_sizes_ok(max_rows, H, V, MDLM_BF16)) return 0;
+  return head_ce_workspace_bytes(max_rows, H, V, MDLM_BF16, false, true);
+}
+
+size_t mdlm_head_ce_dw_workspace_min_bytes(int64_t max_rows, int32_t H, int32_t V) {
+  if (!head_sizes_ok(max_rows, H, V, MDLM_BF16)) return 0;
+  return head_ce_workspace_bytes(max_rows, H, V, MDLM_BF16, true, true);
+}
+
+// Shared checks and launch of both fused head + CE entry points.
+static int head_common(const char* fn, const void* hidden, const void* W, int32_t dtype,
+                       int64_t n_tokens, int32_t H, int32_t V, const int32_t* row_idx,
+                       const int32_t* tgt, const float* w, const int32_t* n_rows,
+                       int64_t max_rows, float softcap, float* loss, float* row_ce,
+                       void* d_hidden, float* dW, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   if (dtype != MDLM_F32 && dtype != MDLM_BF16)
     return fail(MDLM_EINVAL, "%s: unknown dtype %d", fn, dtype);
   if (n_tokens < 0 || H <= 0 || V <= 0)
@@ -176,7 +185,10 @@ int mdlm_fused_head_ce_fwd_bwd(const void* hidden, const void* W, int32_t dtype,
   if (dtype == MDLM_BF16 && max_rows > 0 &&
       ((reinterpret_cast<uintptr_t>(hidden) | reinterpret_cast<uintptr_t>(W)) % 16) != 0)
     return fail(MDLM_EINVAL, "%s: hidden and W must be 16-byte aligned", fn);
-  const size_t need = max_rows > 0 ? head_ce_workspace_bytes(max_rows, H, V, dtype, true) : 0;
+  if (dW && (reinterpret_cast<uintptr_t>(dW) % 16) != 0)
+    return fail(MDLM_EINVAL, "%s: dW must be 16-byte aligned", fn);
+  const size_t need =
+      max_rows > 0 ? head_ce_workspace_bytes(max_rows, H, V, dtype, true, dW != nullptr) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(MDLM_EWORKSPACE, "%s: workspace of %zu bytes, need at least %zu", fn,
                 workspace_bytes, need);
@@ -198,11 +210,38 @@ int mdlm_fused_head_ce_fwd_bwd(const void* hidden, const void* W, int32_t dtype,
   a.loss = loss;
   a.row_ce = row_ce;
   a.d_hidden = d_hidden;
+  a.dW = dW;
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   if (launch_head_ce(a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return check_launch(fn);
   return MDLM_OK;
+}
+
+int mdlm_fused_head_ce_fwd_bwd(const void* hidden, const void* W, int32_t dtype,
+                               int64_t n_tokens, int32_t H, int32_t V,
+                               const int32_t* row_idx, const int32_t* tgt, const float* w,
+                               const int32_t* n_rows, int64_t max_rows, float softcap,
+                               float* loss, float* row_ce, void* d_hidden, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  clear_error();
+  return head_common("mdlm_fused_head_ce_fwd_bwd", hidden, W, dtype, n_tokens, H, V, row_idx,
+                     tgt, w, n_rows, max_rows, softcap, loss, row_ce, d_hidden, nullptr,
+                     workspace, workspace_bytes, stream);
+}
+
+int mdlm_fused_head_ce_fwd_bwd_dw(const void* hidden, const void* W, int64_t n_tokens,
+                                  int32_t H, int32_t V, const int32_t* row_idx,
+                                  const int32_t* tgt, const float* w, const int32_t* n_rows,
+                                  int64_t max_rows, float softcap, float* loss, float* row_ce,
+                                  void* d_hidden, float* dW, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* fn = "mdlm_fused_head_ce_fwd_bwd_dw";
+  if (!dW) return fail(MDLM_EINVAL, "%s: null dW", fn);
+  return head_common(fn, hidden, W, MDLM_BF16, n_tokens, H, V, row_idx, tgt, w, n_rows,
+                     max_rows, softcap, loss, row_ce, d_hidden, dW, workspace, workspace_bytes,
+                     stream);
 }
 
 }  // extern "C"

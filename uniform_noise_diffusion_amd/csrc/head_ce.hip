@@ -647,6 +647,174 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// dW = G^T Hs over one vocabulary chunk (a trainable head's gradient).
+// --------------------------------------------------------------------------
+struct DwArgs {
+  const bf16_t* G;   // [max_rows][ldg], column v - v_begin
+  int64_t ldg;
+  const bf16_t* Hs;  // [max_rows][H]: hidden[row_idx[m]] for m < n_rows
+  int H;
+  int v_begin;
+  int v_end;
+  const int32_t* n_rows;
+  int max_rows;
+  float* dW;         // [V][H]
+};
+
+// Tile of 256 vocabulary entries (operand A: columns of G) by 256 hidden
+// columns (operand B: columns of Hs), K = scored rows.  Both operands are
+// N-major in memory (rows of G and of Hs), staged as 64-row x 512-byte LDS
+// tiles and read through transpose loads.  Wave w owns vocabulary entries
+// 128 (w % 2) .. +127 and hidden columns kWB (w / 2) .. +kWB-1.  Rows past
+// n_rows read as zeros through the buffer range check; the buffer bases move
+// with the K step so every offset stays within 32 bits.
+__global__ void __launch_bounds__(kGemmThreads, 1) dw_kernel(DwArgs a) {
+  __shared__ __attribute__((aligned(1024))) char smem0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem1[kStageBytes];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wa = wave & 1, wb = wave >> 1;
+  const int n_rows = min(*a.n_rows, a.max_rows);
+  const int n_vt = (a.v_end - a.v_begin + kTile - 1) / kTile;
+  const int n_ht = (a.H + kTile - 1) / kTile;
+  const int64_t T = (int64_t)n_vt * n_ht;
+  const int KT = (n_rows + kBK - 1) / kBK;
+
+  // transpose-read roles (as in dh_kernel)
+  const int jl = lane & 15, grp = lane >> 4;
+  const int tr_row = 8 * (grp >> 1) + (jl >> 2);
+  auto col_off = [&](int col) {
+    return (((col >> 3) ^ swz_n(tr_row)) * 16) + ((col >> 2) & 1) * 8;
+  };
+  int a_col_off[4], b_col_off[kNJ];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a_col_off[i] = col_off(wa * 128 + 32 * i + 16 * (grp & 1) + 4 * (jl & 3));
+#pragma unroll
+  for (int j = 0; j < kNJ; ++j)
+    b_col_off[j] = col_off(wb * kWB + 32 * j + 16 * (grp & 1) + 4 * (jl & 3));
+  const int nrow = lane >> 5, nphys = lane & 31;  // N-major loads
+
+  for (int64_t t = logical_block(); t < T; t += gridDim.x) {
+    const int vt = (int)(t / n_ht), ht = (int)(t % n_ht);
+    const int v0 = vt * kTile;  // column of G
+    const int h0 = ht * kTile;
+    uint32_t a_voff[2], b_voff[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int cn = nphys ^ swz_n(2 * par + nrow);
+      a_voff[par] = (uint32_t)((nrow * a.ldg + 8 * cn) * 2);
+      b_voff[par] = (uint32_t)((nrow * a.H + 8 * cn) * 2);
+    }
+    f32x16 acc[4][kNJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    auto issue = [&](char* stage, int k0) {
+      // rows k0.. of both operands; past n_rows the ranges are empty
+      const int64_t rows_left = (int64_t)n_rows - k0;
+      const __amdgpu_buffer_rsrc_t ra =
+          make_rsrc(a.G + (int64_t)k0 * a.ldg + v0, rows_left * a.ldg * 2 - (int64_t)v0 * 2);
+      const __amdgpu_buffer_rsrc_t rb =
+          make_rsrc(a.Hs + (int64_t)k0 * a.H + h0, rows_left * a.H * 2 - (int64_t)h0 * 2);
+      char* sa = stage + (kLoads * wave) * 1024;
+#pragma unroll
+      for (int q = 0; q < kLoads; ++q) {
+        const int r = 2 * (kLoads * wave + q);
+        buf2l(ra, sa + q * 1024, a_voff[q & 1], (uint32_t)(r * a.ldg * 2));
+        buf2l(rb, sa + kOpBytes + q * 1024, b_voff[q & 1], (uint32_t)(r * a.H * 2));
+      }
+    };
+    auto compute = [&](const char* base, auto vmem) {
+      mma_k64<2 * 4 + 2 * kNJ, decltype(vmem)::value>(
+          acc,
+          [&](int kk, bf16x8(&f)[4]) {
+            const char* arow_p = base + (16 * kk + tr_row) * kNRow;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const shortx4 lo = ds_read_tr(arow_p + a_col_off[i]);
+              const shortx4 hi = ds_read_tr(arow_p + 4 * kNRow + a_col_off[i]);
+              const short v8 __attribute__((__vector_size__(16))) = {
+                  lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              f[i] = __builtin_bit_cast(bf16x8, v8);
+            }
+          },
+          [&](int kk, bf16x8(&f)[kNJ]) {
+            const char* brow_p = base + kOpBytes + (16 * kk + tr_row) * kNRow;
+#pragma unroll
+            for (int j = 0; j < kNJ; ++j) {
+              const shortx4 lo = ds_read_tr(brow_p + b_col_off[j]);
+              const shortx4 hi = ds_read_tr(brow_p + 4 * kNRow + b_col_off[j]);
+              const short v8 __attribute__((__vector_size__(16))) = {
+                  lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              f[j] = __builtin_bit_cast(bf16x8, v8);
+            }
+          });
+    };
+
+    __syncthreads();
+    issue(smem0, 0);
+    // same pipeline as the other MFMA kernels (unconditional last prefetch,
+    // of empty ranges, retired by the wait after the loop)
+    int kt = 0;
+    for (; kt + 2 <= KT; kt += 2) {
+      wait_vmem();
+      __syncthreads();
+      issue(smem1, (kt + 1) * kBK);
+      compute(smem0, kInterleave);
+      sched_fence();
+      wait_vmem();
+      __syncthreads();
+      issue(smem0, (kt + 2) * kBK);
+      compute(smem1, kInterleave);
+      sched_fence();
+    }
+    if (kt < KT) {
+      wait_vmem();
+      __syncthreads();
+      compute(smem0, kNoLoads);
+    }
+    wait_vmem();
+
+    // acc element e of block (i, j) on lane l: vocabulary entry v_begin + v0
+    // + wa*128 + 32i + 8(e/4) + 4(l/32) + e%4, hidden column h0 + wb*kWB +
+    // 32j + l%32.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int v = a.v_begin + v0 + wa * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (v >= a.v_end) continue;
+#pragma unroll
+        for (int j = 0; j < kNJ; ++j) {
+          const int h = h0 + wb * kWB + 32 * j + (lane & 31);
+          if (h < a.H) a.dW[(int64_t)v * a.H + h] = acc[i][j][e];
+        }
+      }
+  }
+}
+
+// Hs[m] = hidden[row_idx[m]] for the scored rows (zeros for an out-of-range
+// index), 16 bytes per thread.
+__global__ void __launch_bounds__(kThreads)
+gather_rows_kernel(const bf16_t* __restrict__ hidden, const int32_t* __restrict__ row_idx,
+                   const int32_t* __restrict__ n_rows_ptr, int max_rows, int64_t n_tokens, int H,
+                   bf16_t* __restrict__ Hs) {
+  const int n_rows = min(*n_rows_ptr, max_rows);
+  const int n16 = H / 8;  // H is a multiple of 64
+  for (int m = blockIdx.x; m < n_rows; m += gridDim.x) {
+    const int64_t r = row_idx[m];
+    const bool ok = r >= 0 && r < n_tokens;
+    const uint4* src = reinterpret_cast<const uint4*>(hidden + (ok ? r : 0) * H);
+    uint4* dst = reinterpret_cast<uint4*>(Hs + (int64_t)m * H);
+    for (int i = threadIdx.x; i < n16; i += kThreads)
+      dst[i] = ok ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// --------------------------------------------------------------------------
 // Reductions.
 // --------------------------------------------------------------------------
 __global__ void __launch_bounds__(kThreads)
@@ -837,12 +1005,13 @@ f32_dh_kernel(F32Args a, float* __restrict__ d_hidden) {
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t partial, ztgt, lse, bsum, part, G, total;
+  size_t partial, ztgt, lse, bsum, Hs, part, G, total;
   int n_vt, n_bsum;
 };
 
-// Fixed part of the layout; G gets whatever follows.
-Layout fixed_layout(int64_t max_rows, int H, int V, int dtype, bool grad) {
+// Fixed part of the layout; G gets whatever follows.  `dw`: room for the
+// gathered scored rows of the head-weight gradient.
+Layout fixed_layout(int64_t max_rows, int H, int V, int dtype, bool grad, bool dw = false) {
   Layout L{};
   L.n_vt = (V + kTile - 1) / kTile;
   L.n_bsum = (int)((max_rows + kMergeRows - 1) / kMergeRows);
@@ -851,6 +1020,8 @@ Layout fixed_layout(int64_t max_rows, int H, int V, int dtype, bool grad) {
   L.ztgt = off;    off = align_up(off + (size_t)max_rows * sizeof(float));
   L.lse = off;     off = align_up(off + (size_t)max_rows * sizeof(float));
   L.bsum = off;    off = align_up(off + (size_t)std::max(L.n_bsum, 1) * sizeof(double));
+  L.Hs = off;
+  if (dw) off = align_up(off + (size_t)max_rows * H * sizeof(bf16_t));
   L.part = L.G = off;
   if (grad && dtype == MDLM_BF16) {
     L.part = off;
@@ -871,20 +1042,22 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 // The preferred workspace holds G for the whole vocabulary, so the gradient
 // runs as one chunk; the minimum holds one 256-wide vocabulary chunk.
 size_t head_ce_workspace_bytes(int64_t max_rows, int32_t H, int32_t V, int32_t dtype,
-                               bool minimal) {
-  Layout L = fixed_layout(max_rows, H, V, dtype, true);
+                               bool minimal, bool dw) {
+  Layout L = fixed_layout(max_rows, H, V, dtype, true, dw);
   if (dtype != MDLM_BF16 || max_rows == 0) return L.total;
   const int64_t vc = minimal ? kTile : round_up(V, kTile);
   return L.total + align_up((size_t)max_rows * vc * sizeof(bf16_t));
 }
 
 hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
-  const bool grad = x.d_hidden != nullptr;
+  const bool want_dh = x.d_hidden != nullptr;
+  const bool want_dw = x.dW != nullptr;  // (bf16 only; checked by the caller)
+  const bool grad = want_dh || want_dw;
   const int64_t max_rows = x.max_rows;
   char* ws = reinterpret_cast<char*>(x.workspace);
   const size_t elt = x.dtype == MDLM_BF16 ? 2 : 4;
 
-  if (grad) {
+  if (want_dh) {
     const size_t bytes = (size_t)x.n_tokens * x.H * elt;
     const int64_t n16 = (int64_t)(bytes / 16);
     const int64_t tail = (int64_t)(bytes % 16);
@@ -894,12 +1067,21 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
                                             reinterpret_cast<uint8_t*>(x.d_hidden) + n16 * 16,
                                             tail);
   }
+  if (want_dw) {
+    // dW = 0 first: with no scored rows it stays zero
+    const size_t bytes = (size_t)x.V * x.H * sizeof(float);
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int64_t tail = (int64_t)(bytes % 16);
+    const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n16 + 255) / 256, 4096));
+    zero_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<uint4*>(x.dW), n16,
+                                          reinterpret_cast<uint8_t*>(x.dW) + n16 * 16, tail);
+  }
   if (max_rows == 0) {
     set_float_kernel<<<1, 1, 0, stream>>>(x.loss, 0.f);
     return hipGetLastError();
   }
 
-  Layout L = fixed_layout(max_rows, x.H, x.V, x.dtype, grad);
+  Layout L = fixed_layout(max_rows, x.H, x.V, x.dtype, grad, want_dw);
   float2* partial = reinterpret_cast<float2*>(ws + L.partial);
   float* ztgt = reinterpret_cast<float*>(ws + L.ztgt);
   float* lse = reinterpret_cast<float*>(ws + L.lse);
@@ -1006,6 +1188,20 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   la.G = G;
   la.ldg = vc;
 
+  DwArgs wa{};
+  bf16_t* Hs = reinterpret_cast<bf16_t*>(ws + L.Hs);
+  if (want_dw) {
+    gather_rows_kernel<<<(unsigned)std::min<int64_t>(max_rows, 65535), kThreads, 0, stream>>>(
+        la.hidden, x.row_idx, x.n_rows, (int)max_rows, x.n_tokens, x.H, Hs);
+    wa.G = G;
+    wa.ldg = vc;
+    wa.Hs = Hs;
+    wa.H = x.H;
+    wa.n_rows = x.n_rows;
+    wa.max_rows = (int)max_rows;
+    wa.dW = x.dW;
+  }
+
   DhArgs da{};
   da.G = G;
   da.ldg = vc;
@@ -1024,11 +1220,19 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
       logits_kernel<true, true><<<grid, kGemmThreads, 0, stream>>>(la);
     else
       logits_kernel<true, false><<<grid, kGemmThreads, 0, stream>>>(la);
-    da.v_begin = (int)v0;
-    da.v_end = v1;
-    da.accumulate = chunk > 0;
-    dh_kernel<<<grid, kGemmThreads, 0, stream>>>(da);
+    if (want_dh) {
+      da.v_begin = (int)v0;
+      da.v_end = v1;
+      da.accumulate = chunk > 0;
+      dh_kernel<<<grid, kGemmThreads, 0, stream>>>(da);
+    }
+    if (want_dw) {
+      wa.v_begin = (int)v0;
+      wa.v_end = v1;
+      dw_kernel<<<grid, kGemmThreads, 0, stream>>>(wa);
+    }
   }
+  if (!want_dh) return hipGetLastError();
   // every chunk uses the same slice count (it depends on the chunk width only
   // through the number of K steps, which is at least kMaxSplit unless the
   // chunk is narrower than 512)

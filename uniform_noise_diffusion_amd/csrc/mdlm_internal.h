@@ -134,12 +134,13 @@ struct HeadCeArgs {
   float* loss;
   float* row_ce;
   void* d_hidden;
+  float* dW;  // head-weight gradient [V][H] or null (bf16 only)
   void* workspace;
   size_t workspace_bytes;
 };
 
 size_t head_ce_workspace_bytes(int64_t max_rows, int32_t H, int32_t V, int32_t dtype,
-                               bool minimal);
+                               bool minimal, bool dw);
 hipError_t launch_head_ce(const HeadCeArgs& a, hipStream_t stream);
 
 }  // namespace mdlm
