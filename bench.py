@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--workload", type=int, default=2)
     p.add_argument("--align", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-variants", action="store_true",
+                   help="skip the loss variants (encoder AR term, head-weight gradient, "
+                        "row-list modes)")
     p.add_argument("--no-achievable", action="store_true",
                    help="skip the achievable-peak probes (copy, MFMA loop, library GEMM)")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -225,6 +228,96 @@ def achievable(dev, gemm_shape=None):
     return res
 
 
+def _timed(fn, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+
+def variants(inp, dev, n_bw, reps=5):
+    """The loss variants on the same workload: the encoder AR term (every-token
+    causal rows of mdlm_compact_rows, then the fused head on them), the
+    head-weight gradient call, and mdlm_compact_rows' other modes at the
+    bandwidth size."""
+    import torch
+    from uniform_noise_diffusion_amd import binding as B
+    from uniform_noise_diffusion_amd.pipeline import MdlmLossStep
+    wl = inp.wl
+    x0, cu, h, W = to_device(inp, dev)
+    out = {}
+    if wl.dtype != "bf16":
+        return out
+    step = MdlmLossStep(wl.n_tokens, wl.n_docs, wl.H, wl.V, device=dev)
+    HV = float(wl.H) * wl.V
+    # encoder AR term: lambda * causal next-token CE over the clean sequence
+    step.compact_rows(x0, cu, 1, B.MDLM_WEIGHT_MEAN, 0.5, corrupted=None)
+    t_rows = _timed(lambda: step.compact_rows(x0, cu, 1, B.MDLM_WEIGHT_MEAN, 0.5,
+                                              corrupted=None), reps)
+    m = int(step.n_rows.item())
+    t_head = _timed(lambda: step.head_ce(h, W, wl.softcap, row_ce=False), reps)
+    out["encoder_ar_term"] = dict(
+        rows=m, compact_rows_us=t_rows * 1e6, head_ms=t_head * 1e3,
+        head_algorithmic_tflops=4 * m * HV / t_head / 1e12,
+        head_executed_tflops=6 * m * HV / t_head / 1e12,
+        what="mdlm_compact_rows(every token, shifted, mean weights x 0.5) then "
+             "mdlm_fused_head_ce_fwd_bwd on those rows")
+    # head-weight gradient on the masked rows of seeds 0..reps-1
+    ws = torch.empty(B.mdlm_head_ce_dw_workspace_bytes(wl.n_tokens, wl.H, wl.V),
+                     dtype=torch.uint8, device=dev)
+    dW = torch.empty((wl.V, wl.H), dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    t_dw, t_plain, rows = [], [], []
+    for seed in range(reps):
+        step.corrupt(x0, cu, seed, wl.eps, wl.noise, wl.mask_id, wl.rand_vocab)
+        step.compact(x0, cu, wl.align)
+        rows.append(int(step.n_rows.item()))
+        t_dw.append(_timed(lambda: B.mdlm_fused_head_ce_fwd_bwd_dw(
+            h, W, step.row_idx, step.tgt, step.w, step.n_rows, wl.n_tokens, wl.softcap, loss,
+            None, step.d_hidden, dW, ws), 2))
+        t_plain.append(_timed(lambda: step.head_ce(h, W, wl.softcap, row_ce=False), 2))
+    rows = np.array(rows, dtype=np.float64)
+    out["head_weight_gradient"] = dict(
+        seeds=f"0..{reps - 1}", mean_rows=float(rows.mean()),
+        ms_per_call=float(np.mean(t_dw)) * 1e3,
+        ms_per_call_without_dw=float(np.mean(t_plain)) * 1e3,
+        algorithmic_tflops=float((6 * rows * HV).sum() / np.sum(t_dw) / 1e12),
+        executed_tflops=float((8 * rows * HV).sum() / np.sum(t_dw) / 1e12),
+        dw_gemm_tflops=float((2 * rows * HV).sum() / (np.sum(t_dw) - np.sum(t_plain)) / 1e12),
+        what="mdlm_fused_head_ce_fwd_bwd_dw (loss, d_hidden and dW fp32 [V, H]); the dW "
+             "product's rate is 2 M H V over the time the call adds")
+    del step, ws, dW
+    if n_bw:
+        L = 4096
+        n = n_bw // L * L
+        cu2 = torch.arange(0, n + 1, L, dtype=torch.int32, device=dev)
+        g = torch.Generator(device=dev).manual_seed(0)
+        x2 = torch.randint(0, 126336, (n,), dtype=torch.int32, device=dev, generator=g)
+        s2 = MdlmLossStep(n, n // L, 64, 64, device=dev, head_workspace_bytes=0, want_grad=False)
+        s2.corrupt(x2, cu2, 7, 1e-3, 1, 126336, 126464)
+        res = {}
+        for name, kw in (("causal_mean", dict(weighting=B.MDLM_WEIGHT_MEAN, corrupted=None)),
+                         ("masked_example_mean_clipped",
+                          dict(weighting=B.MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED, weight_clip=5.0))):
+            t = _timed(lambda: s2.compact_rows(x2, cu2, 1, **kw), reps)
+            mm = int(s2.n_rows.item())
+            mask_bytes = 0 if kw.get("corrupted", True) is None else n
+            alg = mask_bytes + 16.0 * mm
+            res[name] = dict(us=t * 1e6, rows=mm, algorithmic_GBs=alg / t / 1e9,
+                             frac=alg / t / 1e9 / PEAK_HBM_GBS)
+        res["what"] = (f"mdlm_compact_rows at {n} tokens in documents of 4,096 (shifted); "
+                       "algorithmic bytes: the mask (1 B per token, if any) + 16 B per row")
+        out["compact_rows_hbm"] = res
+    return out
+
+
 def cpu_baseline(inp, mean_rows, seconds):
     """The fp64 oracle, as it stands, on a bounded sample of the workload.
 
@@ -354,6 +447,9 @@ def main():
                 for op in ("corrupt", "compact"):
                     out[k][f"{op}_frac_of_achievable_copy"] = (
                         out[k][f"{op}_GBs"] / out["achievable"]["copy_GBs"])
+    if not args.no_variants:
+        log("timing the loss variants")
+        out["variants"] = variants(inp, dev, args.bandwidth_tokens)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(inp, rows.mean(), args.cpu_seconds)

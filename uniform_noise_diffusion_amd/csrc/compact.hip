@@ -189,7 +189,8 @@ count_kernel(RowMasks mk, int64_t n, const int32_t* __restrict__ cu, int32_t n_d
 }
 
 // Example-mean weighting, pass 1: one wave per document counts its scored
-// rows.
+// rows, 16 mask bytes per lane per load; bytes outside the document (or its
+// first token, with shifted logits) are masked off.
 template <bool kShifted>
 __global__ void __launch_bounds__(kThreads)
 doc_rows_kernel(RowMasks mk, int64_t n, const int32_t* __restrict__ cu, int32_t n_docs,
@@ -197,9 +198,40 @@ doc_rows_kernel(RowMasks mk, int64_t n, const int32_t* __restrict__ cu, int32_t 
   const int lane = threadIdx.x & 63;
   const int64_t b = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (b >= n_docs) return;
-  const int64_t beg = cu[b], end = min<int64_t>(cu[b + 1], n);
+  const int64_t lo = (int64_t)cu[b] + (kShifted ? 1 : 0);
+  const int64_t hi = min<int64_t>(cu[b + 1], n);
   int cnt = 0;
-  for (int64_t g = beg + (kShifted ? 1 : 0) + lane; g < end; g += 64) cnt += mk.at(g);
+  const bool vec = ((uintptr_t)mk.corrupted % 16) == 0 && ((uintptr_t)mk.eligible % 16) == 0;
+  if (vec) {
+    for (int64_t off = (lo & ~(int64_t)15) + 16 * lane; off < hi; off += 1024) {
+      uint32_t f[4] = {0u, 0u, 0u, 0u};
+      if (off + 16 <= n) {
+        const uint4 ones = make_uint4(1u, 1u, 1u, 1u);
+        const uint4 c = mk.corrupted ? *reinterpret_cast<const uint4*>(mk.corrupted + off) : ones;
+        const uint4 e = mk.eligible ? *reinterpret_cast<const uint4*>(mk.eligible + off) : ones;
+        // (an absent mask gives 0x00000001 per word: widen it to every byte)
+        const uint32_t cw[4] = {c.x, c.y, c.z, c.w}, ew[4] = {e.x, e.y, e.z, e.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          f[q] = (mk.corrupted ? nonzero_flags(cw[q]) : 0x01010101u) &
+                 (mk.eligible ? nonzero_flags(ew[q]) : 0x01010101u);
+      } else {
+        for (int i = 0; i < 16 && off + i < n; ++i)
+          f[i >> 2] |= (uint32_t)mk.at(off + i) << (8 * (i & 3));
+      }
+      // keep the bytes of [lo, hi)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t base = off + 4 * q;
+        const int s0 = (int)min<int64_t>(max<int64_t>(lo - base, 0), 4);
+        const int s1 = (int)min<int64_t>(max<int64_t>(hi - base, 0), 4);
+        const uint64_t keep = ((1ull << (8 * s1)) - 1) & ~((1ull << (8 * s0)) - 1);
+        cnt += __popc(f[q] & (uint32_t)keep);
+      }
+    }
+  } else {
+    for (int64_t g = lo + lane; g < hi; g += 64) cnt += mk.at(g);
+  }
   cnt = wave_sum(cnt);
   if (lane == 0) doc_rows[b] = cnt;
 }
