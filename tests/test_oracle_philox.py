@@ -77,6 +77,20 @@ def test_philox_token_layout_matches_rocrand(rocrand_ref, tag):
     assert np.array_equal(ref, ours)
 
 
+@pytest.mark.parametrize("tag", [1, 2])
+def test_token_words_match_rocrand(rocrand_ref, tag):
+    """oracle.mdlm.token_words itself (the function the corruption uses),
+    across a window that crosses 2^32 tokens."""
+    from oracle.mdlm import token_words
+    seed = 0xFEDCBA9876543210
+    start = 2**32 - 37
+    n = 101
+    ours = token_words(seed, n, tag, start=start).astype(np.uint64)
+    g = np.arange(start, start + n, dtype=np.uint64)
+    ref = rocrand_ref([seed] * n, [tag << 32] * n, g)
+    assert np.array_equal(ref, ours)
+
+
 def test_philox_counter_zero_key_zero_against_rocrand(rocrand_ref):
     ours = np.array(philox4x32_10(0, 0, 0, 0, 0, 0), dtype=np.uint64)
     ref = rocrand_ref([0] * 4, [0] * 4, [0, 1, 2, 3])
