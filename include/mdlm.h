@@ -173,9 +173,10 @@ int mdlm_compact_masked(const uint8_t* corrupted, const int32_t* x0,
 
 /*
  * Workspace bytes that mdlm_compact_rows needs: those of
- * mdlm_compact_workspace_bytes plus, for MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED,
- * one 32-bit word per document and one more.  Returns 0 for n_tokens <= 0
- * or an invalid n_docs or weighting.
+ * mdlm_compact_workspace_bytes plus, for MDLM_WEIGHT_MEAN and
+ * MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED, one 32-bit word per document (its
+ * weight) and, for the latter, one more word per document and one more.
+ * Returns 0 for n_tokens <= 0 or an invalid n_docs or weighting.
  */
 size_t mdlm_compact_rows_workspace_bytes(int64_t n_tokens, int32_t n_docs,
                                          int32_t weighting);

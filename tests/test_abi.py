@@ -220,9 +220,11 @@ def test_compact_rows_pointer_and_workspace_checks(lib):
     assert rows_call(lib, **kw) == B.MDLM_EWORKSPACE
     assert rows_call(lib, weighting=0, **kw) == B.MDLM_EINVAL
     assert "null pointer" in B.mdlm_last_error()
+    # weights per document (mean, example mean); rows per document + 1 (example mean)
     need = B.mdlm_compact_rows_workspace_bytes(n, 9, 2)
-    assert need == compact_ws(n) + 4 * (9 + 1)
-    assert B.mdlm_compact_rows_workspace_bytes(n, 9, 1) == compact_ws(n)
+    assert need == compact_ws(n) + 4 * (9 + 9 + 1)
+    assert B.mdlm_compact_rows_workspace_bytes(n, 9, 1) == compact_ws(n) + 4 * 9
+    assert B.mdlm_compact_rows_workspace_bytes(n, 9, 0) == compact_ws(n)
     assert B.mdlm_compact_rows_workspace_bytes(n, 9, 7) == 0
     assert B.mdlm_compact_rows_workspace_bytes(n, -1, 1) == 0
     assert rows_call(lib, weighting=2, p_doc=fake, ws=fake, ws_bytes=need - 1,

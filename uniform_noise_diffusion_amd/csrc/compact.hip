@@ -64,20 +64,43 @@ __device__ __forceinline__ uint32_t nonzero_flags(uint32_t w) {
   return x & 0x01010101u;
 }
 
-// Which tokens are scored before the alignment rule: corrupted (every token
-// when the mask is absent) and eligible (every token when absent).
+// Which tokens are scored before the alignment rule: corrupted and eligible.
+// kC / kE say whether each mask is present (an absent mask scores every
+// token); they are compile-time so the token loops carry no pointer tests.
+template <bool kC, bool kE>
 struct RowMasks {
   const uint8_t* corrupted;
   const uint8_t* eligible;
   __device__ __forceinline__ bool at(int64_t g) const {
-    return (!corrupted || corrupted[g]) && (!eligible || eligible[g]);
+    return (!kC || corrupted[g]) && (!kE || eligible[g]);
   }
-  // flags (bit 8k) of the 4 tokens at g (4-byte aligned, all in range)
+  // the 4 tokens at g (4-byte aligned, all in range): byte k is nonzero iff
+  // token g + k is scored (a single mask's bytes as they are)
   __device__ __forceinline__ uint32_t word(int64_t g) const {
+    if (kC && !kE) return *reinterpret_cast<const uint32_t*>(corrupted + g);
+    if (kE && !kC) return *reinterpret_cast<const uint32_t*>(eligible + g);
     uint32_t f = 0x01010101u;
-    if (corrupted) f &= nonzero_flags(*reinterpret_cast<const uint32_t*>(corrupted + g));
-    if (eligible) f &= nonzero_flags(*reinterpret_cast<const uint32_t*>(eligible + g));
+    if (kC) f &= nonzero_flags(*reinterpret_cast<const uint32_t*>(corrupted + g));
+    if (kE) f &= nonzero_flags(*reinterpret_cast<const uint32_t*>(eligible + g));
     return f;
+  }
+  // flags of the 16 tokens at off (16-byte aligned, all in range)
+  __device__ __forceinline__ uint4 flags16(int64_t off) const {
+    uint4 f = make_uint4(0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u);
+    if (kC) {
+      const uint4 v = *reinterpret_cast<const uint4*>(corrupted + off);
+      f.x &= nonzero_flags(v.x); f.y &= nonzero_flags(v.y);
+      f.z &= nonzero_flags(v.z); f.w &= nonzero_flags(v.w);
+    }
+    if (kE) {
+      const uint4 v = *reinterpret_cast<const uint4*>(eligible + off);
+      f.x &= nonzero_flags(v.x); f.y &= nonzero_flags(v.y);
+      f.z &= nonzero_flags(v.z); f.w &= nonzero_flags(v.w);
+    }
+    return f;
+  }
+  __device__ __forceinline__ bool aligned16() const {
+    return (!kC || (uintptr_t)corrupted % 16 == 0) && (!kE || (uintptr_t)eligible % 16 == 0);
   }
 };
 
@@ -143,9 +166,9 @@ __device__ __forceinline__ void tile_range(const int32_t* __restrict__ tile_lo,
 }
 
 // One wave per tile: the number of scored tokens of the tile.
-template <bool kShifted>
+template <bool kShifted, bool kC, bool kE>
 __global__ void __launch_bounds__(kThreads)
-count_kernel(RowMasks mk, int64_t n, const int32_t* __restrict__ cu, int32_t n_docs,
+count_kernel(RowMasks<kC, kE> mk, int64_t n, const int32_t* __restrict__ cu, int32_t n_docs,
              const int32_t* __restrict__ tile_lo, const int32_t* __restrict__ tile_hi,
              int64_t n_tiles, int32_t* __restrict__ tile_counts) {
   const int lane = threadIdx.x & 63;
@@ -153,25 +176,13 @@ count_kernel(RowMasks mk, int64_t n, const int32_t* __restrict__ cu, int32_t n_d
   if (t >= n_tiles) return;
   const int64_t t0 = t * kTile, t1 = min(t0 + kTile, n);
   int cnt = 0;
-  const bool aligned = ((uintptr_t)mk.corrupted % 16) == 0 && ((uintptr_t)mk.eligible % 16) == 0;
-  if (t1 - t0 == kTile && aligned) {
-    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    uint4 c[4], e[4];
+  if (t1 - t0 == kTile && mk.aligned16()) {
+    uint4 f[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t off = t0 + 1024 * i + 16 * lane;
-      c[i] = mk.corrupted ? *reinterpret_cast<const uint4*>(mk.corrupted + off) : zero;
-      e[i] = mk.eligible ? *reinterpret_cast<const uint4*>(mk.eligible + off) : zero;
-    }
-    // flags of one 4-byte word of each mask (an absent mask flags every byte)
-    auto flags = [&](uint32_t cw, uint32_t ew) {
-      return (mk.corrupted ? nonzero_flags(cw) : 0x01010101u) &
-             (mk.eligible ? nonzero_flags(ew) : 0x01010101u);
-    };
+    for (int i = 0; i < 4; ++i) f[i] = mk.flags16(t0 + 1024 * i + 16 * lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      cnt += __popc(flags(c[i].x, e[i].x)) + __popc(flags(c[i].y, e[i].y)) +
-             __popc(flags(c[i].z, e[i].z)) + __popc(flags(c[i].w, e[i].w));
+      cnt += __popc(f[i].x) + __popc(f[i].y) + __popc(f[i].z) + __popc(f[i].w);
   } else {
     for (int64_t g = t0 + lane; g < t1; g += 64) cnt += mk.at(g);
   }
@@ -191,30 +202,22 @@ count_kernel(RowMasks mk, int64_t n, const int32_t* __restrict__ cu, int32_t n_d
 // Example-mean weighting, pass 1: one wave per document counts its scored
 // rows, 16 mask bytes per lane per load; bytes outside the document (or its
 // first token, with shifted logits) are masked off.
-template <bool kShifted>
+template <bool kShifted, bool kC, bool kE>
 __global__ void __launch_bounds__(kThreads)
-doc_rows_kernel(RowMasks mk, int64_t n, const int32_t* __restrict__ cu, int32_t n_docs,
-                int32_t* __restrict__ doc_rows) {
+doc_rows_kernel(RowMasks<kC, kE> mk, int64_t n, const int32_t* __restrict__ cu,
+                int32_t n_docs, int32_t* __restrict__ doc_rows) {
   const int lane = threadIdx.x & 63;
   const int64_t b = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
   if (b >= n_docs) return;
   const int64_t lo = (int64_t)cu[b] + (kShifted ? 1 : 0);
   const int64_t hi = min<int64_t>(cu[b + 1], n);
   int cnt = 0;
-  const bool vec = ((uintptr_t)mk.corrupted % 16) == 0 && ((uintptr_t)mk.eligible % 16) == 0;
-  if (vec) {
+  if (mk.aligned16()) {
     for (int64_t off = (lo & ~(int64_t)15) + 16 * lane; off < hi; off += 1024) {
       uint32_t f[4] = {0u, 0u, 0u, 0u};
       if (off + 16 <= n) {
-        const uint4 ones = make_uint4(1u, 1u, 1u, 1u);
-        const uint4 c = mk.corrupted ? *reinterpret_cast<const uint4*>(mk.corrupted + off) : ones;
-        const uint4 e = mk.eligible ? *reinterpret_cast<const uint4*>(mk.eligible + off) : ones;
-        // (an absent mask gives 0x00000001 per word: widen it to every byte)
-        const uint32_t cw[4] = {c.x, c.y, c.z, c.w}, ew[4] = {e.x, e.y, e.z, e.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          f[q] = (mk.corrupted ? nonzero_flags(cw[q]) : 0x01010101u) &
-                 (mk.eligible ? nonzero_flags(ew[q]) : 0x01010101u);
+        const uint4 v = mk.flags16(off);
+        f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
       } else {
         for (int i = 0; i < 16 && off + i < n; ++i)
           f[i >> 2] |= (uint32_t)mk.at(off + i) << (8 * (i & 3));
@@ -253,6 +256,25 @@ examples_kernel(const int32_t* __restrict__ doc_rows, int32_t n_docs,
   }
 }
 
+// Mean and example-mean weightings: every document's weight into a table
+// (the mean's needs the total row count, summed from the group totals).
+__global__ void __launch_bounds__(kThreads)
+doc_weights_kernel(WeightArgs wa, int32_t n_docs, const int32_t* __restrict__ group_sums,
+                   int32_t n_groups, float* __restrict__ w_doc) {
+  __shared__ int s_total;
+  if (threadIdx.x < 64) {
+    int tot = 0;
+    if (wa.mode == MDLM_WEIGHT_MEAN)
+      for (int g = threadIdx.x; g < n_groups; g += 64) tot += group_sums[g];
+    tot = wave_sum(tot);
+    if (threadIdx.x == 0) s_total = tot;
+  }
+  __syncthreads();
+  const int32_t n_examples = wa.mode == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED ? *wa.n_examples : 0;
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b < n_docs) w_doc[b] = doc_weight(wa, b, s_total, n_examples);
+}
+
 // Per group of 1024 tiles: counts -> exclusive offsets within the group (in
 // place) and the group's total.
 __global__ void __launch_bounds__(kGroup)
@@ -283,12 +305,14 @@ group_scan_kernel(int32_t* __restrict__ tile_counts, int64_t n_tiles,
 
 // Scatter: four rounds per tile; in round j thread t owns the 4 consecutive
 // tokens at 1024 j + 4 t, so every load is contiguous across the wave.
-template <bool kShifted, bool kVec>
+template <bool kShifted, bool kVec, bool kC, bool kE>
 __global__ void __launch_bounds__(kThreads)
-scatter_kernel(RowMasks mk, const int32_t* __restrict__ x0, int64_t n,
+scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict__ eligible,
+               const int32_t* __restrict__ x0, int64_t n,
                const int32_t* __restrict__ cu, int32_t n_docs,
                const int32_t* __restrict__ tile_lo, const int32_t* __restrict__ tile_hi,
-               WeightArgs wa, const int32_t* __restrict__ tile_offsets,
+               const double* __restrict__ p_doc, double scale,
+               const float* __restrict__ w_doc, const int32_t* __restrict__ tile_offsets,
                const int32_t* __restrict__ group_sums, int32_t n_groups,
                int32_t* __restrict__ row_idx, int32_t* __restrict__ tgt, float* __restrict__ w,
                int32_t* __restrict__ n_rows) {
@@ -298,8 +322,11 @@ scatter_kernel(RowMasks mk, const int32_t* __restrict__ x0, int64_t n,
   __shared__ int32_t s_row[kBufs][kRoundTok];
   __shared__ int32_t s_tgt[kBufs][kRoundTok];
   __shared__ float s_w[kBufs][kRoundTok];
-  __shared__ int s_base, s_total;
+  __shared__ int s_base;
 
+  // (the masks arrive as restrict-qualified parameters so that their loads
+  // are known not to alias the row stores)
+  const RowMasks<kC, kE> mk{corrupted, eligible};
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tile = blockIdx.x;
   const int64_t t0 = tile * kTile;
@@ -307,8 +334,16 @@ scatter_kernel(RowMasks mk, const int32_t* __restrict__ x0, int64_t n,
   tile_range(tile_lo, tile_hi, n_docs, tile, &dlo, &dhi);
   const int nd = dhi - dlo + 1;
   const bool cached = nd <= kLdsDocs;
-  if (cached)
+  // per-document weight: scale / (p_b N) computed here, or from the table
+  // of the other weightings
+  auto weight_of_doc = [&](int b) {
+#pragma clang fp contract(off)
+    return w_doc ? w_doc[b] : (float)(scale / (p_doc[b] * (double)n));
+  };
+  if (cached) {
     for (int i = tid; i <= nd; i += kThreads) s_cu[i] = cu[dlo + i];
+    for (int i = tid; i < nd; i += kThreads) s_wd[i] = weight_of_doc(dlo + i);
+  }
   const int grp = (int)(tile / kGroup);
   if (wave == 0) {
     // this tile's offset: its place in its group plus the groups before it
@@ -316,23 +351,12 @@ scatter_kernel(RowMasks mk, const int32_t* __restrict__ x0, int64_t n,
     for (int g = lane; g < grp; g += 64) b += group_sums[g];
     b = wave_sum(b);
     if (lane == 0) s_base = b + tile_offsets[tile];
-  } else if (wave == 1 && (tile == 0 || wa.mode == MDLM_WEIGHT_MEAN)) {
-    // the total row count (the mean weighting divides by it)
+  } else if (wave == 1 && tile == 0) {
     int tot = 0;
     for (int g = lane; g < n_groups; g += 64) tot += group_sums[g];
     tot = wave_sum(tot);
-    if (lane == 0) {
-      s_total = tot;
-      if (tile == 0) *n_rows = tot;
-    }
+    if (lane == 0) *n_rows = tot;
   }
-  __syncthreads();
-  const int64_t total_rows = wa.mode == MDLM_WEIGHT_MEAN ? s_total : 0;
-  const int32_t n_examples =
-      wa.mode == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED ? *wa.n_examples : 0;
-  if (cached)
-    for (int i = tid; i < nd; i += kThreads)
-      s_wd[i] = doc_weight(wa, dlo + i, total_rows, n_examples);
   __syncthreads();
   int64_t out = s_base;
 
@@ -343,7 +367,7 @@ scatter_kernel(RowMasks mk, const int32_t* __restrict__ x0, int64_t n,
     uint32_t sel = 0;
     int32_t vals[4] = {0, 0, 0, 0};
     float wts[4] = {0.f, 0.f, 0.f, 0.f};
-    uint32_t mv = 0;  // bit 8k: token g0 + k is corrupted and eligible
+    uint32_t mv = 0;  // byte k nonzero iff token g0 + k is corrupted and eligible
     const int cnt_here = g0 < n ? (int)min<int64_t>(4, n - g0) : 0;
     if (kVec && cnt_here == 4) {
       mv = mk.word(g0);
@@ -387,7 +411,8 @@ scatter_kernel(RowMasks mk, const int32_t* __restrict__ x0, int64_t n,
       int d = cached ? lds_find_doc(s_cu, nd, g0) : find_doc(cu, dlo, dhi, g0) - dlo;
       int64_t d_beg = cached ? s_cu[d] : cu[dlo + d];
       int64_t d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
-      float wd = cached ? s_wd[d] : doc_weight(wa, dlo + d, total_rows, n_examples);
+      auto weight_of = [&](int dd) { return cached ? s_wd[dd] : weight_of_doc(dlo + dd); };
+      float wd = weight_of(d);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int64_t g = g0 + k;
@@ -399,7 +424,7 @@ scatter_kernel(RowMasks mk, const int32_t* __restrict__ x0, int64_t n,
               d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
             } while (g >= d_end && d < nd - 1);
             d_beg = cached ? s_cu[d] : cu[dlo + d];
-            wd = cached ? s_wd[d] : doc_weight(wa, dlo + d, total_rows, n_examples);
+            wd = weight_of(d);
           }
           if (!kShifted || g != d_beg) {
             sel |= 1u << k;
@@ -457,9 +482,60 @@ size_t compact_workspace_bytes(int64_t n_tokens, int32_t n_docs, int32_t weighti
   // counts, first and last document per tile; one total per group; for the
   // example-mean weighting, scored rows per document and the example count
   size_t words = 3 * (size_t)tiles + (size_t)groups;
+  if (weighting != MDLM_WEIGHT_INV_P) words += (size_t)std::max(n_docs, 0);  // weights
   if (weighting == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED) words += (size_t)std::max(n_docs, 0) + 1;
   return words * sizeof(int32_t);
 }
+
+namespace {
+
+struct Launch {
+  int64_t n;
+  const int32_t* cu;
+  int32_t n_docs;
+  int64_t tiles, groups;
+  int32_t *counts, *tile_lo, *tile_hi, *group_sums, *doc_rows, *n_examples;
+  float* w_doc;  // per-document weights (mean and example-mean weightings), else null
+  const int32_t* x0;
+  WeightArgs wa;
+  int32_t *row_idx, *tgt;
+  float* w;
+  int32_t* n_rows;
+  bool vec;
+  hipStream_t stream;
+};
+
+// The passes after tile_docs_kernel, for one combination of alignment and
+// masks present.
+template <bool kShifted, bool kC, bool kE>
+void run_passes(const Launch& L, RowMasks<kC, kE> mk) {
+  hipStream_t st = L.stream;
+  if (L.wa.mode == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED) {
+    const unsigned g = (unsigned)((L.n_docs + kWaves - 1) / kWaves);
+    doc_rows_kernel<kShifted, kC, kE><<<g, kThreads, 0, st>>>(mk, L.n, L.cu, L.n_docs,
+                                                              L.doc_rows);
+    examples_kernel<<<1, 1024, 0, st>>>(L.doc_rows, L.n_docs, L.n_examples);
+  }
+  const unsigned count_grid = (unsigned)((L.tiles + kWaves - 1) / kWaves);
+  count_kernel<kShifted, kC, kE><<<count_grid, kThreads, 0, st>>>(
+      mk, L.n, L.cu, L.n_docs, L.tile_lo, L.tile_hi, L.tiles, L.counts);
+  group_scan_kernel<<<(unsigned)L.groups, kGroup, 0, st>>>(L.counts, L.tiles, L.group_sums);
+  if (L.w_doc)
+    doc_weights_kernel<<<(unsigned)((L.n_docs + kThreads - 1) / kThreads), kThreads, 0, st>>>(
+        L.wa, L.n_docs, L.group_sums, (int32_t)L.groups, L.w_doc);
+  if (L.vec)
+    scatter_kernel<kShifted, true, kC, kE><<<(unsigned)L.tiles, kThreads, 0, st>>>(
+        mk.corrupted, mk.eligible, L.x0, L.n, L.cu, L.n_docs, L.tile_lo, L.tile_hi, L.wa.p_doc,
+        L.wa.scale, L.w_doc,
+        L.counts, L.group_sums, (int32_t)L.groups, L.row_idx, L.tgt, L.w, L.n_rows);
+  else
+    scatter_kernel<kShifted, false, kC, kE><<<(unsigned)L.tiles, kThreads, 0, st>>>(
+        mk.corrupted, mk.eligible, L.x0, L.n, L.cu, L.n_docs, L.tile_lo, L.tile_hi, L.wa.p_doc,
+        L.wa.scale, L.w_doc,
+        L.counts, L.group_sums, (int32_t)L.groups, L.row_idx, L.tgt, L.w, L.n_rows);
+}
+
+}  // namespace
 
 hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, const int32_t* x0,
                           int64_t n, const int32_t* cu, int32_t n_docs, const double* p_doc,
@@ -476,45 +552,37 @@ hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, con
   int32_t* tile_lo = counts + tiles;
   int32_t* tile_hi = tile_lo + tiles;
   int32_t* group_sums = tile_hi + tiles;
-  const RowMasks mk{corrupted, eligible};
   WeightArgs wa{weighting, scale, clip, p_doc, n, nullptr, nullptr};
-  const bool shifted = align == MDLM_SHIFTED;
+  // after the group totals: (mean, example mean) one weight per document;
+  // (example mean) scored rows per document and the example count
+  float* w_doc = nullptr;
+  int32_t* doc_rows = nullptr;
+  int32_t* n_examples = nullptr;
+  if (weighting != MDLM_WEIGHT_INV_P) w_doc = reinterpret_cast<float*>(group_sums + groups);
   if (weighting == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED) {
-    int32_t* doc_rows = group_sums + groups;
-    int32_t* n_examples = doc_rows + n_docs;
-    const unsigned g = (unsigned)((n_docs + kWaves - 1) / kWaves);
-    if (shifted)
-      doc_rows_kernel<true><<<g, kThreads, 0, stream>>>(mk, n, cu, n_docs, doc_rows);
-    else
-      doc_rows_kernel<false><<<g, kThreads, 0, stream>>>(mk, n, cu, n_docs, doc_rows);
-    examples_kernel<<<1, 1024, 0, stream>>>(doc_rows, n_docs, n_examples);
+    doc_rows = reinterpret_cast<int32_t*>(w_doc + n_docs);
+    n_examples = doc_rows + n_docs;
     wa.doc_rows = doc_rows;
     wa.n_examples = n_examples;
   }
   tile_docs_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(cu, n_docs, n,
                                                                                 tile_lo, tile_hi);
-  const unsigned count_grid = (unsigned)((tiles + kWaves - 1) / kWaves);
-  if (shifted)
-    count_kernel<true><<<count_grid, kThreads, 0, stream>>>(mk, n, cu, n_docs, tile_lo, tile_hi,
-                                                            tiles, counts);
-  else
-    count_kernel<false><<<count_grid, kThreads, 0, stream>>>(mk, n, cu, n_docs, tile_lo, tile_hi,
-                                                             tiles, counts);
-  group_scan_kernel<<<(unsigned)groups, kGroup, 0, stream>>>(counts, tiles, group_sums);
   const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)corrupted % 4 == 0) &&
                    ((uintptr_t)eligible % 4 == 0);
-#define MDLM_SCATTER_LAUNCH(SH, VEC)                                                           \
-  scatter_kernel<SH, VEC><<<(unsigned)tiles, kThreads, 0, stream>>>(                           \
-      mk, x0, n, cu, n_docs, tile_lo, tile_hi, wa, counts, group_sums, (int32_t)groups, row_idx, \
-      tgt, w, n_rows)
-  if (shifted) {
-    if (vec) MDLM_SCATTER_LAUNCH(true, true);
-    else MDLM_SCATTER_LAUNCH(true, false);
-  } else {
-    if (vec) MDLM_SCATTER_LAUNCH(false, true);
-    else MDLM_SCATTER_LAUNCH(false, false);
+  const Launch L{n, cu, n_docs, tiles, groups, counts, tile_lo, tile_hi, group_sums, doc_rows,
+                 n_examples, w_doc, x0, wa, row_idx, tgt, w, n_rows, vec, stream};
+  const bool shifted = align == MDLM_SHIFTED;
+  const int key = (shifted ? 4 : 0) | (corrupted ? 2 : 0) | (eligible ? 1 : 0);
+  switch (key) {
+    case 0: run_passes<false, false, false>(L, {corrupted, eligible}); break;
+    case 1: run_passes<false, false, true>(L, {corrupted, eligible}); break;
+    case 2: run_passes<false, true, false>(L, {corrupted, eligible}); break;
+    case 3: run_passes<false, true, true>(L, {corrupted, eligible}); break;
+    case 4: run_passes<true, false, false>(L, {corrupted, eligible}); break;
+    case 5: run_passes<true, false, true>(L, {corrupted, eligible}); break;
+    case 6: run_passes<true, true, false>(L, {corrupted, eligible}); break;
+    default: run_passes<true, true, true>(L, {corrupted, eligible}); break;
   }
-#undef MDLM_SCATTER_LAUNCH
   return hipGetLastError();
 }
 

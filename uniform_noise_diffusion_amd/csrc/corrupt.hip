@@ -107,6 +107,9 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
   __shared__ int32_t s_cu[kLdsDocs + 1];
   __shared__ int s_cnt[kLdsDocs];
   __shared__ uint32_t s_thr[kLdsDocs];
+  // per 256-token window of the block (window wave + 4 j is round j of wave
+  // `wave`): its first local document | (last - first) << 16
+  __shared__ int s_win[kRounds * kThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t blk0 = (int64_t)blockIdx.x * kTokPerBlock;
@@ -129,6 +132,18 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
     }
   }
   __syncthreads();
+  if (cached && nd > 1) {
+    // the windows' document ranges, once per block (block-uniform branch)
+    if (tid < kRounds * kThreads / 64) {
+      const int64_t ws = blk0 + 256 * (int64_t)tid;
+      if (ws < blk1) {
+        const int d0 = lds_find_doc(s_cu, nd, ws);
+        const int d1 = lds_find_doc(s_cu, nd, min(ws + 256, blk1) - 1);
+        s_win[tid] = d0 | ((d1 - d0) << 16);
+      }
+    }
+    __syncthreads();
+  }
   // Bernoulli threshold of local document d (from LDS when cached)
   auto thr_of = [&](int d) { return cached ? s_thr[d] : threshold_of(p_doc[dlo + d]); };
 
@@ -157,15 +172,19 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
     // per token.
     const int64_t gw = blk0 + 4 * (int64_t)(64 * wave + kThreads * j);
     if (kVec && cached && gw + 256 <= n) {
-      const int dw = lds_find_doc(s_cu, nd, gw);
+      int dw = 0, span = 0;
+      if (nd > 1) {
+        const int pk = s_win[wave + 4 * j];
+        dw = pk & 0xffff;
+        span = pk >> 16;
+      }
       const int4 v = *reinterpret_cast<const int4*>(x0 + g0);
-      if (gw + 256 <= (int64_t)s_cu[dw + 1]) {
+      if (span == 0) {
         const int c = corrupt4<kUniform>(v, g0, s_thr[dw], k0, k1, mask_id, rand_vocab, xt,
                                          corrupted);
         if (lane == 0 && c) atomicAdd(&s_cnt[dw], c);
         continue;
       }
-      const int span = lds_find_doc(s_cu, nd, gw + 255) - dw;
       if (span <= 3) {
         // start of local documents dw+1..dw+3 (past the span: never reached)
         const int64_t b1 = s_cu[dw + 1];
