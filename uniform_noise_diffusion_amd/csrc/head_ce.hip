@@ -25,6 +25,9 @@
 //      the device so that the tile x slice units fill the grid.
 //   5. zero_kernel + scatter_kernel: d_hidden = 0, then d_hidden[row_idx[j]]
 //      = sum of the S slices of dH[j], in the hidden dtype.
+//   6. (trained head only) gather_rows_kernel copies the scored rows of
+//      hidden into the workspace and dw_kernel forms dW = G^T Hs over
+//      256 x 256 (vocab x hidden) tiles, K = scored rows, per vocabulary chunk.
 #include "mdlm_internal.h"
 
 #include <math.h>
@@ -197,9 +200,9 @@ struct LogitsArgs {
 // fragments of 16-deep slice kk+1 are read from LDS while the MFMAs of slice
 // kk run.  `ra` reads the A fragments of a slice, `rb` the B fragments.
 // kVmem global->LDS loads issued just before the call (the next stage's
-// prefetch) are spread over the step, one before every kVmemEvery-th MFMA:
-// issued together at the top of the step they stall the issuing waves (and
-// so the matrix pipes) until the memory pipeline has taken them.
+// prefetch) are spread over the first MFMAs of the step, one before every
+// kVmemEvery-th MFMA, rather than left to the scheduler, which would sink
+// them to the end of the step (leaving them no time to land).
 template <int kReads, int kVmem, typename ReadA, typename ReadB>
 __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB rb) {
   bf16x8 af[2][4], bfr[2][kNJ];
@@ -1067,8 +1070,9 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
                                             reinterpret_cast<uint8_t*>(x.d_hidden) + n16 * 16,
                                             tail);
   }
-  if (want_dw) {
-    // dW = 0 first: with no scored rows it stays zero
+  if (want_dw && max_rows == 0) {
+    // no kernel below runs: dW = 0 here (otherwise dw_kernel writes every
+    // entry, zeros included, whatever the device row count)
     const size_t bytes = (size_t)x.V * x.H * sizeof(float);
     const int64_t n16 = (int64_t)(bytes / 16);
     const int64_t tail = (int64_t)(bytes % 16);
