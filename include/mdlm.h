@@ -268,7 +268,9 @@ size_t mdlm_head_ce_workspace_min_bytes(int64_t max_rows, int32_t H, int32_t V,
  *   dtype       MDLM_BF16 or MDLM_F32.
  *   n_tokens    rows of hidden / d_hidden, >= 0.
  *   H           > 0, a multiple of 64 (else MDLM_EUNSUPPORTED).
- *   V           > 0.
+ *   V           > 0.  With MDLM_BF16, hidden and W must each be smaller
+ *               than 4 GiB (n_tokens * H * 2 and V * H * 2 bytes; else
+ *               MDLM_EUNSUPPORTED).
  *   row_idx, tgt, w   as written by mdlm_compact_masked (tgt in [0, V)).
  *   n_rows      [1] int32 device scalar, 0 <= *n_rows <= max_rows.
  *   max_rows    host bound on *n_rows, 0 <= max_rows <= n_tokens; sizes

@@ -146,6 +146,8 @@ def head_call(lib, **kw):
     (dict(max_rows=65), B.MDLM_EINVAL, "max_rows"),
     (dict(max_rows=-1), B.MDLM_EINVAL, "max_rows"),
     (dict(H=96), B.MDLM_EUNSUPPORTED, "multiple of 64"),
+    (dict(n=1 << 19, H=4096, max_rows=8), B.MDLM_EUNSUPPORTED, "below 4 GiB"),
+    (dict(V=1 << 19, H=4096), B.MDLM_EUNSUPPORTED, "below 4 GiB"),
     (dict(softcap=-1.0), B.MDLM_EINVAL, "softcap"),
     (dict(softcap=float("inf")), B.MDLM_EINVAL, "softcap"),
     (dict(), B.MDLM_EINVAL, "null loss"),

@@ -169,3 +169,50 @@ def test_large_stream_sampled():
     doc = rows // L
     assert np.array_equal(w.view(np.uint32),
                           (1.0 / (p_all[doc] * float(n))).astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("align", [oracle.ALIGNED, oracle.SHIFTED])
+def test_maximum_stream_sampled(align):
+    """The largest stream the ABI accepts: 2^31 - 1 tokens (documents of 4,096,
+    the last one 4,095 long).  p is compared in full; the corruption on
+    sampled documents including the last ones, whose token indices are the
+    largest; the compaction by invariants checked on the device (rows are the
+    scored positions in order, targets gathered from x0, weights
+    1 / (p N))."""
+    L = 4096
+    n = 2**31 - 1
+    n_docs = -(-n // L)
+    cu = torch.arange(0, n_docs + 1, dtype=torch.int64, device=DEV) * L
+    cu[-1] = n
+    cu = cu.to(torch.int32)
+    g = torch.Generator(device=DEV).manual_seed(3)
+    x0 = torch.randint(0, 126336, (n,), dtype=torch.int32, device=DEV, generator=g)
+    step = MdlmLossStep(n, n_docs, 64, 64, device=DEV, head_workspace_bytes=0,
+                        want_grad=False)
+    seed = 2**63 + 7
+    step.corrupt(x0, cu, seed, 1e-3, oracle.NOISE_ABSORB, 126336, 126464)
+    step.compact(x0, cu, align)
+    torch.cuda.synchronize()
+    _, p_all, thr_all = oracle.noise_levels(seed, 1e-3, n_docs)
+    assert np.array_equal(host(step.p_doc).view(np.uint64), p_all.view(np.uint64))
+    for b in [0, 1, n_docs // 2, n_docs - 2, n_docs - 1]:
+        lo, hi = b * L, min((b + 1) * L, n)
+        wsub = token_words(seed, hi - lo, oracle.mdlm.TAG_BERNOULLI, start=lo)
+        exp = ((wsub >> 8) < thr_all[b]).astype(np.uint8)
+        assert np.array_equal(host(step.corrupted[lo:hi]), exp), b
+        assert np.array_equal(host(step.xt[lo:hi]),
+                              np.where(exp == 1, 126336, host(x0[lo:hi]))), b
+        assert int(host(step.doc_counts[b:b + 1])[0]) == int(exp.sum())
+    # compaction invariants on the device
+    m = int(host(step.n_rows)[0])
+    scored = step.corrupted.bool()
+    if align == oracle.SHIFTED:
+        scored[cu[:-1].long()] = False
+    pos = torch.nonzero(scored).flatten()
+    assert m == pos.numel()
+    rows = step.row_idx[:m].long()
+    assert torch.equal(rows, pos - (1 if align == oracle.SHIFTED else 0))
+    assert torch.equal(step.tgt[:m], x0[pos])
+    p_dev = torch.from_numpy(p_all).to(DEV)
+    want_w = (1.0 / (p_dev[pos // L] * float(n))).to(torch.float32)
+    assert torch.equal(step.w[:m].view(torch.int32), want_w.view(torch.int32))

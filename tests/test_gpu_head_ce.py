@@ -196,3 +196,19 @@ def test_full_size_workload_sampled_rows(k, align):
     mask = torch.ones(wl.n_tokens, dtype=torch.bool, device=DEV)
     mask[torch.from_numpy(rows).to(DEV)] = False
     assert torch.count_nonzero(s.d_hidden[mask]).item() == 0
+
+
+def test_one_and_two_entry_vocabularies():
+    """V = 1: every logit is the target's, so CE and the gradient are exactly
+    zero (max = target logit, one term of the sum); V = 2 against the oracle."""
+    import dataclasses
+    base = _small(71, n_docs=3, max_len=200, H=64, V=2)
+    wl1 = dataclasses.replace(base.wl, V=1, mask_id=0, rand_vocab=1, token_hi=0)
+    inp = WL.Inputs(wl1, np.zeros_like(base.x0), base.cu_seqlens, base.hidden,
+                    base.W[:1].copy(), base.hidden_bits, base.W_bits[:1].copy())
+    s = run_step(inp, seed=2, eps=0.7, align=oracle.ALIGNED, softcap=0.0)
+    assert int(host(s.n_rows)[0]) > 0
+    assert float(host(s.loss)[0]) == 0.0
+    assert np.all(d_hidden_host(s) == 0.0)
+    inp2 = _small(72, n_docs=3, max_len=200, H=64, V=2)
+    _compare_full(inp2, seed=3, eps=0.7, align=oracle.SHIFTED, softcap=2.0)

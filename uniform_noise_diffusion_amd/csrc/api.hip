@@ -177,6 +177,11 @@ static int head_common(const char* fn, const void* hidden, const void* W, int32_
     return fail(MDLM_EINVAL, "%s: max_rows must lie in [0, n_tokens]", fn);
   if (n_tokens > INT32_MAX) return fail(MDLM_EUNSUPPORTED, "%s: n_tokens must be below 2^31", fn);
   if (H % 64 != 0) return fail(MDLM_EUNSUPPORTED, "%s: H = %d is not a multiple of 64", fn, H);
+  // the bf16 kernels address hidden (gathered rows) and W (the dH product)
+  // through 32-bit byte offsets
+  if (dtype == MDLM_BF16 && (n_tokens * (int64_t)H * 2 >= (int64_t)1 << 32 ||
+                             (int64_t)V * H * 2 >= (int64_t)1 << 32))
+    return fail(MDLM_EUNSUPPORTED, "%s: bf16 hidden and W must each be below 4 GiB", fn);
   if (!(softcap >= 0.f) || !isfinite(softcap))
     return fail(MDLM_EINVAL, "%s: softcap must be finite and >= 0", fn);
   if (!loss) return fail(MDLM_EINVAL, "%s: null loss", fn);
