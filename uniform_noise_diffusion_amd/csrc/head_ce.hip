@@ -490,7 +490,7 @@ struct DhArgs {
 };
 
 // Number of K-slices: the fewest (up to kMaxSplit) that keep the grid busy,
-// judged by the share of workgroup slots the tile x slice units fill.
+// measured by the share of workgroup slots the tile x slice units fill.
 __host__ __device__ __forceinline__ int dh_splits(int64_t tiles, int grid, int ki) {
   if (tiles <= 0) return 1;
   int best = 1;
