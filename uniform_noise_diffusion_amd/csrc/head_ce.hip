@@ -11,18 +11,23 @@
 //   1. logits_kernel<fwd>: z = W h over 256 x 256 (vocab x row) tiles, K = H,
 //      on bf16 MFMA with fp32 accumulation.  Operands go from global memory
 //      straight into a two-stage LDS ring (no register staging), two waves per
-//      SIMD.  The epilogue caps, takes each row's (max, sum 2^(s-max)) over the
-//      tile's 256 vocabulary entries and picks the target logit.  Logits never
-//      leave registers.
-//   2. merge_kernel: per row, combine the per-tile partials into the
-//      log-sum-exp and CE; per-block sums of w * CE in fp64.
+//      SIMD.  The epilogue caps, takes each row's (max m_h, sum 2^(s - m_h))
+//      over each 128-entry half of the tile and picks the target logit.
+//      Logits never leave registers.  When the gradient is wanted and the
+//      workspace holds G for the whole vocabulary, the epilogue also stashes
+//      2^(s - m_h) zhat' (zhat' = 1 - (zhat/c)^2 with a softcap c, else 1) in
+//      G as bf16: the softmax up to a per-(row, half tile) factor.
+//   2. merge_kernel: per row, combine the partials into the log-sum-exp and
+//      CE; per-block sums of w * CE in fp64.
 //   3. loss_kernel: fixed-order sum of the block sums -> loss.
-//   4. (gradient) for each vocabulary chunk [v0, v1) (one chunk unless the
-//      workspace is small): logits_kernel<grad> recomputes the tiles and
-//      writes G = w (softmax - onehot) zhat' as bf16; dh_kernel forms
-//      dH = G W over 256 x 256 (row x hidden) tiles with W read through LDS
-//      transpose loads, split along the vocabulary into S slices chosen on
-//      the device so that the tile x slice units fill the grid.
+//   4. (gradient) G = w (softmax - onehot) zhat' as bf16, either from the
+//      stash (stash_scale_kernel multiplies by w 2^(m_h - lse) and rewrites
+//      the target entries) or, with a smaller workspace, per vocabulary chunk
+//      [v0, v1) by logits_kernel<grad>, which recomputes the tiles.
+//      dh_kernel forms dH = G W over 256 x 256 (row x hidden) tiles with W
+//      read through LDS transpose loads, split along the vocabulary into S
+//      slices chosen on the device so that the tile x slice units fill the
+//      grid.
 //   5. zero_kernel + scatter_kernel: d_hidden = 0, then d_hidden[row_idx[j]]
 //      = sum of the S slices of dH[j], in the hidden dtype.
 //   6. (trained head only) gather_rows_kernel copies the scored rows of
@@ -66,6 +71,9 @@ constexpr int kLdsBytes = 2 * kStageBytes;    // two stages: 128 KiB
 #endif
 constexpr int kVmemEvery = MDLM_VMEM_EVERY;  // MFMAs per interleaved prefetch load
 static_assert(2 * kLoads * kVmemEvery <= 4 * (16 / kWaves) * (64 / 16), "loads fit in a step");
+#ifndef MDLM_STASH
+#define MDLM_STASH 1
+#endif
 constexpr int kMaxSplit = 8;          // K-splits of the dH product
 constexpr int kMergeRows = 4;         // rows per merge block (one per wave)
 constexpr int kGrid = 256;            // persistent grid: one workgroup per CU
@@ -189,10 +197,11 @@ struct LogitsArgs {
   float inv_softcap;
   int v_begin;  // vocabulary range of this launch
   int v_end;
-  float2* partial;  // fwd: [ceil(V/kTile)][max_rows] (max, sum) in log2 units
+  float2* partial;  // fwd: [2 ceil(V/kTile)][max_rows] (max, sum) per 128-entry half
+                    // tile, in log2 units
   float* ztgt;      // [max_rows] capped target logit x log2(e) (fwd writes, grad reads)
   const float* lse; // grad: [max_rows]
-  bf16_t* G;        // grad: [max_rows][ldg], column = v - v_begin
+  bf16_t* G;        // grad, or fwd with the stash: [max_rows][ldg], column = v - v_begin
   int64_t ldg;
 };
 
@@ -249,13 +258,16 @@ __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB r
 // (operand B, rows of hidden gathered through row_idx), K = H.  Wave w owns
 // vocabulary rows 128 (w % 2) .. +127 and scored rows kWB (w / 2) .. +kWB-1:
 // a 4 x kNJ grid of 32 x 32 MFMA blocks.
-template <bool kGrad, bool kCap>
+// kStash (forward only): the epilogue also keeps the tile's unnormalised
+// softmax, 2^(s - m_t) zhat' with m_t the row's maximum over the tile, as bf16
+// in G, so that the gradient needs no second pass over the logits.
+template <bool kGrad, bool kCap, bool kStash = false>
 __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
+  static_assert(!(kGrad && kStash), "the stash is written by the forward pass");
   // the two stages are separate objects so that the compiler can tell a
   // prefetch into one from reads of the other
   __shared__ __attribute__((aligned(1024))) char smem0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char smem1[kStageBytes];
-  __shared__ float2 red[2][kTile];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -400,16 +412,40 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
             }
           // (the target is never past the vocabulary, so never masked)
           if (mvalid && holds_tgt) a.ztgt[m] = pick_entry(sv, dt);
+          // the row's maximum over this wave's 128 entries (two lanes hold
+          // 64 each); -inf when all of them lie past the vocabulary
           mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          const float mref = mx == -INFINITY ? 0.f : mx;
           float sum = 0.f;
-          if (mx != -INFINITY) {
+          bf16_t* grow = a.G + (int64_t)m * a.ldg - a.v_begin;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 4; ++i)
 #pragma unroll
-              for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f(sv[i][e] - mx);
-          }
+            for (int q = 0; q < 4; ++q) {
+              float g[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float sc = sv[i][4 * q + r];
+                const float e2 = __builtin_amdgcn_exp2f(sc - mref);
+                sum += e2;
+                if (kStash) {
+                  float gv = e2;
+                  if (kCap) {
+                    const float th = sc * kLn2 * a.inv_softcap;
+                    gv = e2 * (1.f - th * th);
+                  }
+                  if (!kFull) gv = 32 * i + 8 * q + r < lim ? gv : 0.f;
+                  g[r] = gv;
+                }
+              }
+              if (kStash && mvalid)
+                *reinterpret_cast<uint2*>(grow + vl + 32 * i + 8 * q) =
+                    make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
+            }
           sum += __shfl_xor(sum, 32, 64);
-          if (lane < 32) red[wa][wb * kWB + 32 * j + lane] = make_float2(mx, sum);
+          if (lane < 32 && mvalid)
+            a.partial[(int64_t)(2 * ((v0 - a.v_begin) / kTile) + wa) * a.max_rows + m] =
+                make_float2(mx, sum);
         } else if (mvalid) {
           // G = w p cap' everywhere, then the target entry is rewritten with
           // w (p - 1) cap' from the capped target logit the forward pass kept
@@ -451,25 +487,6 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
       epilogue(std::true_type{});
     else
       epilogue(std::false_type{});
-    if (!kGrad) {
-      __syncthreads();
-      if (wa == 0) {
-#pragma unroll
-        for (int j = 0; j < kNJ; ++j) {
-          const int col = wb * kWB + 32 * j + (lane & 31);
-          const int m = m0 + col;
-          if (lane < 32 && m < n_rows) {
-            const float2 p0 = red[0][col], p1 = red[1][col];
-            const float mx = fmaxf(p0.x, p1.x);
-            float s = 0.f;
-            if (mx != -INFINITY)
-              s = p0.y * __builtin_amdgcn_exp2f(p0.x - mx) +
-                  p1.y * __builtin_amdgcn_exp2f(p1.x - mx);
-            a.partial[(int64_t)((v0 - a.v_begin) / kTile) * a.max_rows + m] = make_float2(mx, s);
-          }
-        }
-      }
-    }
   }
 }
 
@@ -868,6 +885,55 @@ merge_kernel(const float2* __restrict__ partial, int n_vt, int max_rows,
   }
 }
 
+// Turns the forward pass's stash into G: entry v of row m becomes
+// w_m 2^(m_t - lse2_m) times the stashed 2^(s - m_t) zhat' (t = v / 256, so
+// the factor is w_m p zhat'), and the target entry w_m (p - 1) zhat' from the
+// capped target logit.  One 16-byte group of eight entries per thread,
+// segments of kScaleSeg entries per block iteration.
+constexpr int kScaleSeg = kThreads * 8;
+
+__global__ void __launch_bounds__(kThreads)
+stash_scale_kernel(bf16_t* __restrict__ G, int64_t ldg, const float2* __restrict__ partial,
+                   int max_rows, const float* __restrict__ lse, const float* __restrict__ ztgt,
+                   const int32_t* __restrict__ tgt, const float* __restrict__ w,
+                   const int32_t* __restrict__ n_rows_ptr, int V, float inv_softcap) {
+  const int n_rows = min(*n_rows_ptr, max_rows);
+  const int n_seg = (int)((ldg + kScaleSeg - 1) / kScaleSeg);
+  const int64_t units = (int64_t)n_rows * n_seg;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int m = (int)(u / n_seg);
+    const int v = (int)(u % n_seg) * kScaleSeg + (int)threadIdx.x * 8;
+    if (v >= ldg) continue;
+    const float lse2 = lse[m] * kLog2e;
+    const float wm = w[m];
+    const float f =
+        wm * __builtin_amdgcn_exp2f(partial[(int64_t)(v / (kTile / 2)) * max_rows + m].x - lse2);
+    uint4* gp = reinterpret_cast<uint4*>(G + (int64_t)m * ldg + v);
+    const uint4 in = *gp;
+    const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(wd[k] << 16) * f;
+      x[2 * k + 1] = __uint_as_float(wd[k] & 0xFFFF0000u) * f;
+    }
+    const int dt = tgt[m] - v;
+    if ((unsigned)dt < 8u && v + dt < V) {
+      const float zt2 = ztgt[m];
+      float dc = 1.f;
+      if (inv_softcap > 0.f) {
+        const float th = zt2 * kLn2 * inv_softcap;
+        dc = 1.f - th * th;
+      }
+      const float gt = (__builtin_amdgcn_exp2f(zt2 - lse2) - 1.f) * dc * wm;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = dt == e ? gt : x[e];
+    }
+    *gp = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                     pack_bf16x2(x[6], x[7]));
+  }
+}
+
 __global__ void __launch_bounds__(kThreads)
 loss_kernel(const double* __restrict__ block_sums, int n, float* __restrict__ loss) {
   __shared__ double s[kThreads];
@@ -1019,7 +1085,7 @@ Layout fixed_layout(int64_t max_rows, int H, int V, int dtype, bool grad, bool d
   L.n_vt = (V + kTile - 1) / kTile;
   L.n_bsum = (int)((max_rows + kMergeRows - 1) / kMergeRows);
   size_t off = 0;
-  L.partial = off; off = align_up(off + (size_t)L.n_vt * max_rows * sizeof(float2));
+  L.partial = off; off = align_up(off + (size_t)2 * L.n_vt * max_rows * sizeof(float2));
   L.ztgt = off;    off = align_up(off + (size_t)max_rows * sizeof(float));
   L.lse = off;     off = align_up(off + (size_t)max_rows * sizeof(float));
   L.bsum = off;    off = align_up(off + (size_t)std::max(L.n_bsum, 1) * sizeof(double));
@@ -1098,6 +1164,18 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     cus = kGrid;
   const int grid = std::max(8, std::min(kGrid, cus / 8 * 8));
 
+  // bf16 gradient: vocabulary chunks sized by the workspace given.  When G
+  // holds the whole vocabulary the forward pass stashes the unnormalised
+  // softmax there and the gradient needs no second logits pass.
+  int64_t vc = 0;
+  if (grad && x.dtype == MDLM_BF16) {
+    const size_t g_room = x.workspace_bytes - L.total;
+    vc = (int64_t)(g_room / ((size_t)max_rows * sizeof(bf16_t))) / kTile * kTile;
+    vc = std::min<int64_t>(vc, round_up(x.V, kTile));
+  }
+  const bool stash = MDLM_STASH && grad && x.dtype == MDLM_BF16 && vc >= x.V;
+  bf16_t* G = reinterpret_cast<bf16_t*>(ws + L.G);
+
   if (x.dtype == MDLM_BF16) {
     LogitsArgs la{};
     la.W = reinterpret_cast<const bf16_t*>(x.W);
@@ -1116,10 +1194,18 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     la.v_end = x.V;
     la.partial = partial;
     la.ztgt = ztgt;
-    if (x.softcap > 0.f)
+    la.G = G;
+    la.ldg = vc;
+    if (stash) {
+      if (x.softcap > 0.f)
+        logits_kernel<false, true, true><<<grid, kGemmThreads, 0, stream>>>(la);
+      else
+        logits_kernel<false, false, true><<<grid, kGemmThreads, 0, stream>>>(la);
+    } else if (x.softcap > 0.f) {
       logits_kernel<false, true><<<grid, kGemmThreads, 0, stream>>>(la);
-    else
+    } else {
       logits_kernel<false, false><<<grid, kGemmThreads, 0, stream>>>(la);
+    }
   } else {
     F32Args fa{};
     fa.W = reinterpret_cast<const float*>(x.W);
@@ -1139,7 +1225,9 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     dim3 g((unsigned)max_rows, (unsigned)L.n_vt);
     f32_logits_kernel<false><<<g, kThreads, 0, stream>>>(fa);
   }
-  merge_kernel<<<L.n_bsum, kThreads, 0, stream>>>(partial, L.n_vt, (int)max_rows, ztgt, x.tgt,
+  // (bf16: one partial per 128-entry half tile; fp32: one per 256-entry tile)
+  const int n_part = x.dtype == MDLM_BF16 ? 2 * L.n_vt : L.n_vt;
+  merge_kernel<<<L.n_bsum, kThreads, 0, stream>>>(partial, n_part, (int)max_rows, ztgt, x.tgt,
                                                   x.V, x.w, x.n_rows, lse, x.row_ce, bsum);
   loss_kernel<<<1, kThreads, 0, stream>>>(bsum, L.n_bsum, x.loss);
   if (!grad) return hipGetLastError();
@@ -1167,12 +1255,13 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     return hipGetLastError();
   }
 
-  // bf16 gradient: vocabulary chunks sized by the workspace given
-  const size_t g_room = x.workspace_bytes - L.total;
-  int64_t vc = (int64_t)(g_room / ((size_t)max_rows * sizeof(bf16_t))) / kTile * kTile;
-  vc = std::min<int64_t>(vc, round_up(x.V, kTile));
   float* part = reinterpret_cast<float*>(ws + L.part);
-  bf16_t* G = reinterpret_cast<bf16_t*>(ws + L.G);
+  if (stash) {
+    const int n_seg = (int)((vc + kScaleSeg - 1) / kScaleSeg);
+    const unsigned sgrid = (unsigned)std::min<int64_t>(max_rows * n_seg, (int64_t)cus * 32);
+    stash_scale_kernel<<<sgrid, kThreads, 0, stream>>>(G, vc, partial, (int)max_rows, lse, ztgt,
+                                                       x.tgt, x.w, x.n_rows, x.V, inv_cap);
+  }
 
   LogitsArgs la{};
   la.W = reinterpret_cast<const bf16_t*>(x.W);
@@ -1220,7 +1309,9 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     const int v1 = (int)std::min<int64_t>(x.V, v0 + vc);
     la.v_begin = (int)v0;
     la.v_end = v1;
-    if (x.softcap > 0.f)
+    if (stash)
+      ;  // G is already in place
+    else if (x.softcap > 0.f)
       logits_kernel<true, true><<<grid, kGemmThreads, 0, stream>>>(la);
     else
       logits_kernel<true, false><<<grid, kGemmThreads, 0, stream>>>(la);
