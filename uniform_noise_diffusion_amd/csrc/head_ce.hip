@@ -259,8 +259,9 @@ __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB r
 // vocabulary rows 128 (w % 2) .. +127 and scored rows kWB (w / 2) .. +kWB-1:
 // a 4 x kNJ grid of 32 x 32 MFMA blocks.
 // kStash (forward only): the epilogue also keeps the tile's unnormalised
-// softmax, 2^(s - m_t) zhat' with m_t the row's maximum over the tile, as bf16
-// in G, so that the gradient needs no second pass over the logits.
+// softmax, 2^(s - m_h) zhat' with m_h the row's maximum over the wave's
+// 128-entry half of the tile, as bf16 in G, so that the gradient needs no
+// second pass over the logits.
 template <bool kGrad, bool kCap, bool kStash = false>
 __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
   static_assert(!(kGrad && kStash), "the stash is written by the forward pass");
