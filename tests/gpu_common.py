@@ -64,3 +64,32 @@ def rel_l2(a, b):
 
 def d_hidden_host(step):
     return host(step.d_hidden.float())
+
+
+def far_row_case(seed, H, V, beta, philox_seed, eps, align, n_far=8, softcap=0.0):
+    """A small bf16 case in which n_far of the scored rows (of the oracle's
+    own corruption with `philox_seed`, `eps`, `align`) get one vocabulary
+    entry whose logit is about `beta` nats while their target's logit stays
+    near zero: W row v_k = beta h_r / |h_r|^2 for the row's hidden vector h_r.
+    Returns (inputs, indices of those rows in the scored-row list)."""
+    import dataclasses
+
+    import oracle
+    import workloads as WL
+
+    inp = WL.small_case(seed, n_docs=4, max_len=200, H=H, V=V, softcap=softcap)
+    wl = inp.wl
+    _, corrupted, p, _ = oracle.corrupt(inp.x0, inp.cu_seqlens, philox_seed, eps, wl.noise,
+                                        wl.mask_id, wl.rand_vocab)
+    rows, tgt, _ = oracle.compact(corrupted, inp.x0, inp.cu_seqlens, p, align)
+    assert rows.shape[0] >= 4 * n_far
+    picks = np.linspace(0, rows.shape[0] - 1, n_far).astype(np.int64)
+    taken = set(int(t) for t in tgt)
+    free = [v for v in range(V - 2, -1, -1) if v not in taken][:n_far]
+    assert len(free) == n_far
+    W = inp.W.copy()
+    for k, j in enumerate(picks):
+        h = inp.hidden[rows[j]].astype(np.float64)
+        W[free[k]] = (beta * h / np.dot(h, h)).astype(np.float32)
+    Wr, Wb = WL._round_bf16(W)
+    return dataclasses.replace(inp, W=Wr, W_bits=Wb), picks

@@ -18,7 +18,7 @@ import workloads as WL
 from uniform_noise_diffusion_amd import binding as B
 from uniform_noise_diffusion_amd.pipeline import MdlmLossStep
 
-from gpu_common import DEV, dev_float, dev_tokens, host, rel_l2
+from gpu_common import DEV, dev_float, dev_tokens, far_row_case, host, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -71,6 +71,22 @@ def test_dw_small_tiles_and_ragged_tails(H, V, align, softcap):
     rows, tgt, w = _oracle_rows(inp, 5, 0.6, align)
     assert m == rows.shape[0] and m > 64
     want = oracle.head_ce_weight_grad(inp.hidden, inp.W, rows, tgt, w.astype(np.float32), softcap)
+    assert rel_l2(host(dW), want) < DW_RTOL
+
+
+@pytest.mark.parametrize("want_dh", [True, False])
+def test_dw_with_rows_far_from_their_target(want_dh):
+    # rows whose largest logit is ~100 nats above the target's: the forward
+    # pass keeps them relative to their half-tile maxima (see the head tests)
+    inp, _ = far_row_case(43, H=192, V=2000, beta=100.0, philox_seed=3, eps=0.5,
+                          align=oracle.ALIGNED)
+    step, m, loss, row_ce, dh, dW = _run(inp, 3, 0.5, oracle.ALIGNED, 0.0, want_dh=want_dh)
+    assert host(loss)[0] == host(step.loss)[0]
+    if want_dh:
+        assert torch.equal(dh, step.d_hidden)
+    rows, tgt, w = _oracle_rows(inp, 3, 0.5, oracle.ALIGNED)
+    assert m == rows.shape[0]
+    want = oracle.head_ce_weight_grad(inp.hidden, inp.W, rows, tgt, w.astype(np.float32))
     assert rel_l2(host(dW), want) < DW_RTOL
 
 

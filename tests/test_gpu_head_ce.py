@@ -16,7 +16,7 @@ import oracle
 import workloads as WL
 from uniform_noise_diffusion_amd import binding as B
 
-from gpu_common import DEV, dev_float, d_hidden_host, host, rel_l2, run_step
+from gpu_common import DEV, dev_float, d_hidden_host, far_row_case, host, rel_l2, run_step
 
 pytestmark = pytest.mark.gpu
 
@@ -212,3 +212,24 @@ def test_one_and_two_entry_vocabularies():
     assert np.all(d_hidden_host(s) == 0.0)
     inp2 = _small(72, n_docs=3, max_len=200, H=64, V=2)
     _compare_full(inp2, seed=3, eps=0.7, align=oracle.SHIFTED, softcap=2.0)
+
+
+@pytest.mark.parametrize("beta", [50.0, 100.0])
+@pytest.mark.parametrize("align", [oracle.ALIGNED, oracle.SHIFTED])
+def test_rows_whose_target_lies_far_below_the_row_maximum(beta, align):
+    # Eight scored rows have one logit of about beta nats over a target near 0
+    # (beta = 50: far enough that the forward keeps their softmax relative to
+    # the half-tile maximum; beta = 100: the target-relative value 2^144 would
+    # not even fit in bf16).  Every other row gets logits of a few nats from
+    # those entries.  Loss, per-row CE and d_hidden against the oracle, and
+    # the other rows' d_hidden on their own.
+    inp, picks = far_row_case(41, H=256, V=3000, beta=beta, philox_seed=7, eps=0.5,
+                              align=align)
+    s, _, _ = _compare_full(inp, seed=7, eps=0.5, align=align)
+    loss, ce, dh, rows = _oracle_full(inp, dict(seed=7, eps=0.5, align=align, softcap=0.0,
+                                                noise=inp.wl.noise))
+    assert np.all(ce[picks] > beta - 10)
+    others = np.setdiff1d(np.arange(rows.shape[0]), picks)
+    g_dh = d_hidden_host(s)
+    assert rel_l2(g_dh[rows[others]], dh[rows[others]]) < DH_RTOL
+    assert rel_l2(g_dh[rows[picks]], dh[rows[picks]]) < DH_RTOL

@@ -8,31 +8,38 @@
 //
 // Pipeline for M scored rows (M lives on the device; grids are persistent and
 // read it there):
+//   0. (gradient with the preferred workspace) stash_ref_kernel: each row's
+//      reference R, its capped target logit in log2 units from a plain dot
+//      product.
 //   1. logits_kernel<fwd>: z = W h over 256 x 256 (vocab x row) tiles, K = H,
 //      on bf16 MFMA with fp32 accumulation.  Operands go from global memory
 //      straight into a two-stage LDS ring (no register staging), two waves per
-//      SIMD.  The epilogue caps, takes each row's (max m_h, sum 2^(s - m_h))
-//      over each 128-entry half of the tile and picks the target logit.
-//      Logits never leave registers.  When the gradient is wanted and the
-//      workspace holds G for the whole vocabulary, the epilogue also stashes
-//      2^(s - m_h) zhat' (zhat' = 1 - (zhat/c)^2 with a softcap c, else 1) in
-//      G as bf16: the softmax up to a per-(row, half tile) factor.
+//      SIMD.  The epilogue caps, takes each row's partial (m_h, sum 2^(s-m_h))
+//      over each 128-entry half of the tile (m_h: the half's maximum) and
+//      picks the target logit.  Logits never leave registers.  With the
+//      preferred workspace and the gradient wanted, the epilogue also stashes
+//      2^(s - rho) zhat' (zhat' = 1 - (zhat/c)^2 with a softcap c, else 1) in
+//      G as bf16, the softmax up to a known factor: rho is R unless m_h lies
+//      more than kStashSpan above it, which flags the row.
 //   2. merge_kernel: per row, combine the partials into the log-sum-exp and
 //      CE; per-block sums of w * CE in fp64.
 //   3. loss_kernel: fixed-order sum of the block sums -> loss.
 //   4. (gradient) G = w (softmax - onehot) zhat' as bf16, either from the
-//      stash (stash_scale_kernel multiplies by w 2^(m_h - lse) and rewrites
-//      the target entries) or, with a smaller workspace, per vocabulary chunk
-//      [v0, v1) by logits_kernel<grad>, which recomputes the tiles.
-//      dh_kernel forms dH = G W over 256 x 256 (row x hidden) tiles with W
-//      read through LDS transpose loads, split along the vocabulary into S
-//      slices chosen on the device so that the tile x slice units fill the
-//      grid.
+//      stash (stash_scale_kernel multiplies by w 2^(rho - lse) and rewrites
+//      the target entries, for the flagged rows only unless dW is wanted) or,
+//      with a smaller workspace, per vocabulary chunk [v0, v1) by
+//      logits_kernel<grad>, which recomputes the tiles.  dh_kernel forms
+//      dH = G W over 256 x 256 (row x hidden) tiles with W read through LDS
+//      transpose loads, split along the vocabulary into S slices chosen on
+//      the device so that the tile x slice units fill the grid; for the rows
+//      left as stash it forms sum_v q_v W_v instead.
 //   5. zero_kernel + scatter_kernel: d_hidden = 0, then d_hidden[row_idx[j]]
-//      = sum of the S slices of dH[j], in the hidden dtype.
-//   6. (trained head only) gather_rows_kernel copies the scored rows of
-//      hidden into the workspace and dw_kernel forms dW = G^T Hs over
-//      256 x 256 (vocab x hidden) tiles, K = scored rows, per vocabulary chunk.
+//      = sum of the S slices of dH[j], in the hidden dtype; for stash rows
+//      times the row factor w 2^(R - lse), plus the exact target term.
+//   6. (trained head only) the remaining stash rows become G,
+//      gather_rows_kernel copies the scored rows of hidden into the
+//      workspace and dw_kernel forms dW = G^T Hs over 256 x 256 (vocab x
+//      hidden) tiles, K = scored rows, per vocabulary chunk.
 #include "mdlm_internal.h"
 
 #include <math.h>
@@ -74,7 +81,13 @@ static_assert(2 * kLoads * kVmemEvery <= 4 * (16 / kWaves) * (64 / 16), "loads f
 #ifndef MDLM_STASH
 #define MDLM_STASH 1
 #endif
-constexpr int kMaxSplit = 8;          // K-splits of the dH product
+constexpr int kMaxSplit = 8;
+// The stash of a half tile is taken relative to the row's reference R (its
+// target logit) when the half tile's maximum m_h is at most kStashSpan above
+// R (log2 units), so entries stay below 2^64 and sums of them far below the
+// fp32 range; otherwise relative to m_h, and the row takes the per-half-tile
+// scaling pass.
+constexpr float kStashSpan = 64.f;          // K-splits of the dH product
 constexpr int kMergeRows = 4;         // rows per merge block (one per wave)
 constexpr int kGrid = 256;            // persistent grid: one workgroup per CU
 constexpr float kLog2e = 1.4426950408889634f;
@@ -203,6 +216,8 @@ struct LogitsArgs {
   const float* lse; // grad: [max_rows]
   bf16_t* G;        // grad, or fwd with the stash: [max_rows][ldg], column = v - v_begin
   int64_t ldg;
+  const float* rref;  // fwd with the stash: [max_rows] per-row reference, log2 units
+  int* row_flag;      // fwd with the stash: [max_rows] set where the reference was not used
 };
 
 // Software-pipelined MFMA block for one 64-deep K step of a wave's tile: the
@@ -259,9 +274,11 @@ __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB r
 // vocabulary rows 128 (w % 2) .. +127 and scored rows kWB (w / 2) .. +kWB-1:
 // a 4 x kNJ grid of 32 x 32 MFMA blocks.
 // kStash (forward only): the epilogue also keeps the tile's unnormalised
-// softmax, 2^(s - m_h) zhat' with m_h the row's maximum over the wave's
-// 128-entry half of the tile, as bf16 in G, so that the gradient needs no
-// second pass over the logits.
+// softmax, 2^(s - rho) zhat', as bf16 in G, so that the gradient needs no
+// second pass over the logits.  rho is the row's reference R (see
+// kStashSpan) or, far above it, the row's maximum m_h over the wave's
+// 128-entry half of the tile.  The partials are (m_h, sum 2^(s - m_h)) either
+// way, the same as without the stash.
 template <bool kGrad, bool kCap, bool kStash = false>
 __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
   static_assert(!(kGrad && kStash), "the stash is written by the forward pass");
@@ -417,6 +434,17 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
           // 64 each); -inf when all of them lie past the vocabulary
           mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
           const float mref = mx == -INFINITY ? 0.f : mx;
+          // the stash is 2^(s - rho) = 2^(s - mref) fs with rho = R when m_h
+          // is within kStashSpan of it (fs <= 2^64; it may underflow to 0
+          // where m_h is far below R, whose entries are then negligible),
+          // else rho = m_h and the row is flagged
+          float fs = 1.f;
+          if (kStash) {
+            const float R = mvalid ? a.rref[m] : 0.f;
+            const bool near = !(mx - R > kStashSpan);
+            if (!near && mvalid && lane < 32) a.row_flag[m] = 1;
+            fs = mx == -INFINITY ? 0.f : near ? __builtin_amdgcn_exp2f(mx - R) : 1.f;
+          }
           float sum = 0.f;
           bf16_t* grow = a.G + (int64_t)m * a.ldg - a.v_begin;
 #pragma unroll
@@ -430,10 +458,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
                 const float e2 = __builtin_amdgcn_exp2f(sc - mref);
                 sum += e2;
                 if (kStash) {
-                  float gv = e2;
+                  float gv = e2 * fs;
                   if (kCap) {
                     const float th = sc * kLn2 * a.inv_softcap;
-                    gv = e2 * (1.f - th * th);
+                    gv *= 1.f - th * th;
                   }
                   if (!kFull) gv = 32 * i + 8 * q + r < lim ? gv : 0.f;
                   g[r] = gv;
@@ -886,29 +914,80 @@ merge_kernel(const float2* __restrict__ partial, int n_vt, int max_rows,
   }
 }
 
+// The stash's per-row reference: the capped target logit in log2 units,
+// computed on its own (one wave per row, fp32), and a cleared fallback flag.
+// Rows whose hidden row or target lies outside its range get 0.
+__global__ void __launch_bounds__(kThreads)
+stash_ref_kernel(const bf16_t* __restrict__ hidden, const bf16_t* __restrict__ W, int H, int V,
+                 const int32_t* __restrict__ row_idx, const int32_t* __restrict__ tgt,
+                 const int32_t* __restrict__ n_rows_ptr, int max_rows, int64_t n_tokens,
+                 float softcap, float inv_softcap, float* __restrict__ rref,
+                 int* __restrict__ row_flag) {
+  const int n_rows = min(*n_rows_ptr, max_rows);
+  const int lane = threadIdx.x & 63;
+  for (int j = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); j < n_rows;
+       j += gridDim.x * (kThreads / 64)) {
+    const int64_t r = row_idx[j];
+    const int tg = tgt[j];
+    float acc = 0.f;
+    const bool ok = r >= 0 && r < n_tokens && tg >= 0 && tg < V;
+    if (ok) {
+      const bf16_t* hr = hidden + r * H;
+      const bf16_t* wr = W + (int64_t)tg * H;
+      for (int k = lane * 8; k < H; k += 512) {
+        const uint4 x = *reinterpret_cast<const uint4*>(hr + k);
+        const uint4 y = *reinterpret_cast<const uint4*>(wr + k);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc += __uint_as_float(xs[q] << 16) * __uint_as_float(ys[q] << 16);
+          acc += __uint_as_float(xs[q] & 0xFFFF0000u) * __uint_as_float(ys[q] & 0xFFFF0000u);
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) {
+      float z = acc, dc;
+      if (softcap > 0.f) z = softcap_fwd(z, softcap, inv_softcap, &dc);
+      rref[j] = ok ? z * kLog2e : 0.f;
+      row_flag[j] = 0;
+    }
+  }
+}
+
 // Turns the forward pass's stash into G: entry v of row m becomes
-// w_m 2^(m_t - lse2_m) times the stashed 2^(s - m_t) zhat' (t = v / 256, so
-// the factor is w_m p zhat'), and the target entry w_m (p - 1) zhat' from the
-// capped target logit.  One 16-byte group of eight entries per thread,
-// segments of kScaleSeg entries per block iteration.
+// w_m 2^(rho - lse2_m) times the stashed 2^(s - rho) zhat' (rho: the
+// reference the forward pass used for the half tile holding v, R_m or the
+// half's maximum, decided again here by the same test; so the factor is
+// w_m p zhat'), and the target entry w_m (p - 1) zhat' from the capped target
+// logit.  `which` selects the rows: those the forward pass flagged (1), the
+// others (0; they keep the stash until then, and their dH is finished by
+// scatter_kernel), or all (-1).  One 16-byte group of eight entries per
+// thread, segments of kScaleSeg entries per block iteration.
 constexpr int kScaleSeg = kThreads * 8;
 
 __global__ void __launch_bounds__(kThreads)
 stash_scale_kernel(bf16_t* __restrict__ G, int64_t ldg, const float2* __restrict__ partial,
                    int max_rows, const float* __restrict__ lse, const float* __restrict__ ztgt,
                    const int32_t* __restrict__ tgt, const float* __restrict__ w,
-                   const int32_t* __restrict__ n_rows_ptr, int V, float inv_softcap) {
+                   const int32_t* __restrict__ n_rows_ptr, int V, float inv_softcap,
+                   const float* __restrict__ rref, const int* __restrict__ row_flag,
+                   int which) {
   const int n_rows = min(*n_rows_ptr, max_rows);
   const int n_seg = (int)((ldg + kScaleSeg - 1) / kScaleSeg);
   const int64_t units = (int64_t)n_rows * n_seg;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
     const int m = (int)(u / n_seg);
+    if (which >= 0 && row_flag[m] != which) continue;
     const int v = (int)(u % n_seg) * kScaleSeg + (int)threadIdx.x * 8;
     if (v >= ldg) continue;
     const float lse2 = lse[m] * kLog2e;
     const float wm = w[m];
-    const float f =
-        wm * __builtin_amdgcn_exp2f(partial[(int64_t)(v / (kTile / 2)) * max_rows + m].x - lse2);
+    const float mh = partial[(int64_t)(v / (kTile / 2)) * max_rows + m].x;
+    const float R = rref[m];
+    const float rho = mh - R > kStashSpan ? mh : R;
+    const float f = wm * __builtin_amdgcn_exp2f(rho - lse2);
     uint4* gp = reinterpret_cast<uint4*>(G + (int64_t)m * ldg + v);
     const uint4 in = *gp;
     const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
@@ -967,12 +1046,33 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return (bf16_t)x; }
 
-// d_hidden[row_idx[j]] = sum over the K-slices of dH[j], for every scored row.
+// Rows whose dH slices were formed from the stash q (relative to the row's
+// reference R) rather than from G.  Off the target, G = f q with the row
+// factor f = w 2^(R - lse2); at the target t, G_t = w (p_t - 1) zhat'_t.  The
+// slices hold sum_v q_v W_v in fp32, so dH = f (sum - q_t W_t) + G_t W_t,
+// with q_t the stashed bf16 entry itself: its product with W_t is exact in
+// fp32 and is taken out before the scaling.
+struct StashFix {
+  const float* rref;
+  const int* row_flag;  // rows flagged here were finished by the scaling pass
+  const float* lse;
+  const float* ztgt;
+  const float* w;
+  const int32_t* tgt;
+  const bf16_t* G;
+  int64_t ldg;
+  const bf16_t* W;
+  int V;
+  float inv_softcap;
+};
+
+// d_hidden[row_idx[j]] = sum over the K-slices of dH[j] (with the stash
+// correction for rows that need it), for every scored row.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
 scatter_kernel(const float* __restrict__ part, int H, int grid, int v_span,
                const int32_t* __restrict__ row_idx, const int32_t* __restrict__ n_rows_ptr,
-               int max_rows, int64_t n_tokens, T* __restrict__ d_hidden) {
+               int max_rows, int64_t n_tokens, T* __restrict__ d_hidden, StashFix fx) {
   const int n_rows = min(*n_rows_ptr, max_rows);
   const int64_t tiles = (int64_t)((n_rows + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
   const int S = dh_splits(tiles, grid, (v_span + kBK - 1) / kBK);
@@ -980,10 +1080,36 @@ scatter_kernel(const float* __restrict__ part, int H, int grid, int v_span,
   for (int j = blockIdx.x; j < n_rows; j += gridDim.x) {
     const int64_t r = row_idx[j];
     if (r < 0 || r >= n_tokens) continue;
+    float f = 1.f, qt = 0.f, gt = 0.f;
+    const bf16_t* wt = nullptr;
+    if (fx.rref && fx.row_flag[j] == 0) {
+      const float lse2 = fx.lse[j] * kLog2e;
+      const float wm = fx.w[j];
+      f = wm * __builtin_amdgcn_exp2f(fx.rref[j] - lse2);
+      const int tg = fx.tgt[j];
+      if (tg >= 0 && tg < fx.V) {
+        const float zt2 = fx.ztgt[j];
+        float dc = 1.f;
+        if (fx.inv_softcap > 0.f) {
+          const float th = zt2 * kLn2 * fx.inv_softcap;
+          dc = 1.f - th * th;
+        }
+        qt = (float)fx.G[(int64_t)j * fx.ldg + tg];
+        gt = wm * (__builtin_amdgcn_exp2f(zt2 - lse2) - 1.f) * dc;
+        wt = fx.W + (int64_t)tg * H;
+      }
+    }
     for (int h = threadIdx.x; h < H; h += kThreads) {
       float acc = 0.f;
       for (int k = 0; k < S; ++k) acc += part[k * slice + (int64_t)j * H + h];
-      d_hidden[r * H + h] = from_f32<T>(acc);
+      float d;
+      if (wt) {
+        const float wv = (float)wt[h];
+        d = f * fmaf(-qt, wv, acc) + gt * wv;
+      } else {
+        d = f * acc;
+      }
+      d_hidden[r * H + h] = from_f32<T>(d);
     }
   }
 }
@@ -1075,7 +1201,7 @@ f32_dh_kernel(F32Args a, float* __restrict__ d_hidden) {
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t partial, ztgt, lse, bsum, Hs, part, G, total;
+  size_t partial, ztgt, lse, bsum, rref, flag, Hs, part, G, total;
   int n_vt, n_bsum;
 };
 
@@ -1090,6 +1216,8 @@ Layout fixed_layout(int64_t max_rows, int H, int V, int dtype, bool grad, bool d
   L.ztgt = off;    off = align_up(off + (size_t)max_rows * sizeof(float));
   L.lse = off;     off = align_up(off + (size_t)max_rows * sizeof(float));
   L.bsum = off;    off = align_up(off + (size_t)std::max(L.n_bsum, 1) * sizeof(double));
+  L.rref = off;    off = align_up(off + (size_t)max_rows * sizeof(float));
+  L.flag = off;    off = align_up(off + (size_t)max_rows * sizeof(int));
   L.Hs = off;
   if (dw) off = align_up(off + (size_t)max_rows * H * sizeof(bf16_t));
   L.part = L.G = off;
@@ -1176,6 +1304,8 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   }
   const bool stash = MDLM_STASH && grad && x.dtype == MDLM_BF16 && vc >= x.V;
   bf16_t* G = reinterpret_cast<bf16_t*>(ws + L.G);
+  float* rref = reinterpret_cast<float*>(ws + L.rref);
+  int* row_flag = reinterpret_cast<int*>(ws + L.flag);
 
   if (x.dtype == MDLM_BF16) {
     LogitsArgs la{};
@@ -1197,7 +1327,12 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     la.ztgt = ztgt;
     la.G = G;
     la.ldg = vc;
+    la.rref = rref;
+    la.row_flag = row_flag;
     if (stash) {
+      stash_ref_kernel<<<(unsigned)std::min<int64_t>((max_rows + 3) / 4, 16384), kThreads, 0,
+                         stream>>>(la.hidden, la.W, x.H, x.V, x.row_idx, x.tgt, x.n_rows,
+                                   (int)max_rows, x.n_tokens, x.softcap, inv_cap, rref, row_flag);
       if (x.softcap > 0.f)
         logits_kernel<false, true, true><<<grid, kGemmThreads, 0, stream>>>(la);
       else
@@ -1257,12 +1392,17 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   }
 
   float* part = reinterpret_cast<float*>(ws + L.part);
-  if (stash) {
+  // With the stash: the rows the forward pass flagged become G here; the
+  // others keep the stash through the dH product (scatter_kernel finishes
+  // their dH) and become G only before a dW product, which needs G itself.
+  auto scale_rows = [&](int which) {
     const int n_seg = (int)((vc + kScaleSeg - 1) / kScaleSeg);
     const unsigned sgrid = (unsigned)std::min<int64_t>(max_rows * n_seg, (int64_t)cus * 32);
     stash_scale_kernel<<<sgrid, kThreads, 0, stream>>>(G, vc, partial, (int)max_rows, lse, ztgt,
-                                                       x.tgt, x.w, x.n_rows, x.V, inv_cap);
-  }
+                                                       x.tgt, x.w, x.n_rows, x.V, inv_cap,
+                                                       rref, row_flag, which);
+  };
+  if (stash) scale_rows(want_dh ? 1 : -1);
 
   LogitsArgs la{};
   la.W = reinterpret_cast<const bf16_t*>(x.W);
@@ -1305,14 +1445,52 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   da.max_rows = (int)max_rows;
   da.part = part;
 
+  // every chunk uses the same slice count (it depends on the chunk width only
+  // through the number of K steps, which is at least kMaxSplit unless the
+  // chunk is narrower than 512)
+  auto scatter = [&](const StashFix& fix) {
+    scatter_kernel<bf16_t><<<(unsigned)std::min<int64_t>(max_rows, 65536), kThreads, 0,
+                             stream>>>(part, x.H, grid, (int)std::min<int64_t>(vc, x.V),
+                                       x.row_idx, x.n_rows, (int)max_rows, x.n_tokens,
+                                       reinterpret_cast<bf16_t*>(x.d_hidden), fix);
+  };
+
+  if (stash) {
+    // one chunk: G (or the stash) spans the vocabulary
+    if (want_dh) {
+      da.v_begin = 0;
+      da.v_end = x.V;
+      da.accumulate = 0;
+      dh_kernel<<<grid, kGemmThreads, 0, stream>>>(da);
+      StashFix fix{};
+      fix.rref = rref;
+      fix.row_flag = row_flag;
+      fix.lse = lse;
+      fix.ztgt = ztgt;
+      fix.w = x.w;
+      fix.tgt = x.tgt;
+      fix.G = G;
+      fix.ldg = vc;
+      fix.W = la.W;
+      fix.V = x.V;
+      fix.inv_softcap = inv_cap;
+      scatter(fix);  // (reads the stashed target entries: before they are scaled)
+    }
+    if (want_dw) {
+      if (want_dh) scale_rows(0);
+      wa.v_begin = 0;
+      wa.v_end = x.V;
+      dw_kernel<<<grid, kGemmThreads, 0, stream>>>(wa);
+    }
+    return hipGetLastError();
+  }
+
   int chunk = 0;
   for (int64_t v0 = 0; v0 < x.V; v0 += vc, ++chunk) {
     const int v1 = (int)std::min<int64_t>(x.V, v0 + vc);
     la.v_begin = (int)v0;
     la.v_end = v1;
-    if (stash)
-      ;  // G is already in place
-    else if (x.softcap > 0.f)
+    if (x.softcap > 0.f)
       logits_kernel<true, true><<<grid, kGemmThreads, 0, stream>>>(la);
     else
       logits_kernel<true, false><<<grid, kGemmThreads, 0, stream>>>(la);
@@ -1328,13 +1506,7 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
       dw_kernel<<<grid, kGemmThreads, 0, stream>>>(wa);
     }
   }
-  if (!want_dh) return hipGetLastError();
-  // every chunk uses the same slice count (it depends on the chunk width only
-  // through the number of K steps, which is at least kMaxSplit unless the
-  // chunk is narrower than 512)
-  scatter_kernel<bf16_t><<<(unsigned)std::min<int64_t>(max_rows, 65536), kThreads, 0, stream>>>(
-      part, x.H, grid, (int)std::min<int64_t>(vc, x.V), x.row_idx, x.n_rows, (int)max_rows,
-      x.n_tokens, reinterpret_cast<bf16_t*>(x.d_hidden));
+  if (want_dh) scatter(StashFix{});
   return hipGetLastError();
 }
 
