@@ -70,6 +70,11 @@ constexpr int kTile = 256;            // rows of each operand tile
 constexpr int kBK = 64;               // K elements per main-loop step
 constexpr int kKRow = kBK * 2;        // bytes per row of a K-major tile (128)
 constexpr int kNRow = kTile * 2;      // bytes per row of an N-major tile (512)
+// The 32-row blocks of the tile's scored rows are dealt to the waves in turn:
+// block j of a wave sits kRowStride rows after its block j-1, so that the
+// blocks holding the first n rows of a partial tile fall evenly on the two
+// waves of each SIMD pair.
+constexpr int kRowStride = 32 * (kWaves / 2);
 constexpr int kOpBytes = kTile * kKRow;       // one operand tile: 32 KiB
 constexpr int kStageBytes = 2 * kOpBytes;     // A + B: 64 KiB
 constexpr int kLdsBytes = 2 * kStageBytes;    // two stages: 128 KiB
@@ -142,6 +147,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   const int64_t capped = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)capped,
                                            0x00020000);
+}
+
+// Calls f(integral_constant<int, min(n, N)>) for a wave-uniform n >= 0, so
+// that a loop can be specialised on how many of a wave's blocks are in use.
+template <int N, typename F>
+__device__ __forceinline__ void with_count(int n, F&& f) {
+  if constexpr (N == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (n >= N)
+      f(std::integral_constant<int, N>{});
+    else
+      with_count<N - 1>(n, f);
+  }
 }
 
 // Compile-time count of prefetch loads interleaved with a step's MFMAs.
@@ -227,7 +246,9 @@ struct LogitsArgs {
 // prefetch) are spread over the first MFMAs of the step, one before every
 // kVmemEvery-th MFMA, rather than left to the scheduler, which would sink
 // them to the end of the step (leaving them no time to land).
-template <int kReads, int kVmem, typename ReadA, typename ReadB>
+// Only the first NI A blocks and NJ B blocks take part (the rest lie past the
+// scored rows); the readers' unused fragments are dead and dropped.
+template <int kReads, int kVmem, int NI = 4, int NJ = kNJ, typename ReadA, typename ReadB>
 __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB rb) {
   bf16x8 af[2][4], bfr[2][kNJ];
   ra(0, af[0]);
@@ -240,16 +261,16 @@ __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB r
       rb(kk + 1, bfr[cur ^ 1]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < kNJ; ++j)
+      for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
                                                             0, 0, 0);
   }
   // Issue order for the scheduler: the first slice's reads, then each slice's
   // MFMAs alternated one for one with the next slice's reads (transpose reads
   // count twice in `kReads`), with the loads interleaved as above.
-  constexpr int kMfma = 4 * kNJ;
+  constexpr int kMfma = NI * NJ;
   constexpr int kSlices = kBK / 16;
   __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
 #pragma unroll
@@ -271,8 +292,9 @@ __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB r
 
 // Tile of 256 vocabulary rows (operand A, rows of W) by 256 scored rows
 // (operand B, rows of hidden gathered through row_idx), K = H.  Wave w owns
-// vocabulary rows 128 (w % 2) .. +127 and scored rows kWB (w / 2) .. +kWB-1:
-// a 4 x kNJ grid of 32 x 32 MFMA blocks.
+// vocabulary rows 128 (w % 2) .. +127 and the scored-row blocks
+// 32 (w / 2) + kRowStride j .. +31, j < kNJ: a 4 x kNJ grid of 32 x 32 MFMA
+// blocks, of which only those holding scored rows are computed.
 // kStash (forward only): the epilogue also keeps the tile's unnormalised
 // softmax, 2^(s - rho) zhat', as bf16 in G, so that the gradient needs no
 // second pass over the logits.  rho is the row's reference R (see
@@ -299,7 +321,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
   // fragment-read offsets (bytes within a stage)
   const int fx = swz_k(lane & 15), khalf = lane >> 5;
   const int a_off = (wa * 128 + (lane & 31)) * kKRow;
-  const int b_off = kOpBytes + (wb * kWB + (lane & 31)) * kKRow;
+  const int b_off = kOpBytes + (32 * wb + (lane & 31)) * kKRow;
   // direct-load roles: load q (0..kLoads-1) of this wave fills tile rows
   // 8 (kLoads wave + q) .. +7; lane l supplies row 8 (kLoads wave + q) + l / 8
   // at physical chunk l % 8
@@ -351,55 +373,65 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
         buf2l(rb, sa + kOpBytes + q * 1024, b_voff[q], (uint32_t)(k0 * 2));
       }
     };
-    auto compute = [&](const char* base, auto vmem) {
-      mma_k64<4 + kNJ, decltype(vmem)::value>(
-          acc,
-          [&](int kk, bf16x8(&f)[4]) {
-            const int coff = ((2 * kk + khalf) ^ fx) * 16;
+    // this wave's blocks that hold scored rows (a prefix of its kNJ)
+    const int nv = min(kTile, n_rows - m0);
+    const int kj = max(0, (nv - 32 * wb + kRowStride - 1) / kRowStride);
+    // the K loop, specialised on that count (the waves of a workgroup run
+    // the same loads and barriers whatever their count)
+    auto kloop = [&](auto nj_tag) __attribute__((always_inline)) {
+      constexpr int NJ = decltype(nj_tag)::value;
+      auto compute = [&](const char* base, auto vmem) __attribute__((always_inline)) {
+        if constexpr (NJ > 0)
+          mma_k64<4 + NJ, decltype(vmem)::value, 4, NJ>(
+              acc,
+              [&](int kk, bf16x8(&f)[4]) {
+                const int coff = ((2 * kk + khalf) ^ fx) * 16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
-          },
-          [&](int kk, bf16x8(&f)[kNJ]) {
-            const int coff = ((2 * kk + khalf) ^ fx) * 16;
+                for (int i = 0; i < 4; ++i)
+                  f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
+              },
+              [&](int kk, bf16x8(&f)[kNJ]) {
+                const int coff = ((2 * kk + khalf) ^ fx) * 16;
 #pragma unroll
-            for (int j = 0; j < kNJ; ++j)
-              f[j] = *reinterpret_cast<const bf16x8*>(base + b_off + j * 32 * kKRow + coff);
-          });
+                for (int j = 0; j < NJ; ++j)
+                  f[j] = *reinterpret_cast<const bf16x8*>(base + b_off + j * kRowStride * kKRow +
+                                                          coff);
+              });
+      };
+      __syncthreads();  // the previous tile is done with both stages
+      issue(smem0, 0);
+      // two K steps per trip so that each access names its stage statically;
+      // an odd last step runs after the loop.  The prefetch into smem0 is
+      // unconditional so that it shares a basic block (and so a scheduling
+      // region) with the MFMAs it is interleaved with: on the last trip of an
+      // even KT it reads past K (in-range bytes or zeros), is never consumed,
+      // and the wait after the loop retires it before the stage is reused.
+      int kt = 0;
+      for (; kt + 2 <= KT; kt += 2) {
+        wait_vmem();
+        __syncthreads();
+        issue(smem1, (kt + 1) * kBK);
+        compute(smem0, kInterleave);
+        sched_fence();
+        wait_vmem();
+        __syncthreads();
+        issue(smem0, (kt + 2) * kBK);
+        compute(smem1, kInterleave);
+        sched_fence();
+      }
+      if (kt < KT) {
+        wait_vmem();
+        __syncthreads();
+        compute(smem0, kNoLoads);
+      }
+      wait_vmem();
     };
-
-    __syncthreads();  // the previous tile is done with both stages
-    issue(smem0, 0);
-    // two K steps per trip so that each access names its stage statically;
-    // an odd last step runs after the loop.  The prefetch into smem0 is
-    // unconditional so that it shares a basic block (and so a scheduling
-    // region) with the MFMAs it is interleaved with: on the last trip of an
-    // even KT it reads past K (in-range bytes or zeros), is never consumed,
-    // and the wait after the loop retires it before the stage is reused.
-    int kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-      wait_vmem();
-      __syncthreads();
-      issue(smem1, (kt + 1) * kBK);
-      compute(smem0, kInterleave);
-      sched_fence();
-      wait_vmem();
-      __syncthreads();
-      issue(smem0, (kt + 2) * kBK);
-      compute(smem1, kInterleave);
-      sched_fence();
-    }
-    if (kt < KT) {
-      wait_vmem();
-      __syncthreads();
-      compute(smem0, kNoLoads);
-    }
-    wait_vmem();
+    with_count<kNJ>(kj, kloop);
 
     // ---- epilogue ---------------------------------------------------------
     // Accumulator element e of block (i, j) on lane l holds vocabulary entry
     // vl + 32i + 8(e/4) + e%4, vl = v0 + wa*128 + 4(l/32), for row
-    // m0 + wb*kWB + 32j + l%32.  A row's target sits in this lane's registers
+    // m0 + 32 wb + kRowStride j + l%32.  A row's target sits in this lane's registers
     // iff its offset dt from vl lies in [0, 128) with bit 2 clear.  Only the
     // tile that straddles v_end masks entries past the vocabulary.
     const int vl = v0 + wa * 128 + 4 * (lane >> 5);
@@ -408,7 +440,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
       constexpr bool kFull = decltype(full_tag)::value;
 #pragma unroll
       for (int j = 0; j < kNJ; ++j) {
-        const int m = m0 + wb * kWB + 32 * j + (lane & 31);
+        if (j >= kj) break;  // (no scored row in this block or the next)
+        const int m = m0 + 32 * wb + kRowStride * j + (lane & 31);
         const bool mvalid = m < n_rows;
         const int tg = mvalid ? a.tgt[m] : -1;
         const int dt = tg - vl;
@@ -555,7 +588,9 @@ __host__ __device__ __forceinline__ int dh_splits(int64_t tiles, int grid, int k
 
 // Tile of 256 scored rows (operand A, rows of G) by 256 hidden columns
 // (operand B, columns of W read through transpose loads), K = vocabulary.
-// Wave w owns rows 128 (w % 2) .. +127 and columns kWB (w / 2) .. +kWB-1.
+// Wave w owns the row blocks 32 (w % 2) + 64 i .. +31, i < 4 (dealt in turn,
+// so that a partial tile's rows fall evenly on both SIMD pairs; only blocks
+// holding scored rows are computed) and columns kWB (w / 2) .. +kWB-1.
 __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
   __shared__ __attribute__((aligned(1024))) char smem0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) char smem1[kStageBytes];
@@ -571,7 +606,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
   const int S = dh_splits(T, gridDim.x, KI);
 
   const int fx = swz_k(lane & 15), khalf = lane >> 5;
-  const int a_off = (wa * 128 + (lane & 31)) * kKRow;
+  const int a_off = (32 * wa + (lane & 31)) * kKRow;
   // transpose-read roles: group g = lane / 16 covers K rows 8 (g / 2) .. +7 of
   // a 16-deep slice and columns 16 (g % 2) .. +15 of a 32-column block
   const int jl = lane & 15, grp = lane >> 4;
@@ -627,61 +662,70 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
               (uint32_t)((2 * (kLoads * wave + q) + k0) * a.H * 2));
       }
     };
-    auto compute = [&](const char* base, auto vmem) {
-      const char* bb = base + kOpBytes;
-      mma_k64<4 + 2 * kNJ, decltype(vmem)::value>(
-          acc,
-          [&](int kk, bf16x8(&f)[4]) {
-            const int coff = ((2 * kk + khalf) ^ fx) * 16;
+    // this wave's row blocks that hold scored rows (a prefix of its four)
+    const int nv = min(kTile, n_rows - m0);
+    const int ki = max(0, (nv - 32 * wa + 63) / 64);
+    auto kloop = [&](auto ni_tag) __attribute__((always_inline)) {
+      constexpr int NI = decltype(ni_tag)::value;
+      auto compute = [&](const char* base, auto vmem) __attribute__((always_inline)) {
+        const char* bb = base + kOpBytes;
+        if constexpr (NI > 0)
+          mma_k64<NI + 2 * kNJ, decltype(vmem)::value, NI, kNJ>(
+              acc,
+              [&](int kk, bf16x8(&f)[4]) {
+                const int coff = ((2 * kk + khalf) ^ fx) * 16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
-          },
-          [&](int kk, bf16x8(&f)[kNJ]) {
-            const char* brow_p = bb + (16 * kk + tr_row) * kNRow;
+                for (int i = 0; i < NI; ++i)
+                  f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 64 * kKRow + coff);
+              },
+              [&](int kk, bf16x8(&f)[kNJ]) {
+                const char* brow_p = bb + (16 * kk + tr_row) * kNRow;
 #pragma unroll
-            for (int j = 0; j < kNJ; ++j) {
-              const shortx4 lo = ds_read_tr(brow_p + b_col_off[j]);
-              const shortx4 hi = ds_read_tr(brow_p + 4 * kNRow + b_col_off[j]);
-              const short v8 __attribute__((__vector_size__(16))) = {
-                  lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              f[j] = __builtin_bit_cast(bf16x8, v8);
-            }
-          });
+                for (int j = 0; j < kNJ; ++j) {
+                  const shortx4 lo = ds_read_tr(brow_p + b_col_off[j]);
+                  const shortx4 hi = ds_read_tr(brow_p + 4 * kNRow + b_col_off[j]);
+                  const short v8 __attribute__((__vector_size__(16))) = {
+                      lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                  f[j] = __builtin_bit_cast(bf16x8, v8);
+                }
+              });
+      };
+
+      __syncthreads();
+      issue(smem0, kb * kBK);
+      // same pipeline as the logits tiles (unconditional last prefetch,
+      // retired by the wait after the loop)
+      int kt = kb;
+      for (; kt + 2 <= ke; kt += 2) {
+        wait_vmem();
+        __syncthreads();
+        issue(smem1, (kt + 1) * kBK);
+        compute(smem0, kInterleave);
+        sched_fence();
+        wait_vmem();
+        __syncthreads();
+        issue(smem0, (kt + 2) * kBK);
+        compute(smem1, kInterleave);
+        sched_fence();
+      }
+      if (kt < ke) {
+        wait_vmem();
+        __syncthreads();
+        compute(smem0, kNoLoads);
+      }
+      wait_vmem();
     };
+    with_count<4>(ki, kloop);
 
-    __syncthreads();
-    issue(smem0, kb * kBK);
-    // same pipeline as the logits tiles (unconditional last prefetch, retired
-    // by the wait after the loop)
-    int kt = kb;
-    for (; kt + 2 <= ke; kt += 2) {
-      wait_vmem();
-      __syncthreads();
-      issue(smem1, (kt + 1) * kBK);
-      compute(smem0, kInterleave);
-      sched_fence();
-      wait_vmem();
-      __syncthreads();
-      issue(smem0, (kt + 2) * kBK);
-      compute(smem1, kInterleave);
-      sched_fence();
-    }
-    if (kt < ke) {
-      wait_vmem();
-      __syncthreads();
-      compute(smem0, kNoLoads);
-    }
-    wait_vmem();
-
-    // acc element e of block (i, j) on lane l: row m0 + wa*128 + 32i + 8(e/4)
+    // acc element e of block (i, j) on lane l: row m0 + 32 wa + 64 i + 8(e/4)
     // + 4(l/32) + e%4, column h0 + wb*kWB + 32j + l%32.
     float* out = a.part + (int64_t)s * a.max_rows * a.H;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      if (i >= ki) break;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wa * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int m = m0 + 32 * wa + 64 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (m >= n_rows) continue;
 #pragma unroll
         for (int j = 0; j < kNJ; ++j) {
@@ -692,6 +736,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
           }
         }
       }
+    }
   }
 }
 
