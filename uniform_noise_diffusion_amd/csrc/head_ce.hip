@@ -1008,8 +1008,8 @@ stash_ref_kernel(const bf16_t* __restrict__ hidden, const bf16_t* __restrict__ W
 // w_m p zhat'), and the target entry w_m (p - 1) zhat' from the capped target
 // logit.  `which` selects the rows: those the forward pass flagged (1), the
 // others (0; they keep the stash until then, and their dH is finished by
-// scatter_kernel), or all (-1).  One 16-byte group of eight entries per
-// thread, segments of kScaleSeg entries per block iteration.
+// scatter_kernel), or all (-1).  One block per row at a time (so that rows
+// left out cost one flag read), 16-byte groups of eight entries per thread.
 constexpr int kScaleSeg = kThreads * 8;
 
 __global__ void __launch_bounds__(kThreads)
@@ -1020,42 +1020,54 @@ stash_scale_kernel(bf16_t* __restrict__ G, int64_t ldg, const float2* __restrict
                    const float* __restrict__ rref, const int* __restrict__ row_flag,
                    int which) {
   const int n_rows = min(*n_rows_ptr, max_rows);
-  const int n_seg = (int)((ldg + kScaleSeg - 1) / kScaleSeg);
-  const int64_t units = (int64_t)n_rows * n_seg;
-  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
-    const int m = (int)(u / n_seg);
+  for (int m = blockIdx.x; m < n_rows; m += gridDim.x) {
     if (which >= 0 && row_flag[m] != which) continue;
-    const int v = (int)(u % n_seg) * kScaleSeg + (int)threadIdx.x * 8;
-    if (v >= ldg) continue;
     const float lse2 = lse[m] * kLog2e;
     const float wm = w[m];
-    const float mh = partial[(int64_t)(v / (kTile / 2)) * max_rows + m].x;
     const float R = rref[m];
-    const float rho = mh - R > kStashSpan ? mh : R;
-    const float f = wm * __builtin_amdgcn_exp2f(rho - lse2);
-    uint4* gp = reinterpret_cast<uint4*>(G + (int64_t)m * ldg + v);
-    const uint4 in = *gp;
-    const uint32_t wd[4] = {in.x, in.y, in.z, in.w};
-    float x[8];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[2 * k] = __uint_as_float(wd[k] << 16) * f;
-      x[2 * k + 1] = __uint_as_float(wd[k] & 0xFFFF0000u) * f;
-    }
-    const int dt = tgt[m] - v;
-    if ((unsigned)dt < 8u && v + dt < V) {
+    const int tg = tgt[m];
+    float gt = 0.f;  // the target entry
+    if (tg >= 0 && tg < V) {
       const float zt2 = ztgt[m];
       float dc = 1.f;
       if (inv_softcap > 0.f) {
         const float th = zt2 * kLn2 * inv_softcap;
         dc = 1.f - th * th;
       }
-      const float gt = (__builtin_amdgcn_exp2f(zt2 - lse2) - 1.f) * dc * wm;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = dt == e ? gt : x[e];
+      gt = (__builtin_amdgcn_exp2f(zt2 - lse2) - 1.f) * dc * wm;
     }
-    *gp = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                     pack_bf16x2(x[6], x[7]));
+    uint4* grow = reinterpret_cast<uint4*>(G + (int64_t)m * ldg);
+    // four 16-byte groups in flight per thread
+    for (int v0 = (int)threadIdx.x * 8; v0 < ldg; v0 += 4 * kScaleSeg) {
+      uint4 in[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int v = v0 + b * kScaleSeg;
+        if (v < ldg) in[b] = grow[v / 8];
+      }
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int v = v0 + b * kScaleSeg;
+        if (v >= ldg) break;
+        const float mh = partial[(int64_t)(v / (kTile / 2)) * max_rows + m].x;
+        const float rho = mh - R > kStashSpan ? mh : R;
+        const float f = wm * __builtin_amdgcn_exp2f(rho - lse2);
+        const uint32_t wd[4] = {in[b].x, in[b].y, in[b].z, in[b].w};
+        float x[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          x[2 * k] = __uint_as_float(wd[k] << 16) * f;
+          x[2 * k + 1] = __uint_as_float(wd[k] & 0xFFFF0000u) * f;
+        }
+        const int dt = tg - v;
+        if ((unsigned)dt < 8u && tg < V) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = dt == e ? gt : x[e];
+        }
+        grow[v / 8] = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                 pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7]));
+      }
+    }
   }
 }
 
@@ -1144,17 +1156,32 @@ scatter_kernel(const float* __restrict__ part, int H, int grid, int v_span,
         wt = fx.W + (int64_t)tg * H;
       }
     }
-    for (int h = threadIdx.x; h < H; h += kThreads) {
-      float acc = 0.f;
-      for (int k = 0; k < S; ++k) acc += part[k * slice + (int64_t)j * H + h];
-      float d;
-      if (wt) {
-        const float wv = (float)wt[h];
-        d = f * fmaf(-qt, wv, acc) + gt * wv;
-      } else {
-        d = f * acc;
+    // four consecutive columns per thread (H is a multiple of 64)
+    for (int h = 4 * (int)threadIdx.x; h < H; h += 4 * kThreads) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < S; ++k) {
+        const float4 p = *reinterpret_cast<const float4*>(part + k * slice + (int64_t)j * H + h);
+        acc.x += p.x;
+        acc.y += p.y;
+        acc.z += p.z;
+        acc.w += p.w;
       }
-      d_hidden[r * H + h] = from_f32<T>(d);
+      float d[4] = {f * acc.x, f * acc.y, f * acc.z, f * acc.w};
+      if (wt) {
+        const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
+        const uint2 wb = *reinterpret_cast<const uint2*>(wt + h);
+        const float wv[4] = {__uint_as_float(wb.x << 16), __uint_as_float(wb.x & 0xFFFF0000u),
+                             __uint_as_float(wb.y << 16), __uint_as_float(wb.y & 0xFFFF0000u)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = f * fmaf(-qt, wv[e], a4[e]) + gt * wv[e];
+      }
+      if constexpr (std::is_same<T, bf16_t>::value) {
+        *reinterpret_cast<uint2*>(d_hidden + r * H + h) =
+            make_uint2(pack_bf16x2(d[0], d[1]), pack_bf16x2(d[2], d[3]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d_hidden[r * H + h + e] = from_f32<T>(d[e]);
+      }
     }
   }
 }
@@ -1441,8 +1468,7 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   // others keep the stash through the dH product (scatter_kernel finishes
   // their dH) and become G only before a dW product, which needs G itself.
   auto scale_rows = [&](int which) {
-    const int n_seg = (int)((vc + kScaleSeg - 1) / kScaleSeg);
-    const unsigned sgrid = (unsigned)std::min<int64_t>(max_rows * n_seg, (int64_t)cus * 32);
+    const unsigned sgrid = (unsigned)std::min<int64_t>(max_rows, (int64_t)cus * 8);
     stash_scale_kernel<<<sgrid, kThreads, 0, stream>>>(G, vc, partial, (int)max_rows, lse, ztgt,
                                                        x.tgt, x.w, x.n_rows, x.V, inv_cap,
                                                        rref, row_flag, which);
