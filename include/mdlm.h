@@ -231,9 +231,12 @@ int mdlm_compact_rows(const uint8_t* corrupted, const uint8_t* eligible,
 /*
  * Workspace bytes that mdlm_fused_head_ce_fwd_bwd needs for up to max_rows
  * scored rows of hidden size H against a vocabulary of V.  This is the size
- * the library prefers; a larger workspace is accepted (and lets the backward
- * use fewer, larger vocabulary chunks), a smaller one than
- * mdlm_head_ce_workspace_min_bytes is rejected.  Returns 0 for invalid sizes.
+ * the library prefers: with bf16 it holds a bf16 value per scored row and
+ * vocabulary entry, so the forward pass keeps the softmax there and the
+ * gradient needs no second pass over the logits.  Any size down to
+ * mdlm_head_ce_workspace_min_bytes is accepted (the gradient then recomputes
+ * the logits in vocabulary chunks that fit); a smaller one is rejected.
+ * Returns 0 for invalid sizes.
  */
 size_t mdlm_head_ce_workspace_bytes(int64_t max_rows, int32_t H, int32_t V,
                                     int32_t dtype);
@@ -259,8 +262,11 @@ size_t mdlm_head_ce_workspace_min_bytes(int64_t max_rows, int32_t H, int32_t V,
  * d_hidden is set to exactly zero.  The upstream gradient is taken as 1.
  * row_idx entries must be distinct (as mdlm_compact_masked produces).
  *
- * BF16: inputs bf16, products accumulated in fp32, the per-logit gradient
- * rounded to bf16 before the second product, d_hidden written as bf16.
+ * BF16: inputs bf16, products accumulated in fp32, d_hidden written as bf16.
+ * The second product takes its per-logit factor rounded to bf16: with the
+ * preferred workspace, the softmax relative to the row's target logit
+ * (times zhat'), the row's scale and the target's term then applied in fp32;
+ * with a smaller workspace, the gradient w (softmax - onehot) zhat' itself.
  * F32: everything in fp32.
  *
  *   hidden      [n_tokens, H] row-major, element type `dtype`.
