@@ -66,12 +66,16 @@ def d_hidden_host(step):
     return host(step.d_hidden.float())
 
 
-def far_row_case(seed, H, V, beta, philox_seed, eps, align, n_far=8, softcap=0.0):
+def far_row_case(seed, H, V, beta, philox_seed, eps, align, n_far=8, softcap=0.0,
+                 push_target=False):
     """A small bf16 case in which n_far of the scored rows (of the oracle's
     own corruption with `philox_seed`, `eps`, `align`) get one vocabulary
     entry whose logit is about `beta` nats while their target's logit stays
     near zero: W row v_k = beta h_r / |h_r|^2 for the row's hidden vector h_r.
-    Returns (inputs, indices of those rows in the scored-row list)."""
+    With `push_target`, the target's row of W is set to -beta h_r / |h_r|^2
+    too (about -beta nats), so that with a softcap c the two capped logits
+    sit near +c and -c.  Returns (inputs, indices of those rows in the
+    scored-row list)."""
     import dataclasses
 
     import oracle
@@ -91,5 +95,7 @@ def far_row_case(seed, H, V, beta, philox_seed, eps, align, n_far=8, softcap=0.0
     for k, j in enumerate(picks):
         h = inp.hidden[rows[j]].astype(np.float64)
         W[free[k]] = (beta * h / np.dot(h, h)).astype(np.float32)
+        if push_target:
+            W[tgt[j]] = (-beta * h / np.dot(h, h)).astype(np.float32)
     Wr, Wb = WL._round_bf16(W)
     return dataclasses.replace(inp, W=Wr, W_bits=Wb), picks

@@ -67,6 +67,7 @@ def _check(x0, cu, seed, eps, noise, mask_id, rand_vocab, align):
     (2, 40, 300, True),      # empty documents, several compaction tiles
     (3, 7, 3000, False),     # documents spanning block boundaries
     (4, 600, 20, True),      # many short documents per block
+    (5, 5000, 2, True),      # more documents per 4096-token block than it caches
 ])
 def test_corrupt_compact_bit_exact_small(noise, align, seed, n_docs, max_len, empty):
     x0, cu = _case(seed, n_docs, max_len, empty)

@@ -233,3 +233,18 @@ def test_rows_whose_target_lies_far_below_the_row_maximum(beta, align):
     g_dh = d_hidden_host(s)
     assert rel_l2(g_dh[rows[others]], dh[rows[others]]) < DH_RTOL
     assert rel_l2(g_dh[rows[picks]], dh[rows[picks]]) < DH_RTOL
+
+
+def test_far_rows_under_a_softcap():
+    # with softcap 30 the picked rows' largest capped logit is near +30 and
+    # their target's near -30: 60 nats apart, beyond the stash's span again
+    inp, picks = far_row_case(45, H=256, V=3000, beta=100.0, philox_seed=9, eps=0.5,
+                              align=oracle.SHIFTED, softcap=30.0, push_target=True)
+    params = dict(seed=9, eps=0.5, align=oracle.SHIFTED, softcap=30.0, noise=inp.wl.noise)
+    s, _, _ = _compare_full(inp, seed=9, eps=0.5, align=oracle.SHIFTED, softcap=30.0)
+    loss, ce, dh, rows = _oracle_full(inp, params)
+    assert np.all(ce[picks] > 55)
+    g_dh = d_hidden_host(s)
+    others = np.setdiff1d(np.arange(rows.shape[0]), picks)
+    assert rel_l2(g_dh[rows[others]], dh[rows[others]]) < DH_RTOL
+    assert rel_l2(g_dh[rows[picks]], dh[rows[picks]]) < DH_RTOL
