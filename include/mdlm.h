@@ -284,8 +284,8 @@ size_t mdlm_head_ce_workspace_min_bytes(int64_t max_rows, int32_t H, int32_t V,
  *   softcap     0 = none, else > 0 and finite.
  *   loss        [1] float out.
  *   row_ce      [max_rows] float out, CE_j, or NULL.
- *   d_hidden    [n_tokens, H] out, element type `dtype`, or NULL for a
- *               forward-only call.
+ *   d_hidden    [n_tokens, H] out, element type `dtype`, 16-byte aligned,
+ *               or NULL for a forward-only call.
  *   workspace   device memory, 256-byte aligned, of workspace_bytes >=
  *               mdlm_head_ce_workspace_min_bytes(max_rows, H, V, dtype).
  * Returns MDLM_OK, MDLM_EINVAL, MDLM_EUNSUPPORTED, MDLM_EWORKSPACE or
@@ -317,11 +317,12 @@ size_t mdlm_head_ce_dw_workspace_min_bytes(int64_t max_rows, int32_t H, int32_t 
  * table (the frozen-head case, where no such gradient is formed).
  *
  *   dW[v] = sum_j w[j] * (softmax(zhat_j)[v] - [v == tgt[j]]) * zhat'_jv * h_j
- * (the same per-logit factor as d_hidden, rounded to bf16, times the bf16
- * hidden rows; products accumulated in fp32).
+ * (the per-logit gradient rounded to bf16, times the bf16 hidden rows;
+ * products accumulated in fp32).
  *
  *   hidden, W   bf16 only (the element type is implied).
- *   d_hidden    [n_tokens, H] bf16 out, or NULL (only dW is wanted).
+ *   d_hidden    [n_tokens, H] bf16 out, 16-byte aligned, or NULL (only dW
+ *               is wanted).
  *   dW          [V, H] float out, 16-byte aligned; overwritten (zero when no
  *               row is scored).
  *   workspace   >= mdlm_head_ce_dw_workspace_min_bytes(max_rows, H, V).

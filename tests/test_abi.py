@@ -171,6 +171,9 @@ def test_head_rejects_missing_or_small_workspace(lib):
     kw2 = dict(kw, hidden=odd)
     assert head_call(lib, **kw2) == B.MDLM_EINVAL
     assert "16-byte aligned" in B.mdlm_last_error()
+    kw3 = dict(kw, d_hidden=ctypes.c_void_p((1 << 20) + 8))
+    assert head_call(lib, **kw3) == B.MDLM_EINVAL
+    assert "d_hidden must be 16-byte aligned" in B.mdlm_last_error()
 
 
 def test_compact_rejects_small_workspace(lib):

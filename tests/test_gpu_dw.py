@@ -1,12 +1,13 @@
 """GPU parity of the head-weight gradient (mdlm_fused_head_ce_fwd_bwd_dw).
 
 Small and multi-tile cases compare dW with the oracle's fp64 gradient (1e-2
-relative L2, the d_hidden bar: both products use the same bf16-rounded
-per-logit factor).  The call's loss, row CE and d_hidden must be bit-identical
-to those of mdlm_fused_head_ce_fwd_bwd.  At full size, where the fp64 oracle
-would need trillions of operations, two identities that hold at any size are
-checked: <dW, W> = <d_hidden, hidden> (both equal sum_jv G_jv z_jv) and, with
-no softcap, sum_v dW_v = 0 (each row's softmax minus one-hot sums to zero).
+relative L2, the d_hidden bar; both products take bf16-rounded per-logit
+factors).  The call's loss, row CE and d_hidden must be bit-identical to those
+of mdlm_fused_head_ce_fwd_bwd.  At full size, where the fp64 oracle would need
+trillions of operations, two identities that hold at any size are checked, to
+within the bf16 rounding of those factors: <dW, W> = <d_hidden, hidden> (both
+equal sum_jv G_jv z_jv) and, with no softcap, sum_v dW_v = 0 (each row's
+softmax minus one-hot sums to zero).
 """
 
 import numpy as np

@@ -192,6 +192,8 @@ static int head_common(const char* fn, const void* hidden, const void* W, int32_
     return fail(MDLM_EINVAL, "%s: hidden and W must be 16-byte aligned", fn);
   if (dW && (reinterpret_cast<uintptr_t>(dW) % 16) != 0)
     return fail(MDLM_EINVAL, "%s: dW must be 16-byte aligned", fn);
+  if (d_hidden && (reinterpret_cast<uintptr_t>(d_hidden) % 16) != 0)
+    return fail(MDLM_EINVAL, "%s: d_hidden must be 16-byte aligned", fn);
   const size_t need =
       max_rows > 0 ? head_ce_workspace_bytes(max_rows, H, V, dtype, true, dW != nullptr) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need))
