@@ -86,13 +86,13 @@ static_assert(2 * kLoads * kVmemEvery <= 4 * (16 / kWaves) * (64 / 16), "loads f
 #ifndef MDLM_STASH
 #define MDLM_STASH 1
 #endif
-constexpr int kMaxSplit = 8;
+constexpr int kMaxSplit = 8;          // K-splits of the dH product
 // The stash of a half tile is taken relative to the row's reference R (its
 // target logit) when the half tile's maximum m_h is at most kStashSpan above
 // R (log2 units), so entries stay below 2^64 and sums of them far below the
 // fp32 range; otherwise relative to m_h, and the row takes the per-half-tile
 // scaling pass.
-constexpr float kStashSpan = 64.f;          // K-splits of the dH product
+constexpr float kStashSpan = 64.f;
 constexpr int kMergeRows = 4;         // rows per merge block (one per wave)
 constexpr int kGrid = 256;            // persistent grid: one workgroup per CU
 constexpr float kLog2e = 1.4426950408889634f;
