@@ -247,8 +247,9 @@ def _timed(fn, reps):
 def variants(inp, dev, n_bw, reps=5):
     """The loss variants on the same workload: the encoder AR term (every-token
     causal rows of mdlm_compact_rows, then the fused head on them), the
-    head-weight gradient call, and mdlm_compact_rows' other modes at the
-    bandwidth size."""
+    head-weight gradient call, the fused call with a backward that recomputes
+    the logits (a workspace just short of the preferred size), and
+    mdlm_compact_rows' other modes at the bandwidth size."""
     import torch
     from uniform_noise_diffusion_amd import binding as B
     from uniform_noise_diffusion_amd.pipeline import MdlmLossStep
@@ -275,7 +276,12 @@ def variants(inp, dev, n_bw, reps=5):
                      dtype=torch.uint8, device=dev)
     dW = torch.empty((wl.V, wl.H), dtype=torch.float32, device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
-    t_dw, t_plain, rows = [], [], []
+    # the same call with a workspace one 256-column chunk short of G over the
+    # whole vocabulary: the backward then recomputes the logits (in two
+    # vocabulary chunks) instead of using the forward pass's stash
+    ws_rc = torch.empty(B.mdlm_head_ce_workspace_bytes(wl.n_tokens, wl.H, wl.V, B.MDLM_BF16)
+                        - wl.n_tokens * 256 * 2, dtype=torch.uint8, device=dev)
+    t_dw, t_plain, t_rc, rows = [], [], [], []
     for seed in range(reps):
         step.corrupt(x0, cu, seed, wl.eps, wl.noise, wl.mask_id, wl.rand_vocab)
         step.compact(x0, cu, wl.align)
@@ -284,7 +290,19 @@ def variants(inp, dev, n_bw, reps=5):
             h, W, step.row_idx, step.tgt, step.w, step.n_rows, wl.n_tokens, wl.softcap, loss,
             None, step.d_hidden, dW, ws), 2))
         t_plain.append(_timed(lambda: step.head_ce(h, W, wl.softcap, row_ce=False), 2))
+        t_rc.append(_timed(lambda: B.mdlm_fused_head_ce_fwd_bwd(
+            h, W, step.row_idx, step.tgt, step.w, step.n_rows, wl.n_tokens, wl.softcap, loss,
+            None, step.d_hidden, ws_rc), 2))
     rows = np.array(rows, dtype=np.float64)
+    out["head_recompute_backward"] = dict(
+        seeds=f"0..{reps - 1}", mean_rows=float(rows.mean()),
+        ms_per_call=float(np.mean(t_rc)) * 1e3,
+        ms_per_call_with_stash=float(np.mean(t_plain)) * 1e3,
+        algorithmic_tflops=float((4 * rows * HV).sum() / np.sum(t_rc) / 1e12),
+        executed_tflops=float((6 * rows * HV).sum() / np.sum(t_rc) / 1e12),
+        what="mdlm_fused_head_ce_fwd_bwd with a workspace one 256-column chunk short of "
+             "the preferred size: the backward recomputes the logit tiles (6 M H V "
+             "executed) instead of using the forward pass's stash")
     out["head_weight_gradient"] = dict(
         seeds=f"0..{reps - 1}", mean_rows=float(rows.mean()),
         ms_per_call=float(np.mean(t_dw)) * 1e3,
@@ -293,7 +311,7 @@ def variants(inp, dev, n_bw, reps=5):
         dw_gemm_tflops=float((2 * rows * HV).sum() / (np.sum(t_dw) - np.sum(t_plain)) / 1e12),
         what="mdlm_fused_head_ce_fwd_bwd_dw (loss, d_hidden and dW fp32 [V, H]); the dW "
              "product's rate is 2 M H V over the time the call adds")
-    del step, ws, dW
+    del step, ws, dW, ws_rc
     if n_bw:
         L = 4096
         n = n_bw // L * L
