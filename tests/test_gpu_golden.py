@@ -1,0 +1,45 @@
+"""The library against the oracle's stored outputs on two tiny seeded cases
+(tests/golden/oracle_tiny.json, written from the oracle alone): corruption
+and row lists bit for bit, loss and per-row CE within 1e-3 relative, the
+gradient's per-row norms within 1e-2 relative L2."""
+
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+from gpu_common import d_hidden_host, host, rel_l2, run_step
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, os.path.join(HERE, "golden"))
+
+import make_golden  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+with open(os.path.join(HERE, "golden", "oracle_tiny.json")) as f:
+    STORED = json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("name", sorted(STORED))
+def test_library_matches_stored_oracle_outputs(name):
+    want = STORED[name]
+    inp = make_golden.inputs(make_golden.CASES[name])
+    s = run_step(inp, seed=want["seed"], eps=want["eps"], align=want["align"],
+                 softcap=want["softcap"], noise=want["noise"])
+    m = int(host(s.n_rows)[0])
+    assert m == len(want["row_idx"])
+    assert host(s.xt).tolist() == want["xt"]
+    assert np.flatnonzero(host(s.corrupted)).tolist() == want["corrupted"]
+    assert [f"{v:016x}" for v in host(s.p_doc).view(np.uint64)] == want["p_doc_bits"]
+    assert host(s.doc_counts).tolist() == want["doc_counts"]
+    assert host(s.row_idx)[:m].tolist() == want["row_idx"]
+    assert host(s.tgt)[:m].tolist() == want["tgt"]
+    assert [f"{v:08x}" for v in host(s.w)[:m].view(np.uint32)] == want["w_bits"]
+    assert abs(float(host(s.loss)[0]) - want["loss"]) <= 1e-3 * abs(want["loss"])
+    np.testing.assert_allclose(host(s.row_ce)[:m], want["row_ce"], rtol=1e-3)
+    rows = np.array(want["row_idx"])
+    norms = np.linalg.norm(d_hidden_host(s)[rows].astype(np.float64), axis=1)
+    assert rel_l2(norms, want["d_hidden_row_norms"]) < 1e-2
