@@ -20,6 +20,13 @@ Sources for what is computed:
     (documents stay isolated; padding is excluded from loss) and
     "Adapters, merging and inference" (full-vocabulary CE from hidden states
     through a plain linear output head, aligned targets).
+  * LLaDA-8B-MDLM-LoRA model card, "Training" table, "Objective" row: the
+    corrective mixture's option names (mixture_prob, noise_token_wt,
+    clean_token_wt), all 0 for the MDLM objective.  No formula is given:
+    ``corrupt_mixture`` and ``compact_corrective`` take a stated reading and
+    are pinned only through their reductions (mixture 0 = absorbing noise,
+    mixture 1 = the uniform-noise ids, zero weights = the MDLM row list) and
+    the mixture's frequency; beyond those, parity unpinned.
 """
 
 from .philox import philox4x32_10  # noqa: F401
@@ -32,6 +39,11 @@ from .mdlm import (  # noqa: F401
     corrupt,
     compact,
     compact_rows,
+    corrupt_mixture,
+    compact_corrective,
+    CODE_CLEAN,
+    CODE_MASKED,
+    CODE_REPLACED,
     WEIGHT_INV_P,
     WEIGHT_MEAN,
     WEIGHT_EXAMPLE_MEAN_CLIPPED,

@@ -28,6 +28,12 @@ SHIFTED = 1
 TAG_DOC_T = 0      # per-document noise level t
 TAG_BERNOULLI = 1  # per-token keep/corrupt decision
 TAG_REPLACE = 2    # per-token replacement id under uniform noise
+TAG_MIX = 3        # per-token choice between mask and replacement (mixture)
+
+# Codes of the corrective mixture's corruption mask.
+CODE_CLEAN = 0
+CODE_MASKED = 1
+CODE_REPLACED = 2
 
 _TWO24 = float(1 << 24)
 
@@ -158,6 +164,100 @@ def compact(corrupted, x0, cu_seqlens, p_doc, align):
                 rows.append(g)
             tgts.append(x0[g])
             ws.append(1.0 / (p_doc[b] * float(n)))
+    return (np.asarray(rows, dtype=np.int64), np.asarray(tgts, dtype=np.int64),
+            np.asarray(ws, dtype=np.float64))
+
+
+def corrupt_mixture(x0, cu_seqlens, seed, eps, mixture_prob, mask_id, rand_vocab):
+    """Corruption of the corrective mixture: absorbing corruption in which a
+    share of the corrupted tokens takes a uniform-random id instead of the
+    mask token.
+
+    [LLaDA] Training table, Objective row: the MDLM arm sets mixture_prob,
+    noise_token_wt and clean_token_wt to 0 and is then "absorbing corruption
+    only"; the corrective arm (paragraph before the table) differs from it in
+    mixture_prob and noise_token_wt.  The pages give no formula.  Reading
+    taken (parity unpinned beyond the reductions below): a token is
+    corrupted exactly as under absorbing noise (same noise level, same
+    Bernoulli words); a corrupted token is replaced by a uniform-random id
+    (the uniform-noise draw of ``corrupt``) with probability mixture_prob,
+    decided by (word3(g) >> 8) < ceil(mixture_prob * 2^24) with word3 from
+    stream TAG_MIX, and masked otherwise.  mixture_prob = 0 is absorbing
+    corruption; mixture_prob = 1 replaces every corrupted token with the id
+    uniform noise would give it.
+
+    Returns (xt int32[N], codes uint8[N] (CODE_CLEAN / CODE_MASKED /
+    CODE_REPLACED), p_doc float64[B], doc_counts int32[B] (corrupted tokens
+    of either kind)).
+    """
+    x0 = np.asarray(x0, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    n = x0.shape[0]
+    n_docs = cu.shape[0] - 1
+    assert cu[0] == 0 and cu[-1] == n
+    assert 0.0 <= mixture_prob <= 1.0
+    _, p, thr = noise_levels(seed, eps, n_docs)
+    thr_mix = int(np.ceil(float(mixture_prob) * _TWO24))
+    w1 = token_words(seed, n, TAG_BERNOULLI).astype(np.int64)
+    w2 = token_words(seed, n, TAG_REPLACE).astype(np.uint64)
+    w3 = token_words(seed, n, TAG_MIX).astype(np.int64)
+    xt = x0.copy()
+    codes = np.zeros(n, dtype=np.uint8)
+    doc_counts = np.zeros(n_docs, dtype=np.int32)
+    for b in range(n_docs):
+        for g in range(cu[b], cu[b + 1]):
+            if (w1[g] >> 8) >= thr[b]:
+                continue
+            doc_counts[b] += 1
+            if (w3[g] >> 8) < thr_mix:
+                codes[g] = CODE_REPLACED
+                xt[g] = int((int(w2[g]) * int(rand_vocab)) >> 32)
+            else:
+                codes[g] = CODE_MASKED
+                xt[g] = mask_id
+    return xt.astype(np.int32), codes, p, doc_counts
+
+
+def compact_corrective(codes, x0, cu_seqlens, p_doc, align, noise_token_wt, clean_token_wt):
+    """Scored rows of the corrective mixture's loss, in ascending token order.
+
+    [LLaDA] Training table, Objective row: the option names noise_token_wt
+    and clean_token_wt; with both 0 the loss is the MDLM one (cross-entropy
+    on masked tokens divided by the mask probability).  Reading taken
+    (parity unpinned beyond the reductions): every position predicts its
+    clean token; a masked token keeps the weight 1 / (p_b N), a replaced
+    token gets noise_token_wt / (p_b N) and, when clean_token_wt is not 0,
+    every uncorrupted token gets clean_token_wt / N.  Rows are the corrupted
+    tokens of either kind (a replaced token is listed even at weight 0) and,
+    when clean_token_wt is not 0, every other token; alignment as in
+    ``compact``.  Weights in fp64, stored by the library as fp32.
+
+    Returns (row_idx int64[M], tgt int64[M], w float64[M]).
+    """
+    codes = np.asarray(codes, dtype=np.int64)
+    x0 = np.asarray(x0, dtype=np.int64)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    p_doc = np.asarray(p_doc, dtype=np.float64)
+    n = x0.shape[0]
+    rows, tgts, ws = [], [], []
+    for b in range(cu.shape[0] - 1):
+        for g in range(cu[b], cu[b + 1]):
+            c = codes[g]
+            if c == CODE_CLEAN and clean_token_wt == 0.0:
+                continue
+            if align == SHIFTED:
+                if g == cu[b]:
+                    continue
+                rows.append(g - 1)
+            else:
+                rows.append(g)
+            tgts.append(x0[g])
+            if c == CODE_MASKED:
+                ws.append(1.0 / (p_doc[b] * float(n)))
+            elif c == CODE_REPLACED:
+                ws.append(float(noise_token_wt) / (p_doc[b] * float(n)))
+            else:
+                ws.append(float(clean_token_wt) / float(n))
     return (np.asarray(rows, dtype=np.int64), np.asarray(tgts, dtype=np.int64),
             np.asarray(ws, dtype=np.float64))
 
