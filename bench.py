@@ -249,7 +249,8 @@ def variants(inp, dev, n_bw, reps=5):
     causal rows of mdlm_compact_rows, then the fused head on them), the
     head-weight gradient call, the fused call with a backward that recomputes
     the logits (a workspace just short of the preferred size), and
-    mdlm_compact_rows' other modes at the bandwidth size."""
+    mdlm_compact_rows' other modes and the corrective mixture at the bandwidth
+    size."""
     import torch
     from uniform_noise_diffusion_amd import binding as B
     from uniform_noise_diffusion_amd.pipeline import MdlmLossStep
@@ -333,6 +334,24 @@ def variants(inp, dev, n_bw, reps=5):
         res["what"] = (f"mdlm_compact_rows at {n} tokens in documents of 4,096 (shifted); "
                        "algorithmic bytes: the mask (1 B per token, if any) + 16 B per row")
         out["compact_rows_hbm"] = res
+        # the corrective mixture: corruption with a replaced share, then its row list
+        mix = {}
+        seeds = iter(range(1000, 2000))
+        t = _timed(lambda: s2.corrupt_mixture(x2, cu2, next(seeds), 1e-3, 0.25, 126336,
+                                              126464), reps)
+        mix["corrupt_mixture"] = dict(us=t * 1e6, algorithmic_GBs=9.0 * n / t / 1e9,
+                                      frac=9.0 * n / t / 1e9 / PEAK_HBM_GBS)
+        for name, c in (("compact_corrective", 0.0), ("compact_corrective_clean", 0.1)):
+            t = _timed(lambda: s2.compact_corrective(x2, cu2, 0, 0.5, c), reps)
+            mm = int(s2.n_rows.item())
+            alg = n + 16.0 * mm
+            mix[name] = dict(us=t * 1e6, rows=mm, algorithmic_GBs=alg / t / 1e9,
+                             frac=alg / t / 1e9 / PEAK_HBM_GBS)
+        mix["what"] = (f"mdlm_corrupt_mixture (mixture_prob 0.25) and mdlm_compact_corrective "
+                       f"(noise_token_wt 0.5, clean_token_wt 0 and 0.1) at {n} tokens in "
+                       "documents of 4,096 (aligned); algorithmic bytes: corruption 9 B per "
+                       "token, compaction the codes (1 B per token) + 16 B per row")
+        out["corrective_mixture_hbm"] = mix
     return out
 
 

@@ -123,6 +123,39 @@ int mdlm_corrupt(const int32_t* x0, int64_t n_tokens,
                  int32_t* xt, uint8_t* corrupted, double* p_doc,
                  int32_t* doc_counts, void* stream);
 
+/* Codes written by mdlm_corrupt_mixture into `corrupted`. */
+enum { MDLM_CODE_CLEAN = 0, MDLM_CODE_MASKED = 1, MDLM_CODE_REPLACED = 2 };
+
+/*
+ * mdlm_corrupt_mixture -- corruption of the corrective mixture: absorbing
+ * corruption in which a share of the corrupted tokens takes a uniform-random
+ * id instead of the mask token.
+ *
+ * Defined by: LLaDA-8B-MDLM-LoRA card, Training table, "Objective" row,
+ * which names the corrective options (mixture_prob, noise_token_wt,
+ * clean_token_wt; all 0 for the MDLM objective) without a formula.  The
+ * reading implemented: each token is corrupted exactly as by mdlm_corrupt
+ * with MDLM_NOISE_ABSORB (same p_b, same Bernoulli words); a corrupted token
+ * g is replaced iff (word3 >> 8) < ceil(mixture_prob * 2^24), with word3 =
+ * word (g & 3) at counter (lo32(g >> 2), hi32(g >> 2), 0, 3), and then takes
+ * the id mdlm_corrupt's UNIFORM mode would give it; otherwise it becomes
+ * mask_id.  mixture_prob = 0 gives mdlm_corrupt's ABSORB output exactly;
+ * mixture_prob = 1 gives its UNIFORM tokens (codes 2 in place of 1).
+ *
+ *   mixture_prob  in [0, 1], the share of corrupted tokens replaced.
+ *   corrupted     [n_tokens] uint8 out: MDLM_CODE_CLEAN, MDLM_CODE_MASKED or
+ *                 MDLM_CODE_REPLACED.
+ *   doc_counts    [n_docs] int32 out, corrupted tokens of either kind.
+ *   rand_vocab    >= 1; replacement ids lie in [0, rand_vocab).
+ *   other arguments as for mdlm_corrupt.
+ * Returns MDLM_OK, MDLM_EINVAL or MDLM_EHIP.
+ */
+int mdlm_corrupt_mixture(const int32_t* x0, int64_t n_tokens, const int32_t* cu_seqlens,
+                         int32_t n_docs, uint64_t seed, double eps, double mixture_prob,
+                         int32_t mask_id, int32_t rand_vocab, int32_t* xt,
+                         uint8_t* corrupted, double* p_doc, int32_t* doc_counts,
+                         void* stream);
+
 /* Row weightings of mdlm_compact_rows. */
 enum {
   MDLM_WEIGHT_INV_P = 0,                 /* scale / (p_doc[b] * n_tokens)        */
@@ -227,6 +260,37 @@ int mdlm_compact_rows(const uint8_t* corrupted, const uint8_t* eligible,
                       int32_t* row_idx, int32_t* tgt, float* w,
                       int32_t* n_rows, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * mdlm_compact_corrective -- the scored-row list of the corrective mixture,
+ * from the codes mdlm_corrupt_mixture writes.
+ *
+ * Defined by: LLaDA-8B-MDLM-LoRA card, Training table, "Objective" row
+ * (noise_token_wt and clean_token_wt, both 0 for the MDLM objective, named
+ * without a formula).  The reading implemented: every listed position
+ * predicts its clean token; a masked token (code 1) of document b has the
+ * weight 1 / (p_doc[b] * n_tokens) of mdlm_compact_masked, a replaced token
+ * (code 2) noise_token_wt / (p_doc[b] * n_tokens), and any other token
+ * clean_token_wt / n_tokens, each evaluated in fp64 and rounded once to
+ * fp32.  Listed are the tokens with a nonzero code and, when clean_token_wt
+ * is not 0, every token; rows, targets, alignment and order as for
+ * mdlm_compact_masked.  With both weights 0 the rows are those of
+ * mdlm_compact_masked over (codes != 0), replaced tokens at weight 0.
+ *
+ *   codes       [n_tokens] uint8, as written by mdlm_corrupt_mixture.
+ *   noise_token_wt, clean_token_wt   finite.
+ *   workspace   >= mdlm_compact_workspace_bytes(n_tokens) bytes of device
+ *               memory, 4-byte aligned; contents on entry are ignored.
+ *   other arguments as for mdlm_compact_masked.
+ * Returns MDLM_OK, MDLM_EINVAL, MDLM_EWORKSPACE or MDLM_EHIP.
+ */
+int mdlm_compact_corrective(const uint8_t* codes, const int32_t* x0,
+                            int64_t n_tokens, const int32_t* cu_seqlens,
+                            int32_t n_docs, const double* p_doc, int32_t align,
+                            double noise_token_wt, double clean_token_wt,
+                            int32_t* row_idx, int32_t* tgt, float* w,
+                            int32_t* n_rows, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * Workspace bytes that mdlm_fused_head_ce_fwd_bwd needs for up to max_rows

@@ -189,6 +189,71 @@ def test_compact_rejects_small_workspace(lib):
     assert "workspace" in B.mdlm_last_error()
 
 
+def mixture_call(lib, **kw):
+    a = dict(x0=NULL, n=16, cu=NULL, n_docs=1, seed=0, eps=1e-3, mix=0.5, mask_id=1,
+             rand_vocab=2, xt=NULL, codes=NULL, p_doc=NULL, counts=NULL, stream=NULL)
+    a.update(kw)
+    return lib.mdlm_corrupt_mixture(a["x0"], a["n"], a["cu"], a["n_docs"], a["seed"],
+                                    a["eps"], a["mix"], a["mask_id"], a["rand_vocab"],
+                                    a["xt"], a["codes"], a["p_doc"], a["counts"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(n=-1), B.MDLM_EINVAL, "n_tokens < 0"),
+    (dict(n=1 << 31), B.MDLM_EUNSUPPORTED, "below 2^31"),
+    (dict(n_docs=0), B.MDLM_EINVAL, "n_docs = 0"),
+    (dict(eps=0.0), B.MDLM_EINVAL, "eps"),
+    (dict(mix=-0.1), B.MDLM_EINVAL, "mixture_prob"),
+    (dict(mix=1.5), B.MDLM_EINVAL, "mixture_prob"),
+    (dict(mix=float("nan")), B.MDLM_EINVAL, "mixture_prob"),
+    (dict(rand_vocab=0), B.MDLM_EINVAL, "rand_vocab"),
+    (dict(), B.MDLM_EINVAL, "null token pointer"),
+])
+def test_corrupt_mixture_rejects_bad_arguments(lib, kw, code, msg):
+    assert mixture_call(lib, **kw) == code
+    assert msg in B.mdlm_last_error()
+
+
+def corrective_call(lib, **kw):
+    a = dict(codes=NULL, x0=NULL, n=16, cu=NULL, n_docs=1, p_doc=NULL, align=0, a=0.5, c=0.0,
+             row_idx=NULL, tgt=NULL, w=NULL, n_rows=NULL, ws=NULL, ws_bytes=0, stream=NULL)
+    a.update(kw)
+    return lib.mdlm_compact_corrective(a["codes"], a["x0"], a["n"], a["cu"], a["n_docs"],
+                                       a["p_doc"], a["align"], a["a"], a["c"], a["row_idx"],
+                                       a["tgt"], a["w"], a["n_rows"], a["ws"], a["ws_bytes"],
+                                       a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(n=-1), B.MDLM_EINVAL, "n_tokens < 0"),
+    (dict(n=1 << 31), B.MDLM_EUNSUPPORTED, "below 2^31"),
+    (dict(n_docs=0), B.MDLM_EINVAL, "n_docs"),
+    (dict(align=2), B.MDLM_EINVAL, "alignment"),
+    (dict(a=float("nan")), B.MDLM_EINVAL, "finite"),
+    (dict(c=float("inf")), B.MDLM_EINVAL, "finite"),
+    (dict(), B.MDLM_EINVAL, "null n_rows"),
+])
+def test_compact_corrective_rejects_bad_arguments(lib, kw, code, msg):
+    assert corrective_call(lib, **kw) == code
+    assert msg in B.mdlm_last_error()
+
+
+def test_compact_corrective_pointer_and_workspace_checks(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    n = 1 << 20
+    kw = dict(x0=fake, cu=fake, row_idx=fake, tgt=fake, w=fake, n_rows=fake, n=n)
+    assert corrective_call(lib, p_doc=fake, **kw) == B.MDLM_EINVAL   # no codes
+    assert "null pointer" in B.mdlm_last_error()
+    assert corrective_call(lib, codes=fake, **kw) == B.MDLM_EINVAL   # no p_doc
+    need = B.mdlm_compact_workspace_bytes(n)
+    assert corrective_call(lib, codes=fake, p_doc=fake, ws=fake, ws_bytes=need - 1,
+                           **kw) == B.MDLM_EWORKSPACE
+    odd = ctypes.c_void_p((1 << 20) + 2)
+    assert corrective_call(lib, codes=fake, p_doc=fake, ws=odd, ws_bytes=need,
+                           **kw) == B.MDLM_EINVAL
+    assert "4-byte aligned" in B.mdlm_last_error()
+
+
 def rows_call(lib, **kw):
     a = dict(corrupted=NULL, eligible=NULL, x0=NULL, n=16, cu=NULL, n_docs=1, p_doc=NULL,
              align=0, weighting=1, scale=1.0, clip=10.0, row_idx=NULL, tgt=NULL, w=NULL,

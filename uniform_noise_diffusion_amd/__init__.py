@@ -10,8 +10,9 @@ from .binding import (  # noqa: F401
     MdlmError,
     MDLM_OK, MDLM_EINVAL, MDLM_EUNSUPPORTED, MDLM_EWORKSPACE, MDLM_EHIP,
     MDLM_NOISE_ABSORB, MDLM_NOISE_UNIFORM, MDLM_ALIGNED, MDLM_SHIFTED,
-    MDLM_F32, MDLM_BF16,
-    mdlm_corrupt, mdlm_compact_workspace_bytes, mdlm_compact_masked,
+    MDLM_F32, MDLM_BF16, MDLM_CODE_CLEAN, MDLM_CODE_MASKED, MDLM_CODE_REPLACED,
+    mdlm_corrupt, mdlm_corrupt_mixture, mdlm_compact_workspace_bytes, mdlm_compact_masked,
+    mdlm_compact_corrective,
     mdlm_head_ce_workspace_bytes, mdlm_head_ce_workspace_min_bytes,
     mdlm_fused_head_ce_fwd_bwd, mdlm_last_error, mdlm_version,
 )

@@ -29,11 +29,16 @@ MDLM_BF16 = 1
 MDLM_WEIGHT_INV_P = 0
 MDLM_WEIGHT_MEAN = 1
 MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED = 2
+MDLM_CODE_CLEAN = 0
+MDLM_CODE_MASKED = 1
+MDLM_CODE_REPLACED = 2
 
 EXPORTED = (
     "mdlm_corrupt",
+    "mdlm_corrupt_mixture",
     "mdlm_compact_workspace_bytes",
     "mdlm_compact_masked",
+    "mdlm_compact_corrective",
     "mdlm_compact_rows_workspace_bytes",
     "mdlm_compact_rows",
     "mdlm_head_ce_workspace_bytes",
@@ -70,10 +75,16 @@ def load():
                                        ctypes.c_size_t)
     lib.mdlm_corrupt.argtypes = [vp, i64, vp, i32, u64, f64, i32, i32, i32, vp, vp, vp, vp, vp]
     lib.mdlm_corrupt.restype = ctypes.c_int
+    lib.mdlm_corrupt_mixture.argtypes = [vp, i64, vp, i32, u64, f64, f64, i32, i32, vp, vp, vp,
+                                         vp, vp]
+    lib.mdlm_corrupt_mixture.restype = ctypes.c_int
     lib.mdlm_compact_workspace_bytes.argtypes = [i64]
     lib.mdlm_compact_workspace_bytes.restype = sz
     lib.mdlm_compact_masked.argtypes = [vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.mdlm_compact_masked.restype = ctypes.c_int
+    lib.mdlm_compact_corrective.argtypes = [vp, vp, i64, vp, i32, vp, i32, f64, f64, vp, vp, vp,
+                                            vp, vp, sz, vp]
+    lib.mdlm_compact_corrective.restype = ctypes.c_int
     lib.mdlm_compact_rows_workspace_bytes.argtypes = [i64, i32, i32]
     lib.mdlm_compact_rows_workspace_bytes.restype = sz
     lib.mdlm_compact_rows.argtypes = [vp, vp, vp, i64, vp, i32, vp, i32, i32, f64, f64, vp, vp,
@@ -151,6 +162,23 @@ def mdlm_corrupt(x0, cu_seqlens, seed, eps, noise, mask_id, rand_vocab, xt, corr
                                _ptr(p_doc), _ptr(doc_counts), _stream(stream)))
 
 
+def mdlm_corrupt_mixture(x0, cu_seqlens, seed, eps, mixture_prob, mask_id, rand_vocab, xt,
+                         codes, p_doc, doc_counts, stream=None):
+    """See mdlm_corrupt_mixture in include/mdlm.h."""
+    _need(x0, torch.int32, "x0")
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    _need(xt, torch.int32, "xt")
+    _need(codes, torch.uint8, "codes")
+    _need(p_doc, torch.float64, "p_doc")
+    _need(doc_counts, torch.int32, "doc_counts")
+    n_docs = cu_seqlens.numel() - 1
+    _check(load().mdlm_corrupt_mixture(_ptr(x0), x0.numel(), _ptr(cu_seqlens), n_docs,
+                                       int(seed) & 0xFFFFFFFFFFFFFFFF, float(eps),
+                                       float(mixture_prob), int(mask_id), int(rand_vocab),
+                                       _ptr(xt), _ptr(codes), _ptr(p_doc), _ptr(doc_counts),
+                                       _stream(stream)))
+
+
 def mdlm_compact_workspace_bytes(n_tokens):
     return load().mdlm_compact_workspace_bytes(int(n_tokens))
 
@@ -172,6 +200,26 @@ def mdlm_compact_masked(corrupted, x0, cu_seqlens, p_doc, align, row_idx, tgt, w
                                       cu_seqlens.numel() - 1, _ptr(p_doc), int(align),
                                       _ptr(row_idx), _ptr(tgt), _ptr(w), _ptr(n_rows),
                                       _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mdlm_compact_corrective(codes, x0, cu_seqlens, p_doc, align, noise_token_wt,
+                            clean_token_wt, row_idx, tgt, w, n_rows, workspace, stream=None):
+    """See mdlm_compact_corrective in include/mdlm.h.  `workspace` is a uint8
+    tensor of mdlm_compact_workspace_bytes(n_tokens) bytes."""
+    _need(codes, torch.uint8, "codes")
+    _need(x0, torch.int32, "x0")
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    _need(p_doc, torch.float64, "p_doc")
+    _need(row_idx, torch.int32, "row_idx")
+    _need(tgt, torch.int32, "tgt")
+    _need(w, torch.float32, "w")
+    _need(n_rows, torch.int32, "n_rows")
+    _need(workspace, torch.uint8, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(load().mdlm_compact_corrective(
+        _ptr(codes), _ptr(x0), x0.numel(), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
+        _ptr(p_doc), int(align), float(noise_token_wt), float(clean_token_wt), _ptr(row_idx),
+        _ptr(tgt), _ptr(w), _ptr(n_rows), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def mdlm_compact_rows_workspace_bytes(n_tokens, n_docs, weighting):

@@ -64,6 +64,32 @@ int mdlm_corrupt(const int32_t* x0, int64_t n_tokens, const int32_t* cu_seqlens,
   return MDLM_OK;
 }
 
+int mdlm_corrupt_mixture(const int32_t* x0, int64_t n_tokens, const int32_t* cu_seqlens,
+                         int32_t n_docs, uint64_t seed, double eps, double mixture_prob,
+                         int32_t mask_id, int32_t rand_vocab, int32_t* xt,
+                         uint8_t* corrupted, double* p_doc, int32_t* doc_counts,
+                         void* stream) {
+  clear_error();
+  const char* fn = "mdlm_corrupt_mixture";
+  if (n_tokens < 0) return fail(MDLM_EINVAL, "%s: n_tokens < 0", fn);
+  if (n_tokens > INT32_MAX) return fail(MDLM_EUNSUPPORTED, "%s: n_tokens must be below 2^31", fn);
+  if (n_docs < 0) return fail(MDLM_EINVAL, "%s: n_docs < 0", fn);
+  if (n_docs == 0 && n_tokens > 0) return fail(MDLM_EINVAL, "%s: tokens given but n_docs = 0", fn);
+  if (!(eps > 0.0 && eps <= 1.0)) return fail(MDLM_EINVAL, "%s: eps must lie in (0, 1]", fn);
+  if (!(mixture_prob >= 0.0 && mixture_prob <= 1.0))
+    return fail(MDLM_EINVAL, "%s: mixture_prob must lie in [0, 1]", fn);
+  if (rand_vocab < 1) return fail(MDLM_EINVAL, "%s: rand_vocab must be >= 1", fn);
+  if (n_tokens > 0 && (!x0 || !xt || !corrupted))
+    return fail(MDLM_EINVAL, "%s: null token pointer", fn);
+  if (n_docs > 0 && (!cu_seqlens || !p_doc || !doc_counts))
+    return fail(MDLM_EINVAL, "%s: null document pointer", fn);
+  if (launch_corrupt(x0, n_tokens, cu_seqlens, n_docs, seed, eps, kNoiseMixture, mask_id,
+                     rand_vocab, xt, corrupted, p_doc, doc_counts,
+                     reinterpret_cast<hipStream_t>(stream), mixture_prob) != hipSuccess)
+    return check_launch(fn);
+  return MDLM_OK;
+}
+
 size_t mdlm_compact_workspace_bytes(int64_t n_tokens) {
   return compact_workspace_bytes(n_tokens, 0, MDLM_WEIGHT_INV_P);
 }
@@ -121,6 +147,38 @@ int mdlm_compact_masked(const uint8_t* corrupted, const int32_t* x0, int64_t n_t
   return compact_common("mdlm_compact_masked", true, corrupted, nullptr, x0, n_tokens, cu_seqlens,
                         n_docs, p_doc, align, MDLM_WEIGHT_INV_P, 1.0, 0.0, row_idx, tgt, w,
                         n_rows, workspace, workspace_bytes, stream);
+}
+
+int mdlm_compact_corrective(const uint8_t* codes, const int32_t* x0, int64_t n_tokens,
+                            const int32_t* cu_seqlens, int32_t n_docs, const double* p_doc,
+                            int32_t align, double noise_token_wt, double clean_token_wt,
+                            int32_t* row_idx, int32_t* tgt, float* w, int32_t* n_rows,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* fn = "mdlm_compact_corrective";
+  if (n_tokens < 0) return fail(MDLM_EINVAL, "%s: n_tokens < 0", fn);
+  if (n_tokens > INT32_MAX)
+    return fail(MDLM_EUNSUPPORTED, "%s: n_tokens must be below 2^31", fn);
+  if (n_docs < 0 || (n_docs == 0 && n_tokens > 0))
+    return fail(MDLM_EINVAL, "%s: bad n_docs %d", fn, n_docs);
+  if (align != MDLM_ALIGNED && align != MDLM_SHIFTED)
+    return fail(MDLM_EINVAL, "%s: unknown alignment %d", fn, align);
+  if (!isfinite(noise_token_wt) || !isfinite(clean_token_wt))
+    return fail(MDLM_EINVAL, "%s: token weights must be finite", fn);
+  if (!n_rows) return fail(MDLM_EINVAL, "%s: null n_rows", fn);
+  if (n_tokens > 0 && (!codes || !x0 || !cu_seqlens || !p_doc || !row_idx || !tgt || !w))
+    return fail(MDLM_EINVAL, "%s: null pointer", fn);
+  const size_t need = compact_workspace_bytes(n_tokens, n_docs, MDLM_WEIGHT_INV_P);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MDLM_EWORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes,
+                need);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 4) != 0)
+    return fail(MDLM_EINVAL, "%s: workspace must be 4-byte aligned", fn);
+  if (launch_compact_corrective(codes, x0, n_tokens, cu_seqlens, n_docs, p_doc, align,
+                                noise_token_wt, clean_token_wt, row_idx, tgt, w, n_rows,
+                                workspace, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return check_launch(fn);
+  return MDLM_OK;
 }
 
 int mdlm_compact_rows(const uint8_t* corrupted, const uint8_t* eligible, const int32_t* x0,

@@ -23,6 +23,13 @@
 // most 1024 documents; a wave whose 256 tokens of a round touch at most four
 // documents finds each token's document by comparisons with wave-uniform
 // boundaries instead of a search.
+//
+// The corrective mixture's list (same card and row: noise_token_wt and
+// clean_token_wt, no formula given) uses the same passes: the codes are the
+// mask when clean tokens carry no weight, every token is listed otherwise,
+// and the scatter picks each row's weight by its code from two per-document
+// LDS tables (1 / (p_b N), noise_token_wt / (p_b N)) and one scalar
+// (clean_token_wt / N).
 #include "mdlm_internal.h"
 
 #include <algorithm>
@@ -303,9 +310,18 @@ group_scan_kernel(int32_t* __restrict__ tile_counts, int64_t n_tiles,
   if (tid == 0) group_sums[blockIdx.x] = total;
 }
 
+// Per-token weights of the corrective mixture (kCode): a token's code byte
+// picks the masked weight (the document's scale / (p_b N) with scale 1), the
+// replaced weight (noise_wt / (p_b N)) or the clean weight (clean_wt / N).
+struct CodeWeights {
+  const uint8_t* codes;  // [n] codes 0 clean / 1 masked / 2 replaced
+  double noise_wt;
+  float clean_w;
+};
+
 // Scatter: four rounds per tile; in round j thread t owns the 4 consecutive
 // tokens at 1024 j + 4 t, so every load is contiguous across the wave.
-template <bool kShifted, bool kVec, bool kC, bool kE>
+template <bool kShifted, bool kVec, bool kC, bool kE, bool kCode = false>
 __global__ void __launch_bounds__(kThreads)
 scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict__ eligible,
                const int32_t* __restrict__ x0, int64_t n,
@@ -315,9 +331,10 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
                const float* __restrict__ w_doc, const int32_t* __restrict__ tile_offsets,
                const int32_t* __restrict__ group_sums, int32_t n_groups,
                int32_t* __restrict__ row_idx, int32_t* __restrict__ tgt, float* __restrict__ w,
-               int32_t* __restrict__ n_rows) {
+               int32_t* __restrict__ n_rows, CodeWeights cwt) {
   __shared__ int32_t s_cu[kLdsDocs + 1];
   __shared__ float s_wd[kLdsDocs];
+  __shared__ float s_wd2[kCode ? kLdsDocs : 1];  // replaced-token weights
   __shared__ int s_wsum[kBufs][kWaves];
   __shared__ int32_t s_row[kBufs][kRoundTok];
   __shared__ int32_t s_tgt[kBufs][kRoundTok];
@@ -340,10 +357,20 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
 #pragma clang fp contract(off)
     return w_doc ? w_doc[b] : (float)(scale / (p_doc[b] * (double)n));
   };
+  auto weight2_of_doc = [&](int b) {
+#pragma clang fp contract(off)
+    return (float)(cwt.noise_wt / (p_doc[b] * (double)n));
+  };
   if (cached) {
     for (int i = tid; i <= nd; i += kThreads) s_cu[i] = cu[dlo + i];
     for (int i = tid; i < nd; i += kThreads) s_wd[i] = weight_of_doc(dlo + i);
+    if (kCode)
+      for (int i = tid; i < nd; i += kThreads) s_wd2[i] = weight2_of_doc(dlo + i);
   }
+  // the weight of a selected token from its code and its document's weights
+  auto by_code = [&](uint32_t code, float wm, float wr) {
+    return code == 1u ? wm : code == 2u ? wr : cwt.clean_w;
+  };
   const int grp = (int)(tile / kGroup);
   if (wave == 0) {
     // this tile's offset: its place in its group plus the groups before it
@@ -368,9 +395,11 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
     int32_t vals[4] = {0, 0, 0, 0};
     float wts[4] = {0.f, 0.f, 0.f, 0.f};
     uint32_t mv = 0;  // byte k nonzero iff token g0 + k is corrupted and eligible
+    uint32_t cv = 0;  // (kCode) byte k: the code of token g0 + k
     const int cnt_here = g0 < n ? (int)min<int64_t>(4, n - g0) : 0;
     if (kVec && cnt_here == 4) {
       mv = mk.word(g0);
+      if (kCode) cv = kC && !kE ? mv : *reinterpret_cast<const uint32_t*>(cwt.codes + g0);
       const int4 xv = *reinterpret_cast<const int4*>(x0 + g0);
       vals[0] = xv.x; vals[1] = xv.y; vals[2] = xv.z; vals[3] = xv.w;
     } else {
@@ -378,6 +407,7 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
       for (int k = 0; k < 4; ++k)
         if (k < cnt_here) {
           mv |= (uint32_t)mk.at(g0 + k) << (8 * k);
+          if (kCode) cv |= (uint32_t)cwt.codes[g0 + k] << (8 * k);
           vals[k] = x0[g0 + k];
         }
     }
@@ -393,6 +423,13 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
         const int64_t b3 = span >= 3 ? (int64_t)s_cu[dw + 3] : INT64_MAX;
         const float w0 = s_wd[dw], w1 = s_wd[dw + min(span, 1)];
         const float w2 = s_wd[dw + min(span, 2)], w3 = s_wd[dw + span];
+        float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+        if (kCode) {
+          r0 = s_wd2[dw];
+          r1 = s_wd2[dw + min(span, 1)];
+          r2 = s_wd2[dw + min(span, 2)];
+          r3 = s_wd2[dw + span];
+        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int64_t g = g0 + k;
@@ -401,7 +438,12 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
           const float wk = idx == 0 ? w0 : idx == 1 ? w1 : idx == 2 ? w2 : w3;
           if (((mv >> (8 * k)) & 0xffu) && (!kShifted || g != beg)) {
             sel |= 1u << k;
-            wts[k] = wk;
+            if (kCode) {
+              const float rk = idx == 0 ? r0 : idx == 1 ? r1 : idx == 2 ? r2 : r3;
+              wts[k] = by_code((cv >> (8 * k)) & 0xffu, wk, rk);
+            } else {
+              wts[k] = wk;
+            }
           }
         }
         done = true;
@@ -412,7 +454,9 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
       int64_t d_beg = cached ? s_cu[d] : cu[dlo + d];
       int64_t d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
       auto weight_of = [&](int dd) { return cached ? s_wd[dd] : weight_of_doc(dlo + dd); };
+      auto weight2_of = [&](int dd) { return cached ? s_wd2[dd] : weight2_of_doc(dlo + dd); };
       float wd = weight_of(d);
+      float wr = kCode ? weight2_of(d) : 0.f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int64_t g = g0 + k;
@@ -425,10 +469,11 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
             } while (g >= d_end && d < nd - 1);
             d_beg = cached ? s_cu[d] : cu[dlo + d];
             wd = weight_of(d);
+            if (kCode) wr = weight2_of(d);
           }
           if (!kShifted || g != d_beg) {
             sel |= 1u << k;
-            wts[k] = wd;
+            wts[k] = kCode ? by_code((cv >> (8 * k)) & 0xffu, wd, wr) : wd;
           }
         }
       }
@@ -503,11 +548,12 @@ struct Launch {
   int32_t* n_rows;
   bool vec;
   hipStream_t stream;
+  CodeWeights cwt;  // corrective mixture only
 };
 
 // The passes after tile_docs_kernel, for one combination of alignment and
 // masks present.
-template <bool kShifted, bool kC, bool kE>
+template <bool kShifted, bool kC, bool kE, bool kCode = false>
 void run_passes(const Launch& L, RowMasks<kC, kE> mk) {
   hipStream_t st = L.stream;
   if (L.wa.mode == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED) {
@@ -524,15 +570,15 @@ void run_passes(const Launch& L, RowMasks<kC, kE> mk) {
     doc_weights_kernel<<<(unsigned)((L.n_docs + kThreads - 1) / kThreads), kThreads, 0, st>>>(
         L.wa, L.n_docs, L.group_sums, (int32_t)L.groups, L.w_doc);
   if (L.vec)
-    scatter_kernel<kShifted, true, kC, kE><<<(unsigned)L.tiles, kThreads, 0, st>>>(
+    scatter_kernel<kShifted, true, kC, kE, kCode><<<(unsigned)L.tiles, kThreads, 0, st>>>(
         mk.corrupted, mk.eligible, L.x0, L.n, L.cu, L.n_docs, L.tile_lo, L.tile_hi, L.wa.p_doc,
         L.wa.scale, L.w_doc,
-        L.counts, L.group_sums, (int32_t)L.groups, L.row_idx, L.tgt, L.w, L.n_rows);
+        L.counts, L.group_sums, (int32_t)L.groups, L.row_idx, L.tgt, L.w, L.n_rows, L.cwt);
   else
-    scatter_kernel<kShifted, false, kC, kE><<<(unsigned)L.tiles, kThreads, 0, st>>>(
+    scatter_kernel<kShifted, false, kC, kE, kCode><<<(unsigned)L.tiles, kThreads, 0, st>>>(
         mk.corrupted, mk.eligible, L.x0, L.n, L.cu, L.n_docs, L.tile_lo, L.tile_hi, L.wa.p_doc,
         L.wa.scale, L.w_doc,
-        L.counts, L.group_sums, (int32_t)L.groups, L.row_idx, L.tgt, L.w, L.n_rows);
+        L.counts, L.group_sums, (int32_t)L.groups, L.row_idx, L.tgt, L.w, L.n_rows, L.cwt);
 }
 
 }  // namespace
@@ -569,8 +615,9 @@ hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, con
                                                                                 tile_lo, tile_hi);
   const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)corrupted % 4 == 0) &&
                    ((uintptr_t)eligible % 4 == 0);
-  const Launch L{n, cu, n_docs, tiles, groups, counts, tile_lo, tile_hi, group_sums, doc_rows,
-                 n_examples, w_doc, x0, wa, row_idx, tgt, w, n_rows, vec, stream};
+  const Launch L{n,        cu,     n_docs, tiles,     groups, counts,    tile_lo,
+                 tile_hi,  group_sums, doc_rows, n_examples, w_doc, x0, wa,
+                 row_idx,  tgt,    w,      n_rows,    vec,    stream,    CodeWeights{}};
   const bool shifted = align == MDLM_SHIFTED;
   const int key = (shifted ? 4 : 0) | (corrupted ? 2 : 0) | (eligible ? 1 : 0);
   switch (key) {
@@ -582,6 +629,44 @@ hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, con
     case 5: run_passes<true, false, true>(L, {corrupted, eligible}); break;
     case 6: run_passes<true, true, false>(L, {corrupted, eligible}); break;
     default: run_passes<true, true, true>(L, {corrupted, eligible}); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_corrective(const uint8_t* codes, const int32_t* x0, int64_t n,
+                                     const int32_t* cu, int32_t n_docs, const double* p_doc,
+                                     int32_t align, double noise_wt, double clean_wt,
+                                     int32_t* row_idx, int32_t* tgt, float* w, int32_t* n_rows,
+                                     void* workspace, hipStream_t stream) {
+  if (n <= 0) {
+    set_int_kernel<<<1, 1, 0, stream>>>(n_rows, 0);
+    return hipGetLastError();
+  }
+  const int64_t tiles = (n + kTile - 1) / kTile;
+  const int64_t groups = (tiles + kGroup - 1) / kGroup;
+  int32_t* counts = reinterpret_cast<int32_t*>(workspace);
+  int32_t* tile_lo = counts + tiles;
+  int32_t* tile_hi = tile_lo + tiles;
+  int32_t* group_sums = tile_hi + tiles;
+  // masked rows: the inverse-p weight with scale 1
+  WeightArgs wa{MDLM_WEIGHT_INV_P, 1.0, 0.0, p_doc, n, nullptr, nullptr};
+  tile_docs_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(cu, n_docs, n,
+                                                                                tile_lo, tile_hi);
+  const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)codes % 4 == 0);
+  const CodeWeights cwt{codes, noise_wt, (float)(clean_wt / (double)n)};
+  const Launch L{n,        cu,     n_docs,  tiles,   groups, counts,  tile_lo,
+                 tile_hi,  group_sums, nullptr, nullptr, nullptr, x0,  wa,
+                 row_idx,  tgt,    w,       n_rows,  vec,    stream,  cwt};
+  const bool shifted = align == MDLM_SHIFTED;
+  // without clean rows the codes are the selection mask (nonzero: corrupted
+  // either way); with them every token is a row
+  const bool clean = clean_wt != 0.0;
+  if (shifted) {
+    if (clean) run_passes<true, false, false, true>(L, {nullptr, nullptr});
+    else run_passes<true, true, false, true>(L, {codes, nullptr});
+  } else {
+    if (clean) run_passes<false, false, false, true>(L, {nullptr, nullptr});
+    else run_passes<false, true, false, true>(L, {codes, nullptr});
   }
   return hipGetLastError();
 }

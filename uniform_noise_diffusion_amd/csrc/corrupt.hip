@@ -4,7 +4,12 @@
 // per sequence, mask probability p = (1 - 1e-3) t + 1e-3); diffusiongemma card,
 // "Finetuning notes" (uniform-random ids at a per-example rate t ~ U(eps, 1));
 // Axolotl diffusion docs, "Packed training" (documents in a packed stream stay
-// isolated, so each draws its own t).
+// isolated, so each draws its own t).  The corrective mixture (same card and
+// row: mixture_prob and noise_token_wt, no formula given) is read as
+// absorbing corruption in which a corrupted token takes the uniform-noise id
+// instead of the mask token when a fourth Philox stream's word falls under
+// ceil(mixture_prob 2^24); its output byte is then a code (1 masked, 2
+// replaced) rather than a flag.
 //
 // Layout: a block covers 4096 tokens in four rounds; in round j thread t owns
 // the 4 consecutive tokens starting at 4 (t + 256 j), exactly the output of one
@@ -54,54 +59,66 @@ __device__ __forceinline__ int wave_sum(int v) {
 }
 
 // Four consecutive tokens g0..g0+3 (g0 a multiple of 4), loaded as v, with
-// Bernoulli thresholds t0..t3: writes xt and the mask bytes and returns the
-// four corruption flags as bits 0, 8, 16, 24.
-template <bool kUniform>
+// Bernoulli thresholds t0..t3: writes xt and the mask bytes (with the
+// mixture: codes 1 masked / 2 replaced) and returns the four corruption
+// flags as bits 0, 8, 16, 24.
+template <int kMode>
 __device__ __forceinline__ uint32_t corrupt4_core(int4 v, int64_t g0, uint32_t t0, uint32_t t1,
                                                   uint32_t t2, uint32_t t3, uint32_t k0,
                                                   uint32_t k1, int32_t mask_id,
-                                                  uint32_t rand_vocab, int32_t* __restrict__ xt,
+                                                  uint32_t rand_vocab, uint32_t thr_mix,
+                                                  int32_t* __restrict__ xt,
                                                   uint8_t* __restrict__ corrupted) {
   const uint64_t q = (uint64_t)g0 >> 2;
   const uint4 r1 =
       philox4x32_10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagBernoulli), k0, k1);
-  uint4 r2 = make_uint4(0, 0, 0, 0);
-  if (kUniform)
+  uint4 r2 = make_uint4(0, 0, 0, 0), r3 = make_uint4(0, 0, 0, 0);
+  if (kMode != MDLM_NOISE_ABSORB)
     r2 = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagReplace), k0, k1);
+  if (kMode == kNoiseMixture)
+    r3 = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagMix), k0, k1);
   const bool c0 = (r1.x >> 8) < t0, c1 = (r1.y >> 8) < t1;
   const bool c2 = (r1.z >> 8) < t2, c3 = (r1.w >> 8) < t3;
-  auto repl = [&](uint32_t w2) {
-    return kUniform ? (int32_t)(((uint64_t)w2 * rand_vocab) >> 32) : mask_id;
+  // replaced (rather than masked) when corrupted
+  auto rep = [&](uint32_t w3) {
+    return kMode == MDLM_NOISE_UNIFORM || (kMode == kNoiseMixture && (w3 >> 8) < thr_mix);
   };
-  *reinterpret_cast<int4*>(xt + g0) =
-      make_int4(c0 ? repl(r2.x) : v.x, c1 ? repl(r2.y) : v.y, c2 ? repl(r2.z) : v.z,
-                c3 ? repl(r2.w) : v.w);
+  const bool p0 = rep(r3.x), p1 = rep(r3.y), p2 = rep(r3.z), p3 = rep(r3.w);
+  auto out = [&](bool c, bool pr, uint32_t w2, int32_t x) {
+    return c ? (pr ? (int32_t)(((uint64_t)w2 * rand_vocab) >> 32) : mask_id) : x;
+  };
+  *reinterpret_cast<int4*>(xt + g0) = make_int4(out(c0, p0, r2.x, v.x), out(c1, p1, r2.y, v.y),
+                                                out(c2, p2, r2.z, v.z), out(c3, p3, r2.w, v.w));
   const uint32_t bits =
       (uint32_t)c0 | ((uint32_t)c1 << 8) | ((uint32_t)c2 << 16) | ((uint32_t)c3 << 24);
-  *reinterpret_cast<uint32_t*>(corrupted + g0) = bits;
+  uint32_t codes = bits;
+  if (kMode == kNoiseMixture)
+    codes += ((uint32_t)(c0 && p0) | ((uint32_t)(c1 && p1) << 8) |
+              ((uint32_t)(c2 && p2) << 16) | ((uint32_t)(c3 && p3) << 24));
+  *reinterpret_cast<uint32_t*>(corrupted + g0) = codes;
   return bits;
 }
 
 // corrupt4_core for four tokens of one document (threshold thr); returns the
 // wave's corrupted count (every lane of the wave must call it).
-template <bool kUniform>
+template <int kMode>
 __device__ __forceinline__ int corrupt4(int4 v, int64_t g0, uint32_t thr, uint32_t k0,
                                         uint32_t k1, int32_t mask_id, uint32_t rand_vocab,
-                                        int32_t* __restrict__ xt,
+                                        uint32_t thr_mix, int32_t* __restrict__ xt,
                                         uint8_t* __restrict__ corrupted) {
-  const uint32_t bits = corrupt4_core<kUniform>(v, g0, thr, thr, thr, thr, k0, k1, mask_id,
-                                                rand_vocab, xt, corrupted);
+  const uint32_t bits = corrupt4_core<kMode>(v, g0, thr, thr, thr, thr, k0, k1, mask_id,
+                                             rand_vocab, thr_mix, xt, corrupted);
   int c = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) c += __popcll(__ballot((bits >> (8 * k)) & 1u));
   return c;
 }
 
-template <bool kUniform, bool kVec>
+template <int kMode, bool kVec>
 __global__ void __launch_bounds__(kThreads)
 corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restrict__ cu,
                int32_t n_docs, uint32_t k0, uint32_t k1, const double* __restrict__ p_doc,
-               int32_t mask_id, uint32_t rand_vocab, int32_t* __restrict__ xt,
+               int32_t mask_id, uint32_t rand_vocab, uint32_t thr_mix, int32_t* __restrict__ xt,
                uint8_t* __restrict__ corrupted, int32_t* __restrict__ doc_counts) {
   __shared__ int s_dlo, s_dhi;
   __shared__ int32_t s_cu[kLdsDocs + 1];
@@ -157,8 +174,8 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
     int c = 0;
 #pragma unroll
     for (int j = 0; j < kRounds; ++j)
-      c += corrupt4<kUniform>(v[j], blk0 + 4 * (int64_t)(tid + kThreads * j), thr, k0, k1,
-                              mask_id, rand_vocab, xt, corrupted);
+      c += corrupt4<kMode>(v[j], blk0 + 4 * (int64_t)(tid + kThreads * j), thr, k0, k1,
+                           mask_id, rand_vocab, thr_mix, xt, corrupted);
     if (lane == 0 && c) atomicAdd(&doc_counts[dlo], c);
     return;
   }
@@ -180,8 +197,8 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
       }
       const int4 v = *reinterpret_cast<const int4*>(x0 + g0);
       if (span == 0) {
-        const int c = corrupt4<kUniform>(v, g0, s_thr[dw], k0, k1, mask_id, rand_vocab, xt,
-                                         corrupted);
+        const int c = corrupt4<kMode>(v, g0, s_thr[dw], k0, k1, mask_id, rand_vocab, thr_mix,
+                                      xt, corrupted);
         if (lane == 0 && c) atomicAdd(&s_cnt[dw], c);
         continue;
       }
@@ -200,8 +217,8 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
           idx[k] = (int)(g >= b1) + (int)(g >= b2) + (int)(g >= b3);
           tk[k] = idx[k] == 0 ? th0 : idx[k] == 1 ? th1 : idx[k] == 2 ? th2 : th3;
         }
-        const uint32_t bits = corrupt4_core<kUniform>(v, g0, tk[0], tk[1], tk[2], tk[3], k0, k1,
-                                                      mask_id, rand_vocab, xt, corrupted);
+        const uint32_t bits = corrupt4_core<kMode>(v, g0, tk[0], tk[1], tk[2], tk[3], k0, k1,
+                                                   mask_id, rand_vocab, thr_mix, xt, corrupted);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (i > span) break;
@@ -221,12 +238,16 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
       const uint64_t q = (uint64_t)g0 >> 2;
       const uint4 r1 = philox4x32_10(
           make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagBernoulli), k0, k1);
-      uint4 r2 = make_uint4(0, 0, 0, 0);
-      if (kUniform)
+      uint4 r2 = make_uint4(0, 0, 0, 0), r3 = make_uint4(0, 0, 0, 0);
+      if (kMode != MDLM_NOISE_ABSORB)
         r2 = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagReplace), k0,
                            k1);
+      if (kMode == kNoiseMixture)
+        r3 = philox4x32_10(make_uint4((uint32_t)q, (uint32_t)(q >> 32), 0u, kTagMix), k0, k1);
       const uint32_t w1[4] = {r1.x, r1.y, r1.z, r1.w};
       const uint32_t w2[4] = {r2.x, r2.y, r2.z, r2.w};
+      const uint32_t w3[4] = {r3.x, r3.y, r3.z, r3.w};
+      uint32_t code_bits = 0;  // the stored mask bytes (codes with the mixture)
       const int cnt_here = (int)min<int64_t>(4, n - g0);
       int32_t in[4];
       if (kVec && cnt_here == 4) {
@@ -257,17 +278,20 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
           dl[k] = d;
           if ((w1[k] >> 8) < thr) {
             flag_bits |= 1u << (8 * k);
-            out[k] = kUniform ? (int32_t)(((uint64_t)w2[k] * rand_vocab) >> 32) : mask_id;
+            const bool replaced = kMode == MDLM_NOISE_UNIFORM ||
+                                  (kMode == kNoiseMixture && (w3[k] >> 8) < thr_mix);
+            code_bits |= (kMode == kNoiseMixture && replaced ? 2u : 1u) << (8 * k);
+            out[k] = replaced ? (int32_t)(((uint64_t)w2[k] * rand_vocab) >> 32) : mask_id;
           }
         }
       }
       if (kVec && cnt_here == 4) {
         *reinterpret_cast<int4*>(xt + g0) = make_int4(out[0], out[1], out[2], out[3]);
-        *reinterpret_cast<uint32_t*>(corrupted + g0) = flag_bits;
+        *reinterpret_cast<uint32_t*>(corrupted + g0) = code_bits;
       } else {
         for (int k = 0; k < cnt_here; ++k) {
           xt[g0 + k] = out[k];
-          corrupted[g0 + k] = (uint8_t)((flag_bits >> (8 * k)) & 1u);
+          corrupted[g0 + k] = (uint8_t)((code_bits >> (8 * k)) & 0xffu);
         }
       }
     }
@@ -330,7 +354,8 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
 hipError_t launch_corrupt(const int32_t* x0, int64_t n, const int32_t* cu, int32_t n_docs,
                           uint64_t seed, double eps, int32_t noise, int32_t mask_id,
                           int32_t rand_vocab, int32_t* xt, uint8_t* corrupted,
-                          double* p_doc, int32_t* doc_counts, hipStream_t stream) {
+                          double* p_doc, int32_t* doc_counts, hipStream_t stream,
+                          double mixture_prob) {
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   if (n_docs > 0) {
     noise_level_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
@@ -339,17 +364,23 @@ hipError_t launch_corrupt(const int32_t* x0, int64_t n, const int32_t* cu, int32
   if (n > 0) {
     const unsigned grid = (unsigned)((n + kTokPerBlock - 1) / kTokPerBlock);
     const uint32_t rv = (uint32_t)rand_vocab;
+    // ceil(mixture_prob * 2^24): exact (power-of-two scaling), 0 .. 2^24
+    const uint32_t thr_mix = (uint32_t)ceil(mixture_prob * 16777216.0);
     const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)xt % 16 == 0) &&
                      ((uintptr_t)corrupted % 4 == 0);
-#define MDLM_CORRUPT_LAUNCH(U, VEC)                                                      \
-  corrupt_kernel<U, VEC><<<grid, kThreads, 0, stream>>>(x0, n, cu, n_docs, k0, k1, p_doc, \
-                                                        mask_id, rv, xt, corrupted, doc_counts)
+#define MDLM_CORRUPT_LAUNCH(M, VEC)                                                       \
+  corrupt_kernel<M, VEC><<<grid, kThreads, 0, stream>>>(x0, n, cu, n_docs, k0, k1, p_doc,  \
+                                                        mask_id, rv, thr_mix, xt, corrupted, \
+                                                        doc_counts)
     if (noise == MDLM_NOISE_UNIFORM) {
-      if (vec) MDLM_CORRUPT_LAUNCH(true, true);
-      else MDLM_CORRUPT_LAUNCH(true, false);
+      if (vec) MDLM_CORRUPT_LAUNCH(MDLM_NOISE_UNIFORM, true);
+      else MDLM_CORRUPT_LAUNCH(MDLM_NOISE_UNIFORM, false);
+    } else if (noise == kNoiseMixture) {
+      if (vec) MDLM_CORRUPT_LAUNCH(kNoiseMixture, true);
+      else MDLM_CORRUPT_LAUNCH(kNoiseMixture, false);
     } else {
-      if (vec) MDLM_CORRUPT_LAUNCH(false, true);
-      else MDLM_CORRUPT_LAUNCH(false, false);
+      if (vec) MDLM_CORRUPT_LAUNCH(MDLM_NOISE_ABSORB, true);
+      else MDLM_CORRUPT_LAUNCH(MDLM_NOISE_ABSORB, false);
     }
 #undef MDLM_CORRUPT_LAUNCH
   }

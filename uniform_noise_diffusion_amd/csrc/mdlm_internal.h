@@ -45,6 +45,10 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
 constexpr uint32_t kTagDocT = 0;
 constexpr uint32_t kTagBernoulli = 1;
 constexpr uint32_t kTagReplace = 2;
+constexpr uint32_t kTagMix = 3;  // corrective mixture: mask or replace a corrupted token
+// Corruption modes: the two noise modes of mdlm_corrupt, and the corrective
+// mixture of mdlm_corrupt_mixture (mask bytes are then codes 1 / 2).
+constexpr int32_t kNoiseMixture = 2;
 
 // Index of the document holding token g: the b with cu[b] <= g < cu[b+1],
 // searched among documents [lo, hi] (which must contain it).
@@ -105,13 +109,22 @@ __device__ __forceinline__ int lds_find_doc(const int32_t* s_cu, int nd, int64_t
 }
 
 // ---- launchers implemented in the kernel translation units ---------------
+// noise: MDLM_NOISE_ABSORB, MDLM_NOISE_UNIFORM or kNoiseMixture (then
+// mixture_prob in [0, 1] is the share of corrupted tokens replaced)
 hipError_t launch_corrupt(const int32_t* x0, int64_t n_tokens, const int32_t* cu,
                           int32_t n_docs, uint64_t seed, double eps, int32_t noise,
                           int32_t mask_id, int32_t rand_vocab, int32_t* xt,
                           uint8_t* corrupted, double* p_doc, int32_t* doc_counts,
-                          hipStream_t stream);
+                          hipStream_t stream, double mixture_prob = 0.0);
 
 size_t compact_workspace_bytes(int64_t n_tokens, int32_t n_docs, int32_t weighting);
+// the corrective mixture's row list (mdlm_compact_corrective); workspace as
+// for the inverse-p weighting
+hipError_t launch_compact_corrective(const uint8_t* codes, const int32_t* x0, int64_t n,
+                                     const int32_t* cu, int32_t n_docs, const double* p_doc,
+                                     int32_t align, double noise_wt, double clean_wt,
+                                     int32_t* row_idx, int32_t* tgt, float* w, int32_t* n_rows,
+                                     void* workspace, hipStream_t stream);
 hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, const int32_t* x0,
                           int64_t n_tokens, const int32_t* cu, int32_t n_docs,
                           const double* p_doc, int32_t align, int32_t weighting, double scale,

@@ -50,6 +50,20 @@ class MdlmLossStep:
         B.mdlm_compact_masked(self.corrupted, x0, cu_seqlens, self.p_doc, align, self.row_idx,
                               self.tgt, self.w, self.n_rows, self.compact_ws, stream)
 
+    def corrupt_mixture(self, x0, cu_seqlens, seed, eps, mixture_prob, mask_id, rand_vocab,
+                        stream=None):
+        """mdlm_corrupt_mixture: `corrupted` then holds the codes (0 clean,
+        1 masked, 2 replaced)."""
+        B.mdlm_corrupt_mixture(x0, cu_seqlens, seed, eps, mixture_prob, mask_id, rand_vocab,
+                               self.xt, self.corrupted, self.p_doc, self.doc_counts, stream)
+
+    def compact_corrective(self, x0, cu_seqlens, align, noise_token_wt, clean_token_wt,
+                           stream=None):
+        """mdlm_compact_corrective over the codes of the last corrupt_mixture()."""
+        B.mdlm_compact_corrective(self.corrupted, x0, cu_seqlens, self.p_doc, align,
+                                  noise_token_wt, clean_token_wt, self.row_idx, self.tgt,
+                                  self.w, self.n_rows, self.compact_ws, stream)
+
     def compact_rows(self, x0, cu_seqlens, align, weighting, weight_scale=1.0,
                      weight_clip=float("inf"), corrupted=True, eligible=None, stream=None):
         """mdlm_compact_rows into this step's row buffers: `corrupted` True uses
