@@ -66,6 +66,8 @@ WEIGHTS = [(0.0, 0.0), (0.5, 0.0), (1.0, 0.0), (0.3, 0.7), (2.0, -0.5)]
     (3, 7, 3000, False),     # documents spanning block boundaries
     (4, 600, 20, True),      # many short documents per block
     (5, 5000, 2, True),      # more documents per 4096-token block than it caches
+    (6, 3000, 9, False),     # about 800 documents per block: cached by the masked
+                             # form, not by the code-weight form
 ])
 def test_corrective_bit_exact_small(a, c, align, seed, n_docs, max_len, empty):
     x0, cu = _case(seed, n_docs, max_len, empty)

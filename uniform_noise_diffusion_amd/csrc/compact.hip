@@ -20,7 +20,7 @@
 //      round's scored tokens with ballots, stages (row, target, weight) in a
 //      double-buffered LDS area and writes them with coalesced stores.
 // A tile's document offsets and weights are cached in LDS when it touches at
-// most 1024 documents; a wave whose 256 tokens of a round touch at most four
+// most 1024 documents (682 with the corrective mixture's second table); a wave whose 256 tokens of a round touch at most four
 // documents finds each token's document by comparisons with wave-uniform
 // boundaries instead of a search.
 //
@@ -332,9 +332,11 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
                const int32_t* __restrict__ group_sums, int32_t n_groups,
                int32_t* __restrict__ row_idx, int32_t* __restrict__ tgt, float* __restrict__ w,
                int32_t* __restrict__ n_rows, CodeWeights cwt) {
-  __shared__ int32_t s_cu[kLdsDocs + 1];
-  __shared__ float s_wd[kLdsDocs];
-  __shared__ float s_wd2[kCode ? kLdsDocs : 1];  // replaced-token weights
+  // the code-weight form holds a second weight table in the same LDS budget
+  constexpr int kDocs = kCode ? kLdsDocs * 2 / 3 : kLdsDocs;
+  __shared__ int32_t s_cu[kDocs + 1];
+  __shared__ float s_wd[kDocs];
+  __shared__ float s_wd2[kCode ? kDocs : 1];  // replaced-token weights
   __shared__ int s_wsum[kBufs][kWaves];
   __shared__ int32_t s_row[kBufs][kRoundTok];
   __shared__ int32_t s_tgt[kBufs][kRoundTok];
@@ -350,7 +352,7 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
   int dlo, dhi;
   tile_range(tile_lo, tile_hi, n_docs, tile, &dlo, &dhi);
   const int nd = dhi - dlo + 1;
-  const bool cached = nd <= kLdsDocs;
+  const bool cached = nd <= kDocs;
   // per-document weight: scale / (p_b N) computed here, or from the table
   // of the other weightings
   auto weight_of_doc = [&](int b) {
