@@ -104,3 +104,21 @@ def test_random_head_weight_gradient(case):
     want = oracle.head_ce_weight_grad(inp.hidden, inp.W, rows, tgt, w.astype(np.float32),
                                       softcap)
     assert rel_l2(host(dW), want) < 1e-2
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_corrective_mixture(case):
+    """Random layouts, mixture shares and token weights through
+    mdlm_corrupt_mixture and mdlm_compact_corrective, bit for bit."""
+    from test_gpu_corrective import _check as _check_corrective
+    rng = np.random.default_rng(4000 + case)
+    cu = _layout(rng, 40000)
+    V = int(rng.integers(2, 200000))
+    x0 = rng.integers(0, V, size=int(cu[-1])).astype(np.int32)
+    eps = float(rng.choice([1e-3, rng.random(), 1.0]))
+    mix = float(rng.choice([0.0, rng.random(), 1.0]))
+    a = float(rng.choice([0.0, rng.random(), 1.0]))
+    c = float(rng.choice([0.0, 0.0, rng.random()]))
+    align = int(rng.integers(0, 2))
+    seed = int(rng.integers(0, 2**63))
+    _check_corrective(x0, cu, seed, eps, mix, align, a, c, int(rng.integers(0, V)), V)
