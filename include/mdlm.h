@@ -14,6 +14,11 @@
  *                                hidden states, without writing logits to
  *                                memory.
  *
+ * Loss variants replace the first two calls: mdlm_compact_rows (every-token
+ * causal rows, an eligibility mask, other weightings) and the corrective
+ * mixture's mdlm_corrupt_mixture + mdlm_compact_corrective;
+ * mdlm_fused_head_ce_fwd_bwd_dw adds the head's own gradient.
+ *
  * The method is defined on these pages:
  *   - LLaDA-8B-MDLM-LoRA model card, "Training" table, "Objective" row:
  *     t ~ U(0,1) per sequence, mask probability p = (1 - 1e-3) t + 1e-3,
