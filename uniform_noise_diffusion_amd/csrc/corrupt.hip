@@ -30,6 +30,11 @@ constexpr int kThreads = 256;
 #endif
 constexpr int kRounds = MDLM_CORRUPT_ROUNDS;
 constexpr int kTokPerBlock = kThreads * 4 * kRounds;  // 4096 by default
+#ifndef MDLM_CORRUPT_PRELOAD
+#define MDLM_CORRUPT_PRELOAD 1
+#endif
+// a full block loads all its tokens before locating its documents
+constexpr bool kPreload = MDLM_CORRUPT_PRELOAD;
 constexpr int kLdsDocs = 1024;                        // documents cached per block
 
 __global__ void __launch_bounds__(kThreads)
@@ -131,6 +136,15 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t blk0 = (int64_t)blockIdx.x * kTokPerBlock;
   const int64_t blk1 = min(blk0 + kTokPerBlock, n);
+  // A full block issues the loads of all its tokens first, so that they are
+  // in flight while the block finds its documents and fills its tables.
+  const bool full = kVec && kPreload && blk1 - blk0 == kTokPerBlock;
+  int4 vpre[kRounds];
+  if (full) {
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j)
+      vpre[j] = *reinterpret_cast<const int4*>(x0 + blk0 + 4 * (int64_t)(tid + kThreads * j));
+  }
   if (wave == 0) {
     const int d = wave_find_doc(cu, n_docs, blk0);
     if (lane == 0) s_dlo = d;
@@ -169,7 +183,8 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
     int4 v[kRounds];
 #pragma unroll
     for (int j = 0; j < kRounds; ++j)
-      v[j] = *reinterpret_cast<const int4*>(x0 + blk0 + 4 * (int64_t)(tid + kThreads * j));
+      v[j] = full ? vpre[j]
+                  : *reinterpret_cast<const int4*>(x0 + blk0 + 4 * (int64_t)(tid + kThreads * j));
     const uint32_t thr = s_thr[0];
     int c = 0;
 #pragma unroll
@@ -180,6 +195,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
     return;
   }
 
+#pragma unroll
   for (int j = 0; j < kRounds; ++j) {
     const int64_t g0 = blk0 + 4 * (int64_t)(tid + kThreads * j);
     // Fast paths for a wave whose 256 tokens all exist (wave-uniform tests):
@@ -195,7 +211,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
         dw = pk & 0xffff;
         span = pk >> 16;
       }
-      const int4 v = *reinterpret_cast<const int4*>(x0 + g0);
+      const int4 v = full ? vpre[j] : *reinterpret_cast<const int4*>(x0 + g0);
       if (span == 0) {
         const int c = corrupt4<kMode>(v, g0, s_thr[dw], k0, k1, mask_id, rand_vocab, thr_mix,
                                       xt, corrupted);
@@ -251,7 +267,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
       const int cnt_here = (int)min<int64_t>(4, n - g0);
       int32_t in[4];
       if (kVec && cnt_here == 4) {
-        const int4 v = *reinterpret_cast<const int4*>(x0 + g0);
+        const int4 v = full ? vpre[j] : *reinterpret_cast<const int4*>(x0 + g0);
         in[0] = v.x; in[1] = v.y; in[2] = v.z; in[3] = v.w;
       } else {
 #pragma unroll
