@@ -10,7 +10,7 @@
 // read it there):
 //   0. (gradient with the preferred workspace) stash_ref_kernel: each row's
 //      reference R, its capped target logit in log2 units from a plain dot
-//      product.
+//      product; its spare blocks clear d_hidden.
 //   1. logits_kernel<fwd>: z = W h over 256 x 256 (vocab x row) tiles, K = H,
 //      on bf16 MFMA with fp32 accumulation.  Operands go from global memory
 //      straight into a two-stage LDS ring (no register staging), two waves per
@@ -33,7 +33,7 @@
 //      transpose loads, split along the vocabulary into S slices chosen on
 //      the device so that the tile x slice units fill the grid; for the rows
 //      left as stash it forms sum_v q_v W_v instead.
-//   5. zero_kernel + scatter_kernel: d_hidden = 0, then d_hidden[row_idx[j]]
+//   5. d_hidden = 0 (zero_kernel, or step 0), then scatter_kernel: d_hidden[row_idx[j]]
 //      = sum of the S slices of dH[j], in the hidden dtype; for stash rows
 //      times the row factor w 2^(R - lse), plus the exact target term.
 //   6. (trained head only) the remaining stash rows become G,
@@ -229,8 +229,9 @@ struct LogitsArgs {
   float inv_softcap;
   int v_begin;  // vocabulary range of this launch
   int v_end;
-  float2* partial;  // fwd: [2 ceil(V/kTile)][max_rows] (max, sum) per 128-entry half
-                    // tile, in log2 units
+  float2* partial;  // fwd: [max_rows][n_part] (max, sum) per 128-entry half tile, in
+                    // log2 units (row-major, so that a row's partials are contiguous)
+  int n_part;       // 2 ceil(V/kTile)
   float* ztgt;      // [max_rows] capped target logit x log2(e) (fwd writes, grad reads)
   const float* lse; // grad: [max_rows]
   bf16_t* G;        // grad, or fwd with the stash: [max_rows][ldg], column = v - v_begin
@@ -506,7 +507,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
             }
           sum += __shfl_xor(sum, 32, 64);
           if (lane < 32 && mvalid)
-            a.partial[(int64_t)(2 * ((v0 - a.v_begin) / kTile) + wa) * a.max_rows + m] =
+            a.partial[(int64_t)m * a.n_part + 2 * ((v0 - a.v_begin) / kTile) + wa] =
                 make_float2(mx, sum);
         } else if (mvalid) {
           // G = w p cap' everywhere, then the target entry is rewritten with
@@ -912,7 +913,7 @@ gather_rows_kernel(const bf16_t* __restrict__ hidden, const int32_t* __restrict_
 // Reductions.
 // --------------------------------------------------------------------------
 __global__ void __launch_bounds__(kThreads)
-merge_kernel(const float2* __restrict__ partial, int n_vt, int max_rows,
+merge_kernel(const float2* __restrict__ partial, int n_part, int max_rows,
              const float* __restrict__ ztgt, const int32_t* __restrict__ tgt, int V,
              const float* __restrict__ w, const int32_t* __restrict__ n_rows_ptr,
              float* __restrict__ lse_out, float* __restrict__ row_ce,
@@ -924,8 +925,8 @@ merge_kernel(const float2* __restrict__ partial, int n_vt, int max_rows,
   double c = 0.0;
   if (j < n_rows) {
     float mx = -INFINITY, s = 0.f;
-    for (int t = lane; t < n_vt; t += 64) {
-      const float2 p = partial[(int64_t)t * max_rows + j];
+    for (int t = lane; t < n_part; t += 64) {
+      const float2 p = partial[(int64_t)j * n_part + t];
       const float nm = fmaxf(mx, p.x);
       if (nm != -INFINITY)
         s = s * __builtin_amdgcn_exp2f(mx - nm) + p.y * __builtin_amdgcn_exp2f(p.x - nm);
@@ -961,17 +962,29 @@ merge_kernel(const float2* __restrict__ partial, int n_vt, int max_rows,
 
 // The stash's per-row reference: the capped target logit in log2 units,
 // computed on its own (one wave per row, fp32), and a cleared fallback flag.
-// Rows whose hidden row or target lies outside its range get 0.
+// Rows whose hidden row or target lies outside its range get 0.  The first
+// ref_blocks blocks do this; any blocks after them clear d_hidden (z16
+// 16-byte words at zp, then z_tail bytes), which would otherwise take a
+// launch of its own.
 __global__ void __launch_bounds__(kThreads)
 stash_ref_kernel(const bf16_t* __restrict__ hidden, const bf16_t* __restrict__ W, int H, int V,
                  const int32_t* __restrict__ row_idx, const int32_t* __restrict__ tgt,
                  const int32_t* __restrict__ n_rows_ptr, int max_rows, int64_t n_tokens,
                  float softcap, float inv_softcap, float* __restrict__ rref,
-                 int* __restrict__ row_flag) {
+                 int* __restrict__ row_flag, int ref_blocks, uint4* __restrict__ zp,
+                 int64_t z16, uint8_t* __restrict__ ztail, int64_t z_tail) {
+  if ((int)blockIdx.x >= ref_blocks) {
+    const int64_t zb = blockIdx.x - ref_blocks, nzb = gridDim.x - ref_blocks;
+    for (int64_t i = zb * kThreads + threadIdx.x; i < z16; i += nzb * kThreads)
+      zp[i] = make_uint4(0, 0, 0, 0);
+    if (zb == 0)
+      for (int64_t i = threadIdx.x; i < z_tail; i += kThreads) ztail[i] = 0;
+    return;
+  }
   const int n_rows = min(*n_rows_ptr, max_rows);
   const int lane = threadIdx.x & 63;
   for (int j = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); j < n_rows;
-       j += gridDim.x * (kThreads / 64)) {
+       j += ref_blocks * (kThreads / 64)) {
     const int64_t r = row_idx[j];
     const int tg = tgt[j];
     float acc = 0.f;
@@ -1014,7 +1027,7 @@ constexpr int kScaleSeg = kThreads * 8;
 
 __global__ void __launch_bounds__(kThreads)
 stash_scale_kernel(bf16_t* __restrict__ G, int64_t ldg, const float2* __restrict__ partial,
-                   int max_rows, const float* __restrict__ lse, const float* __restrict__ ztgt,
+                   int n_part, int max_rows, const float* __restrict__ lse, const float* __restrict__ ztgt,
                    const int32_t* __restrict__ tgt, const float* __restrict__ w,
                    const int32_t* __restrict__ n_rows_ptr, int V, float inv_softcap,
                    const float* __restrict__ rref, const int* __restrict__ row_flag,
@@ -1049,7 +1062,7 @@ stash_scale_kernel(bf16_t* __restrict__ G, int64_t ldg, const float2* __restrict
       for (int b = 0; b < 4; ++b) {
         const int v = v0 + b * kScaleSeg;
         if (v >= ldg) break;
-        const float mh = partial[(int64_t)(v / (kTile / 2)) * max_rows + m].x;
+        const float mh = partial[(int64_t)m * n_part + v / (kTile / 2)].x;
         const float rho = mh - R > kStashSpan ? mh : R;
         const float f = wm * __builtin_amdgcn_exp2f(rho - lse2);
         const uint32_t wd[4] = {in[b].x, in[b].y, in[b].z, in[b].w};
@@ -1202,7 +1215,8 @@ struct F32Args {
   int max_rows;
   float softcap;
   float inv_softcap;
-  float2* partial;
+  float2* partial;  // [max_rows][n_part], one (max, sum) per 256-entry tile
+  int n_part;       // ceil(V/kTile)
   float* ztgt;
   const float* lse;
   float* G;  // [max_rows][V]
@@ -1243,7 +1257,7 @@ __global__ void __launch_bounds__(kThreads) f32_logits_kernel(F32Args a) {
       if (M != -INFINITY)
         for (int i = 0; i < kThreads / 64; ++i)
           S += red[i].y * __builtin_amdgcn_exp2f(red[i].x - M);
-      a.partial[(int64_t)blockIdx.y * a.max_rows + m] = make_float2(M, S);
+      a.partial[(int64_t)m * a.n_part + blockIdx.y] = make_float2(M, S);
     }
   } else if (vok) {
     float p = __builtin_amdgcn_exp2f(z * kLog2e - a.lse[m] * kLog2e);
@@ -1327,16 +1341,18 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   char* ws = reinterpret_cast<char*>(x.workspace);
   const size_t elt = x.dtype == MDLM_BF16 ? 2 : 4;
 
-  if (want_dh) {
-    const size_t bytes = (size_t)x.n_tokens * x.H * elt;
-    const int64_t n16 = (int64_t)(bytes / 16);
-    const int64_t tail = (int64_t)(bytes % 16);
-    const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n16 + 255) / 256, 4096));
-    if (bytes)
-      zero_kernel<<<grid, 256, 0, stream>>>(reinterpret_cast<uint4*>(x.d_hidden), n16,
-                                            reinterpret_cast<uint8_t*>(x.d_hidden) + n16 * 16,
-                                            tail);
-  }
+  // d_hidden = 0: its own launch here, or (bf16 with the stash) in the
+  // spare blocks of stash_ref_kernel below
+  const size_t dh_bytes = want_dh ? (size_t)x.n_tokens * x.H * elt : 0;
+  const int64_t dh16 = (int64_t)(dh_bytes / 16), dh_tail = (int64_t)(dh_bytes % 16);
+  const unsigned dh_blocks =
+      (unsigned)std::max<int64_t>(1, std::min<int64_t>((dh16 + 255) / 256, 4096));
+  uint8_t* dh_tail_ptr = reinterpret_cast<uint8_t*>(x.d_hidden) + dh16 * 16;
+  auto zero_dh = [&]() {
+    if (dh_bytes)
+      zero_kernel<<<dh_blocks, 256, 0, stream>>>(reinterpret_cast<uint4*>(x.d_hidden), dh16,
+                                                 dh_tail_ptr, dh_tail);
+  };
   if (want_dw && max_rows == 0) {
     // no kernel below runs: dW = 0 here (otherwise dw_kernel writes every
     // entry, zeros included, whatever the device row count)
@@ -1348,6 +1364,7 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
                                           reinterpret_cast<uint8_t*>(x.dW) + n16 * 16, tail);
   }
   if (max_rows == 0) {
+    zero_dh();
     set_float_kernel<<<1, 1, 0, stream>>>(x.loss, 0.f);
     return hipGetLastError();
   }
@@ -1375,6 +1392,7 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     vc = std::min<int64_t>(vc, round_up(x.V, kTile));
   }
   const bool stash = MDLM_STASH && grad && x.dtype == MDLM_BF16 && vc >= x.V;
+  if (!stash) zero_dh();
   bf16_t* G = reinterpret_cast<bf16_t*>(ws + L.G);
   float* rref = reinterpret_cast<float*>(ws + L.rref);
   int* row_flag = reinterpret_cast<int*>(ws + L.flag);
@@ -1396,15 +1414,19 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     la.v_begin = 0;
     la.v_end = x.V;
     la.partial = partial;
+    la.n_part = 2 * L.n_vt;
     la.ztgt = ztgt;
     la.G = G;
     la.ldg = vc;
     la.rref = rref;
     la.row_flag = row_flag;
     if (stash) {
-      stash_ref_kernel<<<(unsigned)std::min<int64_t>((max_rows + 3) / 4, 16384), kThreads, 0,
-                         stream>>>(la.hidden, la.W, x.H, x.V, x.row_idx, x.tgt, x.n_rows,
-                                   (int)max_rows, x.n_tokens, x.softcap, inv_cap, rref, row_flag);
+      const int ref_blocks = (int)std::min<int64_t>((max_rows + 3) / 4, 16384);
+      const unsigned zb = dh_bytes ? dh_blocks : 0;
+      stash_ref_kernel<<<(unsigned)ref_blocks + zb, kThreads, 0, stream>>>(
+          la.hidden, la.W, x.H, x.V, x.row_idx, x.tgt, x.n_rows, (int)max_rows, x.n_tokens,
+          x.softcap, inv_cap, rref, row_flag, ref_blocks,
+          reinterpret_cast<uint4*>(x.d_hidden), dh16, dh_tail_ptr, dh_tail);
       if (x.softcap > 0.f)
         logits_kernel<false, true, true><<<grid, kGemmThreads, 0, stream>>>(la);
       else
@@ -1429,6 +1451,7 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     fa.softcap = x.softcap;
     fa.inv_softcap = inv_cap;
     fa.partial = partial;
+    fa.n_part = L.n_vt;
     fa.ztgt = ztgt;
     dim3 g((unsigned)max_rows, (unsigned)L.n_vt);
     f32_logits_kernel<false><<<g, kThreads, 0, stream>>>(fa);
@@ -1469,7 +1492,8 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   // their dH) and become G only before a dW product, which needs G itself.
   auto scale_rows = [&](int which) {
     const unsigned sgrid = (unsigned)std::min<int64_t>(max_rows, (int64_t)cus * 8);
-    stash_scale_kernel<<<sgrid, kThreads, 0, stream>>>(G, vc, partial, (int)max_rows, lse, ztgt,
+    stash_scale_kernel<<<sgrid, kThreads, 0, stream>>>(G, vc, partial, 2 * L.n_vt,
+                                                       (int)max_rows, lse, ztgt,
                                                        x.tgt, x.w, x.n_rows, x.V, inv_cap,
                                                        rref, row_flag, which);
   };
