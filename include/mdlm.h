@@ -44,6 +44,9 @@
  *   - Host-side argument checks run first.  If one fails the call returns a
  *     non-zero status, enqueues nothing and records a message readable
  *     through mdlm_last_error().  Launch failures return MDLM_EHIP.
+ *   - Output buffers must not overlap the inputs or one another (mdlm_corrupt,
+ *     for one, uses xt's memory for its own bookkeeping before it writes the
+ *     tokens there).
  *   - Device-resident data is not inspected on the host.  Preconditions on it
  *     (cu_seqlens nondecreasing from 0 to n_tokens, token and target ids in
  *     range) are the caller's responsibility; violating them gives

@@ -217,3 +217,59 @@ def test_maximum_stream_sampled(align):
     p_dev = torch.from_numpy(p_all).to(DEV)
     want_w = (1.0 / (p_dev[pos // L] * float(n))).to(torch.float32)
     assert torch.equal(step.w[:m].view(torch.int32), want_w.view(torch.int32))
+
+
+@pytest.mark.parametrize("fill", ["zeros", "minus_one", "int_max", "random_docs", "other_layout"])
+def test_corruption_ignores_stale_xt(fill):
+    """The corruption call keeps per-block document hints in xt before it
+    writes the tokens there; whatever xt holds on entry must not change the
+    result.  xt is pre-filled with values that are out of range, in range but
+    wrong, or the output of an earlier call with another document layout."""
+    rng = np.random.default_rng(8)
+    n = 40 * 4096 + 123
+    cu = WL.lognormal_stream_offsets(12, 296, n).astype(np.int32)
+    x0 = rng.integers(0, 999, size=n).astype(np.int32)
+    nd = cu.shape[0] - 1
+    step = MdlmLossStep(n, max(nd, 41), 64, 64, device=DEV, head_workspace_bytes=0,
+                        want_grad=False)
+    tx0 = torch.from_numpy(x0).to(DEV)
+    if fill == "other_layout":
+        cu_other = np.minimum(np.arange(0, n + 4096, 4096), n).astype(np.int32)
+        cu_other = np.unique(cu_other)
+        B_other = cu_other.shape[0] - 1
+        p_other = torch.empty(B_other, dtype=torch.float64, device=DEV)
+        c_other = torch.empty(B_other, dtype=torch.int32, device=DEV)
+        from uniform_noise_diffusion_amd import binding as Bn
+        Bn.mdlm_corrupt(tx0, torch.from_numpy(cu_other).to(DEV), 1, 1e-3, 0, 999, 1000,
+                        step.xt, step.corrupted, p_other, c_other)
+    else:
+        val = {"zeros": 0, "minus_one": -1, "int_max": 2**31 - 1}.get(fill)
+        if val is None:
+            step.xt.copy_(torch.from_numpy(rng.integers(0, nd, size=n).astype(np.int32)))
+        else:
+            step.xt.fill_(val)
+    p_doc = torch.empty(nd, dtype=torch.float64, device=DEV)
+    counts = torch.empty(nd, dtype=torch.int32, device=DEV)
+    from uniform_noise_diffusion_amd import binding as Bn
+    Bn.mdlm_corrupt(tx0, torch.from_numpy(cu).to(DEV), 99, 1e-3, 0, 999, 1000, step.xt,
+                    step.corrupted, p_doc, counts)
+    torch.cuda.synchronize()
+    xt, corrupted, p, cnt = oracle.corrupt(x0, cu, 99, 1e-3, 0, 999, 1000)
+    assert np.array_equal(host(step.xt), xt)
+    assert np.array_equal(host(step.corrupted), corrupted)
+    assert np.array_equal(host(counts), cnt)
+
+
+@pytest.mark.parametrize("align", [oracle.ALIGNED, oracle.SHIFTED])
+def test_long_documents(align):
+    """Documents spanning more blocks than the per-document hints cover
+    (the blocks past them search for their documents), among enough short
+    ones that the mean length selects the hints."""
+    lengths = ([300_000] + [5] * 1500 + [4096 * 70] + [17] * 500 + [0] * 10
+               + [4096 * 64 + 1] + [3] * 3000)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    rng = np.random.default_rng(9)
+    x0 = rng.integers(0, 999, size=int(cu[-1])).astype(np.int32)
+    for noise in (oracle.NOISE_ABSORB, oracle.NOISE_UNIFORM):
+        _check(x0, cu, 1234 + noise, 0.3, noise, 999, 1000, align)
