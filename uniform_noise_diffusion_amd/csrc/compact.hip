@@ -331,7 +331,7 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
                const float* __restrict__ w_doc, const int32_t* __restrict__ tile_offsets,
                const int32_t* __restrict__ group_sums, int32_t n_groups,
                int32_t* __restrict__ row_idx, int32_t* __restrict__ tgt, float* __restrict__ w,
-               int32_t* __restrict__ n_rows, CodeWeights cwt) {
+               int32_t* __restrict__ n_rows, CodeWeights cwt, bool single) {
   // the code-weight form holds a second weight table in the same LDS budget
   constexpr int kDocs = kCode ? kLdsDocs * 2 / 3 : kLdsDocs;
   __shared__ int32_t s_cu[kDocs + 1];
@@ -349,8 +349,10 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t tile = blockIdx.x;
   const int64_t t0 = tile * kTile;
-  int dlo, dhi;
-  tile_range(tile_lo, tile_hi, n_docs, tile, &dlo, &dhi);
+  // `single`: the whole stream is this one tile, run without the count and
+  // scan passes (every document, offset 0, and the row count written here)
+  int dlo = 0, dhi = n_docs - 1;
+  if (!single) tile_range(tile_lo, tile_hi, n_docs, tile, &dlo, &dhi);
   const int nd = dhi - dlo + 1;
   const bool cached = nd <= kDocs;
   // per-document weight: scale / (p_b N) computed here, or from the table
@@ -374,7 +376,9 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
     return code == 1u ? wm : code == 2u ? wr : cwt.clean_w;
   };
   const int grp = (int)(tile / kGroup);
-  if (wave == 0) {
+  if (single) {
+    if (tid == 0) s_base = 0;
+  } else if (wave == 0) {
     // this tile's offset: its place in its group plus the groups before it
     int b = 0;
     for (int g = lane; g < grp; g += 64) b += group_sums[g];
@@ -518,6 +522,7 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
     // with one buffer, the next round's staging must wait for this copy
     if (kBufs == 1) __syncthreads();
   }
+  if (single && tid == 0) *n_rows = (int32_t)out;
 }
 
 }  // namespace
@@ -551,6 +556,7 @@ struct Launch {
   bool vec;
   hipStream_t stream;
   CodeWeights cwt;  // corrective mixture only
+  bool single;      // one tile, per-document weights needing no totals: scatter alone
 };
 
 // The passes after tile_docs_kernel, for one combination of alignment and
@@ -558,6 +564,19 @@ struct Launch {
 template <bool kShifted, bool kC, bool kE, bool kCode = false>
 void run_passes(const Launch& L, RowMasks<kC, kE> mk) {
   hipStream_t st = L.stream;
+  if (L.single) {
+    if (L.vec)
+      scatter_kernel<kShifted, true, kC, kE, kCode><<<1, kThreads, 0, st>>>(
+          mk.corrupted, mk.eligible, L.x0, L.n, L.cu, L.n_docs, nullptr, nullptr, L.wa.p_doc,
+          L.wa.scale, nullptr, nullptr, nullptr, 0, L.row_idx, L.tgt, L.w, L.n_rows, L.cwt,
+          true);
+    else
+      scatter_kernel<kShifted, false, kC, kE, kCode><<<1, kThreads, 0, st>>>(
+          mk.corrupted, mk.eligible, L.x0, L.n, L.cu, L.n_docs, nullptr, nullptr, L.wa.p_doc,
+          L.wa.scale, nullptr, nullptr, nullptr, 0, L.row_idx, L.tgt, L.w, L.n_rows, L.cwt,
+          true);
+    return;
+  }
   if (L.wa.mode == MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED) {
     const unsigned g = (unsigned)((L.n_docs + kWaves - 1) / kWaves);
     doc_rows_kernel<kShifted, kC, kE><<<g, kThreads, 0, st>>>(mk, L.n, L.cu, L.n_docs,
@@ -575,12 +594,14 @@ void run_passes(const Launch& L, RowMasks<kC, kE> mk) {
     scatter_kernel<kShifted, true, kC, kE, kCode><<<(unsigned)L.tiles, kThreads, 0, st>>>(
         mk.corrupted, mk.eligible, L.x0, L.n, L.cu, L.n_docs, L.tile_lo, L.tile_hi, L.wa.p_doc,
         L.wa.scale, L.w_doc,
-        L.counts, L.group_sums, (int32_t)L.groups, L.row_idx, L.tgt, L.w, L.n_rows, L.cwt);
+        L.counts, L.group_sums, (int32_t)L.groups, L.row_idx, L.tgt, L.w, L.n_rows, L.cwt,
+        false);
   else
     scatter_kernel<kShifted, false, kC, kE, kCode><<<(unsigned)L.tiles, kThreads, 0, st>>>(
         mk.corrupted, mk.eligible, L.x0, L.n, L.cu, L.n_docs, L.tile_lo, L.tile_hi, L.wa.p_doc,
         L.wa.scale, L.w_doc,
-        L.counts, L.group_sums, (int32_t)L.groups, L.row_idx, L.tgt, L.w, L.n_rows, L.cwt);
+        L.counts, L.group_sums, (int32_t)L.groups, L.row_idx, L.tgt, L.w, L.n_rows, L.cwt,
+        false);
 }
 
 }  // namespace
@@ -613,13 +634,18 @@ hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, con
     wa.doc_rows = doc_rows;
     wa.n_examples = n_examples;
   }
-  tile_docs_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(cu, n_docs, n,
-                                                                                tile_lo, tile_hi);
+  // a single tile with per-document weights needs none of the passes before
+  // the scatter
+  const bool single = tiles == 1 && weighting == MDLM_WEIGHT_INV_P;
+  if (!single)
+    tile_docs_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
+        cu, n_docs, n, tile_lo, tile_hi);
   const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)corrupted % 4 == 0) &&
                    ((uintptr_t)eligible % 4 == 0);
   const Launch L{n,        cu,     n_docs, tiles,     groups, counts,    tile_lo,
                  tile_hi,  group_sums, doc_rows, n_examples, w_doc, x0, wa,
-                 row_idx,  tgt,    w,      n_rows,    vec,    stream,    CodeWeights{}};
+                 row_idx,  tgt,    w,      n_rows,    vec,    stream,    CodeWeights{},
+                 single};
   const bool shifted = align == MDLM_SHIFTED;
   const int key = (shifted ? 4 : 0) | (corrupted ? 2 : 0) | (eligible ? 1 : 0);
   switch (key) {
@@ -652,13 +678,16 @@ hipError_t launch_compact_corrective(const uint8_t* codes, const int32_t* x0, in
   int32_t* group_sums = tile_hi + tiles;
   // masked rows: the inverse-p weight with scale 1
   WeightArgs wa{MDLM_WEIGHT_INV_P, 1.0, 0.0, p_doc, n, nullptr, nullptr};
-  tile_docs_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(cu, n_docs, n,
-                                                                                tile_lo, tile_hi);
+  const bool single = tiles == 1;
+  if (!single)
+    tile_docs_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
+        cu, n_docs, n, tile_lo, tile_hi);
   const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)codes % 4 == 0);
   const CodeWeights cwt{codes, noise_wt, (float)(clean_wt / (double)n)};
   const Launch L{n,        cu,     n_docs,  tiles,   groups, counts,  tile_lo,
                  tile_hi,  group_sums, nullptr, nullptr, nullptr, x0,  wa,
-                 row_idx,  tgt,    w,       n_rows,  vec,    stream,  cwt};
+                 row_idx,  tgt,    w,       n_rows,  vec,    stream,  cwt,
+                 single};
   const bool shifted = align == MDLM_SHIFTED;
   // without clean rows the codes are the selection mask (nonzero: corrupted
   // either way); with them every token is a row
