@@ -68,6 +68,8 @@ def _check(x0, cu, seed, eps, noise, mask_id, rand_vocab, align):
     (3, 7, 3000, False),     # documents spanning block boundaries
     (4, 600, 20, True),      # many short documents per block
     (5, 5000, 2, True),      # more documents per 4096-token block than it caches
+    (10, 2000, 2, True),     # one block, more documents than it caches
+    (11, 1024, 4, False),    # one block holding exactly as many documents as it caches
 ])
 def test_corrupt_compact_bit_exact_small(noise, align, seed, n_docs, max_len, empty):
     x0, cu = _case(seed, n_docs, max_len, empty)

@@ -53,20 +53,25 @@ constexpr int64_t kHintMaxMeanLen = 1024;
 // holds, b at the block's second slot (at most kHintBlocks blocks each).  A
 // block reads its two slots before writing any token and checks them
 // against the offsets, so a slot nobody wrote is harmless.
-__global__ void __launch_bounds__(kThreads)
-noise_level_kernel(int32_t n_docs, uint32_t k0, uint32_t k1, double eps,
-                   double* __restrict__ p_doc, int32_t* __restrict__ doc_counts,
-                   const int32_t* __restrict__ cu, int64_t n, int32_t* __restrict__ xt,
-                   bool hints) {
+// p_b = eps + (1 - eps) t_b for document b, t_b from its Philox word.
+__device__ __forceinline__ double doc_p(int b, uint32_t k0, uint32_t k1, double eps) {
 #pragma clang fp contract(off)
-  const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= n_docs) return;
   const uint4 r = philox4x32_10(make_uint4((uint32_t)b, 0u, 0u, kTagDocT), k0, k1);
   const double t = (double)(r.x >> 8) * 0x1p-24;
   // evaluated as (1 - eps), times t, plus eps; each step rounded, no fusion
   const double one_minus_eps = 1.0 - eps;
   const double scaled = one_minus_eps * t;
-  p_doc[b] = eps + scaled;
+  return eps + scaled;
+}
+
+__global__ void __launch_bounds__(kThreads)
+noise_level_kernel(int32_t n_docs, uint32_t k0, uint32_t k1, double eps,
+                   double* __restrict__ p_doc, int32_t* __restrict__ doc_counts,
+                   const int32_t* __restrict__ cu, int64_t n, int32_t* __restrict__ xt,
+                   bool hints) {
+  const int b = blockIdx.x * kThreads + threadIdx.x;
+  if (b >= n_docs) return;
+  p_doc[b] = doc_p(b, k0, k1, eps);
   doc_counts[b] = 0;
   if (!hints) return;
   const int64_t s = cu[b], e = cu[b + 1];
@@ -154,7 +159,8 @@ __global__ void __launch_bounds__(kThreads)
 corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restrict__ cu,
                int32_t n_docs, uint32_t k0, uint32_t k1, const double* __restrict__ p_doc,
                int32_t mask_id, uint32_t rand_vocab, uint32_t thr_mix, int32_t* __restrict__ xt,
-               uint8_t* __restrict__ corrupted, int32_t* __restrict__ doc_counts, bool hints) {
+               uint8_t* __restrict__ corrupted, int32_t* __restrict__ doc_counts, bool hints,
+               double* __restrict__ p_out, double eps) {
   __shared__ int s_dlo, s_dhi;
   __shared__ int32_t s_cu[kLdsDocs + 1];
   __shared__ int s_cnt[kLdsDocs];
@@ -188,7 +194,23 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
   };
   int dlo = 0, nd = 0;
   bool hinted = false;
-  if (hints) {
+  if (p_out) {
+    // The whole stream in this one block, at most kLdsDocs documents: the
+    // noise levels are drawn here (no noise_level_kernel), every document
+    // is in the table, and the counts are cleared before any is added to.
+    for (int b = tid; b < n_docs; b += kThreads) {
+      const double p = doc_p(b, k0, k1, eps);
+      p_out[b] = p;
+      doc_counts[b] = 0;
+      s_cu[b] = cu[b];
+      s_cnt[b] = 0;
+      s_thr[b] = threshold_of(p);
+    }
+    if (tid == 0) s_cu[n_docs] = cu[n_docs];
+    nd = n_docs;
+    hinted = true;
+    __syncthreads();
+  } else if (hints) {
     if (tid == 0) {
       s_dlo = xt[blk0];
       s_dhi = blk1 - blk0 >= 2 ? xt[blk0 + 1] : s_dlo;
@@ -432,7 +454,9 @@ hipError_t launch_corrupt(const int32_t* x0, int64_t n, const int32_t* cu, int32
                           double mixture_prob) {
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const bool hints = n > 0 && n < (int64_t)n_docs * kHintMaxMeanLen;
-  if (n_docs > 0) {
+  // one block over at most kLdsDocs documents: it draws the noise levels too
+  const bool single = n > 0 && n <= kTokPerBlock && n_docs <= kLdsDocs;
+  if (n_docs > 0 && !single) {
     noise_level_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
         n_docs, k0, k1, eps, p_doc, doc_counts, cu, n, xt, hints);
   }
@@ -444,9 +468,11 @@ hipError_t launch_corrupt(const int32_t* x0, int64_t n, const int32_t* cu, int32
     const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)xt % 16 == 0) &&
                      ((uintptr_t)corrupted % 4 == 0);
 #define MDLM_CORRUPT_LAUNCH(M, VEC)                                                       \
-  corrupt_kernel<M, VEC><<<grid, kThreads, 0, stream>>>(x0, n, cu, n_docs, k0, k1, p_doc,  \
+  corrupt_kernel<M, VEC><<<grid, kThreads, 0, stream>>>(x0, n, cu, n_docs, k0, k1,         \
+                                                        single ? nullptr : p_doc,          \
                                                         mask_id, rv, thr_mix, xt, corrupted, \
-                                                        doc_counts, hints)
+                                                        doc_counts, hints && !single,      \
+                                                        single ? p_doc : nullptr, eps)
     if (noise == MDLM_NOISE_UNIFORM) {
       if (vec) MDLM_CORRUPT_LAUNCH(MDLM_NOISE_UNIFORM, true);
       else MDLM_CORRUPT_LAUNCH(MDLM_NOISE_UNIFORM, false);
