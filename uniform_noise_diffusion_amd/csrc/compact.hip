@@ -17,12 +17,14 @@
 //      within the group (in place) and writes the group's total;
 //   4. scatter_kernel: each block adds the totals of the groups before its own
 //      to its offset, re-reads its tile in four 1024-token rounds, ranks each
-//      round's scored tokens with ballots, stages (row, target, weight) in a
-//      double-buffered LDS area and writes them with coalesced stores.
+//      round's scored tokens with ballots, stages (row, target, weight) in
+//      LDS and writes them with coalesced stores.
+// A stream of one tile whose weights need no totals runs pass 4 alone.
 // A tile's document offsets and weights are cached in LDS when it touches at
-// most 1024 documents (682 with the corrective mixture's second table); a wave whose 256 tokens of a round touch at most four
-// documents finds each token's document by comparisons with wave-uniform
-// boundaries instead of a search.
+// most 1024 documents (682 with the corrective mixture's second table); a
+// wave whose 256 tokens of a round touch at most four documents finds each
+// token's document by comparisons with wave-uniform boundaries instead of a
+// search.
 //
 // The corrective mixture's list (same card and row: noise_token_wt and
 // clean_token_wt, no formula given) uses the same passes: the codes are the

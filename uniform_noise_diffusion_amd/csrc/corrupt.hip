@@ -14,11 +14,14 @@
 // Layout: a block covers 4096 tokens in four rounds; in round j thread t owns
 // the 4 consecutive tokens starting at 4 (t + 256 j), exactly the output of one
 // Philox call per stream, and a wave's loads and stores are contiguous.  The
-// documents a block touches are found once by a wave-wide search and their
-// offsets and thresholds cached in LDS; corrupted counts are summed per wave
-// and document before one LDS atomic, and one global atomic per (block,
+// documents a block touches are found once (from hints the noise-level
+// kernel leaves when documents are short, else by a wave-wide search) and
+// their offsets and thresholds cached in LDS; corrupted counts are summed per
+// wave and document before one LDS atomic, and one global atomic per (block,
 // document).  A wave whose 256 tokens share a document takes a branch-free
 // path (the kernel is bound by instruction issue, not by memory, otherwise).
+// A stream of one block needs no noise-level launch: the block draws the
+// noise levels itself.
 #include "mdlm_internal.h"
 
 namespace mdlm {
