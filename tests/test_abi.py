@@ -324,6 +324,9 @@ def test_probe_library_exports_its_header():
     lib = probe.load()
     for n in names:
         assert hasattr(lib, n), n
+    for m in re.finditer(r"\b(mdlm_\w+)\s*\(([^)]*)\)\s*;", text):
+        n_params = len([q for q in m.group(2).split(",") if q.strip()])
+        assert len(getattr(lib, m.group(1)).argtypes) == n_params, m.group(1)
     # invalid launch shapes are refused before anything is enqueued
     assert lib.mdlm_probe_mfma(None, 0, 1, None) != 0
     assert lib.mdlm_probe_mfma(None, 1, 0, None) != 0
@@ -362,3 +365,27 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         B.load()
+
+
+def declared_prototypes():
+    """name -> number of parameters, from the header's prototypes."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(mdlm_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = [p.strip() for p in m.group(2).split(",") if p.strip()]
+        if params == ["void"]:
+            params = []
+        out[m.group(1)] = len(params)
+    return out
+
+
+def test_binding_signatures_match_the_header(lib):
+    """Every ctypes declaration in the binding takes as many arguments as the
+    header's prototype (a miscounted binding would shift every argument)."""
+    protos = declared_prototypes()
+    assert set(protos) == set(B.EXPORTED)
+    for name, n in protos.items():
+        fn = getattr(lib, name)
+        assert fn.argtypes is not None, name
+        assert len(fn.argtypes) == n, (name, len(fn.argtypes), n)
