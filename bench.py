@@ -248,9 +248,10 @@ def variants(inp, dev, n_bw, reps=5):
     """The loss variants on the same workload: the encoder AR term (every-token
     causal rows of mdlm_compact_rows, then the fused head on them), the
     head-weight gradient call, the fused call with a backward that recomputes
-    the logits (a workspace just short of the preferred size), and
-    mdlm_compact_rows' other modes and the corrective mixture at the bandwidth
-    size."""
+    the logits (a workspace just short of the preferred size), the fused call
+    on one eighth of the vocabulary (one GPU's share of a vocabulary-parallel
+    head), and mdlm_compact_rows' other modes and the corrective mixture at
+    the bandwidth size."""
     import torch
     from uniform_noise_diffusion_amd import binding as B
     from uniform_noise_diffusion_amd.pipeline import MdlmLossStep
@@ -312,7 +313,31 @@ def variants(inp, dev, n_bw, reps=5):
         dw_gemm_tflops=float((2 * rows * HV).sum() / (np.sum(t_dw) - np.sum(t_plain)) / 1e12),
         what="mdlm_fused_head_ce_fwd_bwd_dw (loss, d_hidden and dW fp32 [V, H]); the dW "
              "product's rate is 2 M H V over the time the call adds")
-    del step, ws, dW, ws_rc
+    # one GPU's share of a vocabulary-parallel head over 8 GPUs: the fused
+    # call on the first V/8 rows of W, targets folded into the shard (the
+    # all-reduces of the row statistics and of d_hidden that the sharded
+    # head adds are not included)
+    V8 = wl.V // 8
+    W8 = W[:V8]
+    ws8 = torch.empty(B.mdlm_head_ce_workspace_bytes(wl.n_tokens, wl.H, V8, B.MDLM_BF16),
+                      dtype=torch.uint8, device=dev)
+    t8, rows8 = [], []
+    for seed in range(reps):
+        step.corrupt(x0, cu, seed, wl.eps, wl.noise, wl.mask_id, wl.rand_vocab)
+        step.compact(x0, cu, wl.align)
+        rows8.append(int(step.n_rows.item()))
+        tg8 = torch.remainder(step.tgt, V8)
+        t8.append(_timed(lambda: B.mdlm_fused_head_ce_fwd_bwd(
+            h, W8, step.row_idx, tg8, step.w, step.n_rows, wl.n_tokens, wl.softcap, loss, None,
+            step.d_hidden, ws8), 2))
+    rows8 = np.array(rows8, dtype=np.float64)
+    out["head_vocab_shard_of_8"] = dict(
+        V_shard=V8, seeds=f"0..{reps - 1}", mean_rows=float(rows8.mean()),
+        ms_per_call=float(np.mean(t8)) * 1e3,
+        algorithmic_tflops=float((4 * rows8 * wl.H * V8).sum() / np.sum(t8) / 1e12),
+        what="mdlm_fused_head_ce_fwd_bwd on W[:V/8] (one GPU's share of a vocabulary-parallel "
+             "head over 8 GPUs); the collectives of the sharded head are not included")
+    del step, ws, dW, ws_rc, ws8
     if n_bw:
         L = 4096
         n = n_bw // L * L
@@ -397,8 +422,15 @@ def cpu_baseline(inp, mean_rows, seconds):
         cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or os.cpu_count()
     except Exception:  # noqa: BLE001
         cores = os.cpu_count()
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return dict(value=wl.n_tokens / est_step, unit="tokens/s", cores=cores, kind="oracle",
-                seconds_per_step=est_step,
+                host_cpus=os.cpu_count(), cpu_model=cpu_model, seconds_per_step=est_step,
                 sample=(f"oracle corrupt+compact over all {wl.n_tokens} tokens ({t_cc:.2f} s); "
                         f"fp64 head+CE fwd+bwd timed on {', '.join(str(x) for x, _ in samples)} "
                         f"scored rows ({spent:.1f} s in all), per-call cost {a:.2f} s + "
