@@ -377,6 +377,17 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
     // this wave's blocks that hold scored rows (a prefix of its kNJ)
     const int nv = min(kTile, n_rows - m0);
     const int kj = max(0, (nv - 32 * wb + kRowStride - 1) / kRowStride);
+    // the epilogue's per-row inputs, loaded before the K loop so that they
+    // arrive during it (the loop's waits keep later loads from moving up)
+    int tg_pre[kNJ];
+    float ref_pre[kNJ];
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) {
+      const int m = m0 + 32 * wb + kRowStride * j + (lane & 31);
+      const bool mv = m < n_rows;
+      tg_pre[j] = mv ? a.tgt[m] : -1;
+      ref_pre[j] = kStash && mv ? a.rref[m] : 0.f;
+    }
     // the K loop, specialised on that count (the waves of a workgroup run
     // the same loads and barriers whatever their count)
     auto kloop = [&](auto nj_tag) __attribute__((always_inline)) {
@@ -444,7 +455,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
         if (j >= kj) break;  // (no scored row in this block or the next)
         const int m = m0 + 32 * wb + kRowStride * j + (lane & 31);
         const bool mvalid = m < n_rows;
-        const int tg = mvalid ? a.tgt[m] : -1;
+        const int tg = tg_pre[j];
         const int dt = tg - vl;
         const bool holds_tgt = (unsigned)dt < 128u && (dt & 4) == 0;
         if (!kGrad) {
@@ -474,7 +485,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
           // else rho = m_h and the row is flagged
           float fs = 1.f;
           if (kStash) {
-            const float R = mvalid ? a.rref[m] : 0.f;
+            const float R = ref_pre[j];
             const bool near = !(mx - R > kStashSpan);
             if (!near && mvalid && lane < 32) a.row_flag[m] = 1;
             fs = mx == -INFINITY ? 0.f : near ? __builtin_amdgcn_exp2f(mx - R) : 1.f;
