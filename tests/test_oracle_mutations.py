@@ -7,7 +7,9 @@ level's affine map and its 24-bit scale, the shifted row index, the 1/p
 weight, the softcap derivative, the target column, the gradient's sign, a
 log-sum-exp that misses a vocabulary chunk, and in the variants the
 example-mean divisor, the eligibility position, the mean's denominator and
-the weight in the head-weight gradient.
+the weight in the head-weight gradient, and in the corrective mixture the
+masked and replaced weights swapped, the replace decision inverted or drawn
+from the corruption word, and the clean weight taken over the clean tokens.
 """
 
 import math
@@ -23,6 +25,7 @@ import test_oracle_noise as TN
 import test_oracle_philox as TP
 from test_oracle_philox import rocrand_ref  # noqa: F401  (the fixture)
 import test_oracle_variants as TV
+import test_oracle_corrective as TC
 
 _MODULES = (M, oracle, TL, TN, TP, TV)
 
@@ -209,3 +212,52 @@ def test_head_weight_gradient_without_row_weights(monkeypatch):
                     softcap, chunk)
     _patch(monkeypatch, "head_ce_weight_grad", bad)
     _fails(TV.test_head_weight_gradient_finite_differences, 0.0)
+
+
+# ---- corrective mixture ---------------------------------------------------
+
+
+def _patch_c(monkeypatch, name, fn):
+    for mod in (M, oracle, TC):
+        if hasattr(mod, name):
+            monkeypatch.setattr(mod, name, fn)
+
+
+def test_corrective_weights_swapped(monkeypatch):
+    orig = M.compact_corrective
+
+    def bad(codes, x0, cu_seqlens, p_doc, align, a, c):
+        codes = np.asarray(codes)
+        swapped = np.where(codes == M.CODE_MASKED, M.CODE_REPLACED,
+                           np.where(codes == M.CODE_REPLACED, M.CODE_MASKED, codes))
+        return orig(swapped.astype(np.uint8), x0, cu_seqlens, p_doc, align, a, c)
+    _patch_c(monkeypatch, "compact_corrective", bad)
+    _fails(TC.test_row_list_brute_force, M.ALIGNED, 0.5, 0.0)
+
+
+def test_mixture_decision_inverted(monkeypatch):
+    orig = M.corrupt_mixture
+
+    def bad(x0, cu_seqlens, seed, eps, mixture_prob, mask_id, rand_vocab):
+        return orig(x0, cu_seqlens, seed, eps, 1.0 - mixture_prob, mask_id, rand_vocab)
+    _patch_c(monkeypatch, "corrupt_mixture", bad)
+    _fails(TC.test_mixture_zero_is_absorbing_noise)
+
+
+def test_mixture_decision_from_the_corruption_word(monkeypatch):
+    monkeypatch.setattr(M, "TAG_MIX", M.TAG_BERNOULLI)
+    _fails(TC.test_mixture_frequency_and_independence, 0.1)
+
+
+def test_clean_weight_over_clean_tokens(monkeypatch):
+    orig = M.compact_corrective
+
+    def bad(codes, x0, cu_seqlens, p_doc, align, a, c):
+        rows, tgt, w = orig(codes, x0, cu_seqlens, p_doc, align, a, c)
+        codes = np.asarray(codes)
+        g = rows + 1 if align == M.SHIFTED else rows
+        clean = codes[g] == M.CODE_CLEAN
+        n, n_clean = codes.shape[0], max(int((codes == M.CODE_CLEAN).sum()), 1)
+        return rows, tgt, np.where(clean, w * n / n_clean, w)
+    _patch_c(monkeypatch, "compact_corrective", bad)
+    _fails(TC.test_row_list_brute_force, M.ALIGNED, 2.0, 0.25)
