@@ -275,3 +275,104 @@ def test_long_documents(align):
     x0 = rng.integers(0, 999, size=int(cu[-1])).astype(np.int32)
     for noise in (oracle.NOISE_ABSORB, oracle.NOISE_UNIFORM):
         _check(x0, cu, 1234 + noise, 0.3, noise, 999, 1000, align)
+
+
+def _offset_view(n, dtype, fill=None):
+    """A device tensor of n elements that starts one element into its
+    allocation, so that its address is not 16-byte aligned."""
+    base = torch.empty(n + 1, dtype=dtype, device=DEV)
+    if fill is not None:
+        base.fill_(fill)
+    return base[1:]
+
+
+@pytest.mark.parametrize("noise", [oracle.NOISE_ABSORB, oracle.NOISE_UNIFORM])
+@pytest.mark.parametrize("align", [oracle.ALIGNED, oracle.SHIFTED])
+@pytest.mark.parametrize("mean_len", [30, 5000])
+def test_unaligned_buffers(noise, align, mean_len):
+    """Token, mask and row buffers that are not 16-byte (the mask: not
+    4-byte) aligned take the kernels' scalar paths; results as the oracle's."""
+    from uniform_noise_diffusion_amd import binding as Bn
+    rng = np.random.default_rng(13 + mean_len)
+    n = 3 * 4096 + 777
+    cu = WL.lognormal_stream_offsets(14 + mean_len, mean_len, n).astype(np.int32)
+    nd = cu.shape[0] - 1
+    x0 = rng.integers(0, 999, size=n).astype(np.int32)
+    tx0 = _offset_view(n, torch.int32)
+    tx0.copy_(torch.from_numpy(x0))
+    tcu = torch.from_numpy(cu).to(DEV)
+    xt = _offset_view(n, torch.int32)
+    corr = _offset_view(n, torch.uint8)
+    p_doc = torch.empty(nd, dtype=torch.float64, device=DEV)
+    counts = torch.empty(nd, dtype=torch.int32, device=DEV)
+    Bn.mdlm_corrupt(tx0, tcu, 321, 1e-3, noise, 999, 1000, xt, corr, p_doc, counts)
+    rows = _offset_view(n, torch.int32)
+    tgt = _offset_view(n, torch.int32)
+    w = _offset_view(n, torch.float32)
+    n_rows = torch.empty(1, dtype=torch.int32, device=DEV)
+    ws = torch.empty(Bn.mdlm_compact_workspace_bytes(n), dtype=torch.uint8, device=DEV)
+    Bn.mdlm_compact_masked(corr, tx0, tcu, p_doc, align, rows, tgt, w, n_rows, ws)
+    torch.cuda.synchronize()
+    e_xt, e_corr, e_p, e_cnt = oracle.corrupt(x0, cu, 321, 1e-3, noise, 999, 1000)
+    assert np.array_equal(host(xt), e_xt)
+    assert np.array_equal(host(corr), e_corr)
+    assert np.array_equal(host(counts), e_cnt)
+    e_rows, e_tgt, e_w = oracle.compact(e_corr, x0, cu, e_p, align)
+    m = int(host(n_rows)[0])
+    assert m == e_rows.shape[0]
+    assert np.array_equal(host(rows)[:m], e_rows)
+    assert np.array_equal(host(tgt)[:m], e_tgt)
+    assert np.array_equal(host(w)[:m].view(np.uint32), e_w.astype(np.float32).view(np.uint32))
+    # the corrective pair on the same unaligned buffers
+    Bn.mdlm_corrupt_mixture(tx0, tcu, 322, 1e-3, 0.4, 999, 1000, xt, corr, p_doc, counts)
+    Bn.mdlm_compact_corrective(corr, tx0, tcu, p_doc, align, 0.5, 0.2, rows, tgt, w, n_rows, ws)
+    torch.cuda.synchronize()
+    e_xt, e_codes, e_p, e_cnt = oracle.corrupt_mixture(x0, cu, 322, 1e-3, 0.4, 999, 1000)
+    assert np.array_equal(host(xt), e_xt)
+    assert np.array_equal(host(corr), e_codes)
+    e_rows, e_tgt, e_w = oracle.compact_corrective(e_codes, x0, cu, e_p, align, 0.5, 0.2)
+    m = int(host(n_rows)[0])
+    assert m == e_rows.shape[0]
+    assert np.array_equal(host(rows)[:m], e_rows)
+    assert np.array_equal(host(tgt)[:m], e_tgt)
+    assert np.array_equal(host(w)[:m].view(np.uint32), e_w.astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("weighting", [oracle.WEIGHT_MEAN, oracle.WEIGHT_EXAMPLE_MEAN_CLIPPED])
+def test_unaligned_row_masks(weighting):
+    """mdlm_compact_rows with corruption and eligibility masks that are not
+    4-byte aligned (the per-document count of the example mean included)."""
+    from uniform_noise_diffusion_amd import binding as Bn
+    rng = np.random.default_rng(17)
+    n = 2 * 4096 + 333
+    cu = WL.lognormal_stream_offsets(18, 200, n).astype(np.int32)
+    nd = cu.shape[0] - 1
+    x0 = rng.integers(0, 999, size=n).astype(np.int32)
+    corr_h = (rng.random(n) < 0.5).astype(np.uint8)
+    elig_h = (rng.random(n) < 0.8).astype(np.uint8)
+    p_h = rng.uniform(0.01, 1.0, size=nd)
+    tx0 = torch.from_numpy(x0).to(DEV)
+    tcu = torch.from_numpy(cu).to(DEV)
+    corr = _offset_view(n, torch.uint8)
+    corr.copy_(torch.from_numpy(corr_h))
+    elig = _offset_view(n, torch.uint8)
+    elig.copy_(torch.from_numpy(elig_h))
+    p_doc = torch.from_numpy(p_h).to(DEV)
+    rows = torch.empty(n, dtype=torch.int32, device=DEV)
+    tgt = torch.empty(n, dtype=torch.int32, device=DEV)
+    w = torch.empty(n, dtype=torch.float32, device=DEV)
+    n_rows = torch.empty(1, dtype=torch.int32, device=DEV)
+    ws = torch.empty(Bn.mdlm_compact_rows_workspace_bytes(n, nd, weighting), dtype=torch.uint8,
+                     device=DEV)
+    for align in (oracle.ALIGNED, oracle.SHIFTED):
+        Bn.mdlm_compact_rows(corr, elig, tx0, tcu, p_doc, align, weighting, 1.5, 4.0, rows, tgt,
+                             w, n_rows, ws)
+        torch.cuda.synchronize()
+        e_rows, e_tgt, e_w = oracle.compact_rows(x0, cu, align, corr_h, elig_h, p_h, weighting,
+                                                 1.5, 4.0)
+        m = int(host(n_rows)[0])
+        assert m == e_rows.shape[0]
+        assert np.array_equal(host(rows)[:m], e_rows)
+        assert np.array_equal(host(tgt)[:m], e_tgt)
+        assert np.array_equal(host(w)[:m].view(np.uint32),
+                              e_w.astype(np.float32).view(np.uint32))
