@@ -41,6 +41,10 @@
  *   - Every call is asynchronous on `stream` (a hipStream_t passed as void*;
  *     NULL means the default stream).  Outputs are valid once the stream
  *     reaches the call.  No call synchronises with the host.
+ *   - Calls only launch kernels (no memset, no allocation), so a sequence of
+ *     them may be captured in a HIP graph; a replay reuses the host arguments
+ *     (seed, sizes, weights) given at capture, and the device data as it is
+ *     at replay.
  *   - Host-side argument checks run first.  If one fails the call returns a
  *     non-zero status, enqueues nothing and records a message readable
  *     through mdlm_last_error().  Launch failures return MDLM_EHIP.
