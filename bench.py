@@ -35,6 +35,7 @@ import numpy as np  # noqa: E402
 
 METRIC = "corrupted-LM loss fwd+bwd tokens/s at V=126,464; % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_VALU_TFLOPS = 157.3   # the fp32 path runs on the vector ALUs
 PEAK_HBM_GBS = 8000.0
 
 
@@ -475,14 +476,17 @@ def main():
     value = wl.n_tokens * K / total_s
     log(f"steps: {r['total_ms'] / K:.3f} ms/step, head+CE {head_s.mean() * 1e3:.3f} ms/call, "
         f"mean scored rows {rows.mean():.0f}, {achieved:.1f} TFLOP/s")
+    # the counters' bytes belong to the workload they were taken on
     traffic = None
     if args.traffic_json and os.path.exists(args.traffic_json):
         with open(args.traffic_json) as f:
             t = json.load(f)
-        if t.get("current"):
+        if t.get("current") and t.get("workload") == wl.name:
             traffic = t.get("bytes_per_call")
-    roofline = dict(bound="mfma", achieved=achieved, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / PEAK_BF16_TFLOPS, traffic=traffic,
+    bf16 = wl.dtype == "bf16"
+    peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_VALU_TFLOPS
+    roofline = dict(bound="mfma" if bf16 else "alu", achieved=achieved, peak=peak,
+                    unit="TFLOP/s", frac=achieved / peak, traffic=traffic,
                     kernel="mdlm_fused_head_ce_fwd_bwd",
                     ms_per_call=float(head_s.mean() * 1e3),
                     algorithmic_flops_per_call=float(flops_alg.mean()))
@@ -500,7 +504,8 @@ def main():
         log("measuring achievable peaks")
         ach = achievable(dev, (wl.V, wl.H, int(round(rows.mean()))))
         out["achievable"] = ach
-        roofline["frac_of_achievable"] = achieved / ach["mfma_bf16_tflops"]
+        if bf16:
+            roofline["frac_of_achievable"] = achieved / ach["mfma_bf16_tflops"]
     if args.bandwidth_tokens:
         log("timing corruption/compaction bandwidth")
         out["corrupt_compact_hbm"] = bandwidth(args.bandwidth_tokens, dev)
