@@ -1036,13 +1036,35 @@ stash_ref_kernel(const bf16_t* __restrict__ hidden, const bf16_t* __restrict__ W
 // left out cost one flag read), 16-byte groups of eight entries per thread.
 constexpr int kScaleSeg = kThreads * 8;
 
+// The loss: a fixed-order sum of the merge kernel's block sums by one block
+// of kThreads threads (strided per thread, then a tree), whichever kernel
+// runs it.
+__device__ __forceinline__ void sum_block_sums(const double* __restrict__ block_sums, int n,
+                                               float* __restrict__ loss, double* s) {
+  double t = 0.0;
+  for (int i = threadIdx.x; i < n; i += kThreads) t += block_sums[i];
+  s[threadIdx.x] = t;
+  __syncthreads();
+  for (int off = kThreads / 2; off > 0; off >>= 1) {
+    if (threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *loss = (float)s[0];
+}
+
 __global__ void __launch_bounds__(kThreads)
 stash_scale_kernel(bf16_t* __restrict__ G, int64_t ldg, const float2* __restrict__ partial,
                    int n_part, int max_rows, const float* __restrict__ lse, const float* __restrict__ ztgt,
                    const int32_t* __restrict__ tgt, const float* __restrict__ w,
                    const int32_t* __restrict__ n_rows_ptr, int V, float inv_softcap,
                    const float* __restrict__ rref, const int* __restrict__ row_flag,
-                   int which) {
+                   int which, const double* __restrict__ block_sums, int n_bsum,
+                   float* __restrict__ loss) {
+  // (with block_sums) block 0 also sums the loss, saving its own launch
+  if (block_sums && blockIdx.x == 0) {
+    __shared__ double s[kThreads];
+    sum_block_sums(block_sums, n_bsum, loss, s);
+  }
   const int n_rows = min(*n_rows_ptr, max_rows);
   for (int m = blockIdx.x; m < n_rows; m += gridDim.x) {
     if (which >= 0 && row_flag[m] != which) continue;
@@ -1098,15 +1120,7 @@ stash_scale_kernel(bf16_t* __restrict__ G, int64_t ldg, const float2* __restrict
 __global__ void __launch_bounds__(kThreads)
 loss_kernel(const double* __restrict__ block_sums, int n, float* __restrict__ loss) {
   __shared__ double s[kThreads];
-  double t = 0.0;
-  for (int i = threadIdx.x; i < n; i += kThreads) t += block_sums[i];
-  s[threadIdx.x] = t;
-  __syncthreads();
-  for (int off = kThreads / 2; off > 0; off >>= 1) {
-    if (threadIdx.x < off) s[threadIdx.x] += s[threadIdx.x + off];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) *loss = (float)s[0];
+  sum_block_sums(block_sums, n, loss, s);
 }
 
 __global__ void set_float_kernel(float* p, float v) { *p = v; }
@@ -1471,7 +1485,8 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   const int n_part = x.dtype == MDLM_BF16 ? 2 * L.n_vt : L.n_vt;
   merge_kernel<<<L.n_bsum, kThreads, 0, stream>>>(partial, n_part, (int)max_rows, ztgt, x.tgt,
                                                   x.V, x.w, x.n_rows, lse, x.row_ce, bsum);
-  loss_kernel<<<1, kThreads, 0, stream>>>(bsum, L.n_bsum, x.loss);
+  // with the stash the loss is summed by the first scaling launch below
+  if (!stash) loss_kernel<<<1, kThreads, 0, stream>>>(bsum, L.n_bsum, x.loss);
   if (!grad) return hipGetLastError();
 
   if (x.dtype == MDLM_F32) {
@@ -1501,14 +1516,13 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   // With the stash: the rows the forward pass flagged become G here; the
   // others keep the stash through the dH product (scatter_kernel finishes
   // their dH) and become G only before a dW product, which needs G itself.
-  auto scale_rows = [&](int which) {
+  auto scale_rows = [&](int which, bool with_loss) {
     const unsigned sgrid = (unsigned)std::min<int64_t>(max_rows, (int64_t)cus * 8);
-    stash_scale_kernel<<<sgrid, kThreads, 0, stream>>>(G, vc, partial, 2 * L.n_vt,
-                                                       (int)max_rows, lse, ztgt,
-                                                       x.tgt, x.w, x.n_rows, x.V, inv_cap,
-                                                       rref, row_flag, which);
+    stash_scale_kernel<<<sgrid, kThreads, 0, stream>>>(
+        G, vc, partial, 2 * L.n_vt, (int)max_rows, lse, ztgt, x.tgt, x.w, x.n_rows, x.V,
+        inv_cap, rref, row_flag, which, with_loss ? bsum : nullptr, L.n_bsum, x.loss);
   };
-  if (stash) scale_rows(want_dh ? 1 : -1);
+  if (stash) scale_rows(want_dh ? 1 : -1, true);
 
   LogitsArgs la{};
   la.W = reinterpret_cast<const bf16_t*>(x.W);
@@ -1583,7 +1597,7 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
       scatter(fix);  // (reads the stashed target entries: before they are scaled)
     }
     if (want_dw) {
-      if (want_dh) scale_rows(0);
+      if (want_dh) scale_rows(0, false);
       wa.v_begin = 0;
       wa.v_end = x.V;
       dw_kernel<<<grid, kGemmThreads, 0, stream>>>(wa);
