@@ -23,7 +23,8 @@
 //      more than kStashSpan above it, which flags the row.
 //   2. merge_kernel: per row, combine the partials into the log-sum-exp and
 //      CE; per-block sums of w * CE in fp64.
-//   3. loss_kernel: fixed-order sum of the block sums -> loss.
+//   3. fixed-order sum of the block sums -> loss: by block 0 of the first
+//      stash_scale_kernel launch when the stash is used, else by loss_kernel.
 //   4. (gradient) G = w (softmax - onehot) zhat' as bf16, either from the
 //      stash (stash_scale_kernel multiplies by w 2^(rho - lse) and rewrites
 //      the target entries, for the flagged rows only unless dW is wanted) or,
