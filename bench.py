@@ -8,8 +8,8 @@ step draws fresh noise (Philox seed = step index), as a training loop would.
 
 Default workload: one sequence of 4,096 tokens, H = 4,096, V = 126,464, bf16
 inputs with fp32 accumulation, absorbing noise (eps = 1e-3), aligned logits
-(LLaDA-8B-MDLM-LoRA card, Training table: batch of sequences of at most 4,096
-tokens, bf16 base weights).  Inputs are seeded synthetic data resident in HBM
+(LLaDA-8B-MDLM-LoRA card, Training table: a batch holds sequences no longer
+than 4,096 tokens; the base weights are bf16).  Inputs are seeded synthetic data resident in HBM
 before timing starts.
 
 Prints ONE JSON line: tokens/s of whole steps, the roofline of the fused
@@ -57,6 +57,9 @@ def parse():
     p.add_argument("--no-achievable", action="store_true",
                    help="skip the achievable-peak probes (copy, MFMA loop, library GEMM)")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="skip timing the other bf16 workloads (varlen, packed, canvas)")
+    p.add_argument("--other-steps", type=int, default=10)
     p.add_argument("--bandwidth-tokens", type=int, default=1 << 27,
                    help="tokens of the corruption/compaction bandwidth run (0 = skip)")
     p.add_argument("--calibrate-copy", type=int, default=0,
@@ -67,6 +70,14 @@ def parse():
                                                           "head_ce_traffic.json"),
                    help="measured HBM traffic of the fused call, if current")
     return p.parse_args()
+
+
+def head_source_sha256():
+    """sha256 of the fused call's kernel source, to tie counter results to it."""
+    import hashlib
+    path = os.path.join(ROOT, "uniform_noise_diffusion_amd", "csrc", "head_ce.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def to_device(inp, dev):
@@ -92,20 +103,22 @@ def gpu_steps(args, inp, dev):
     step = MdlmLossStep(wl.n_tokens, wl.n_docs, wl.H, wl.V, dtype=dtype, device=dev)
 
     def one(seed, ev=None):
+        # (events on torch's current stream, which the calls are launched on)
+        if ev is not None:
+            ev[0].record()
         step.corrupt(x0, cu, seed, wl.eps, wl.noise, wl.mask_id, wl.rand_vocab)
         step.compact(x0, cu, align)
         if ev is not None:
-            ev[0].record()
+            ev[1].record()
         step.head_ce(h, W, wl.softcap, row_ce=False)
         if ev is not None:
-            ev[1].record()
+            ev[2].record()
 
     for i in range(args.warmup):
         one(1_000_000 + i)
     torch.cuda.synchronize()
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -117,7 +130,8 @@ def gpu_steps(args, inp, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    head_ms = [a.elapsed_time(b) for a, b in evs]
+    head_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
     losses = []
     rows = []
     # scored-row counts of the timed seeds, recomputed after the timed region
@@ -130,7 +144,8 @@ def gpu_steps(args, inp, dev):
     losses.append(float(step.loss.item()))
     if not all(np.isfinite(losses)):
         raise RuntimeError("non-finite loss")
-    return dict(total_ms=total_ms, wall_s=wall, head_ms=head_ms, rows=rows, align=align)
+    return dict(total_ms=total_ms, wall_s=wall, head_ms=head_ms, step_ms=step_ms, rows=rows,
+                align=align)
 
 
 def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
@@ -227,6 +242,21 @@ def achievable(dev, gemm_shape=None):
         res["library_gemm_tflops"] = 2.0 * V * H * M * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
         res["library_gemm"] = (f"torch.matmul (hipBLASLt) bf16 [{V} x {H}] x [{H} x {M}], the "
                                "forward logits' shape, output written; context, not a target")
+        del A, B, C
+        # the library's rate on a large square product, where it is at its best
+        S = 8192
+        A = torch.randn(S, S, device=dev).to(torch.bfloat16)
+        B = torch.randn(S, S, device=dev).to(torch.bfloat16)
+        C = A @ B
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            C = A @ B
+        e1.record()
+        torch.cuda.synchronize()
+        res["library_gemm_square_tflops"] = 2.0 * S ** 3 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+        res["library_gemm_square"] = (f"torch.matmul (hipBLASLt) bf16 {S} x {S} x {S}; context "
+                                      "for what a library GEMM reaches on this GPU")
         del A, B, C
     return res
 
@@ -381,43 +411,71 @@ def variants(inp, dev, n_bw, reps=5):
     return out
 
 
-def cpu_baseline(inp, mean_rows, seconds):
-    """The fp64 oracle, as it stands, on a bounded sample of the workload.
+def other_workloads(dev, steps, warmup):
+    """The other bf16 workloads, each timed like the default one (whole steps
+    on one stream, Philox seed = step index): llada8b-varlen-12docs,
+    nemotron3b-packed-16384 with aligned and shifted logits, and
+    diffusiongemma-canvas-8x1024.  For each: ms per step (aggregate and
+    median), tokens/s, and the fused call's 4 M H V rate against the bf16
+    peak."""
+    import torch
+    import workloads as WL
+    out = {}
+    inp = None
+    for k, align in ((3, None), (4, 0), (4, 1), (5, None)):
+        wl = WL.make_workload(k)
+        log(f"other workload {wl.name} (align {wl.align if align is None else align})")
+        if inp is None or inp.wl.index != k:
+            inp = None
+            torch.cuda.empty_cache()
+            inp = WL.generate(wl)
+        a = argparse.Namespace(steps=steps, warmup=warmup, align=align)
+        r = gpu_steps(a, inp, dev)
+        rows = np.array(r["rows"], dtype=np.float64)
+        head_s = np.array(r["head_ms"]) * 1e-3
+        fl = 4.0 * rows * wl.H * wl.V
+        tf = fl.sum() / head_s.sum() / 1e12
+        name = wl.name + ("-shifted" if r["align"] == 1 and wl.align == 0 else "")
+        out[name] = dict(
+            n_tokens=wl.n_tokens, H=wl.H, V=wl.V, softcap=wl.softcap,
+            noise="absorb" if wl.noise == 0 else "uniform",
+            align="aligned" if r["align"] == 0 else "shifted", steps=steps,
+            mean_scored_rows=float(rows.mean()), ms_per_step=r["total_ms"] / steps,
+            median_ms_per_step=float(np.median(r["step_ms"])),
+            tokens_per_s=wl.n_tokens * steps / (r["total_ms"] * 1e-3),
+            head_ms_per_call=float(head_s.mean() * 1e3), head_tflops=float(tf),
+            head_frac_of_bf16_peak=float(tf / PEAK_BF16_TFLOPS))
+    del inp
+    torch.cuda.empty_cache()
+    return out
 
-    The oracle's head + CE call has a fixed cost per call (it converts every
-    chunk of W to fp64) plus a cost per scored row, so it is timed on a
-    doubling number of rows until a call takes about half the budget, and the
-    last two timings give the line a + b * rows that is evaluated at the
-    workload's mean scored-row count."""
+
+def cpu_baseline(inp, seconds, align):
+    """The fp64 oracle, as it stands, timed over whole steps of the workload:
+    corruption, the row list and the head + CE forward and gradient over
+    every scored row, for Philox seeds 0, 1, ... (the seeds of the timed GPU
+    steps) until about `seconds` have been spent, at least one step.  The
+    rate is the workload's tokens over the median step time."""
     import oracle
     wl = inp.wl
-    t0 = time.perf_counter()
-    xt, corrupted, p, _ = oracle.corrupt(inp.x0, inp.cu_seqlens, 0, wl.eps, wl.noise,
-                                         wl.mask_id, wl.rand_vocab)
-    rows, tgt, w = oracle.compact(corrupted, inp.x0, inp.cu_seqlens, p, wl.align)
-    t_cc = time.perf_counter() - t0
-    m_all = rows.shape[0]
-    samples = []
-    s = 8
+    steps = []
     spent = 0.0
+    seed = 0
     while True:
-        s = min(s, m_all)
+        t0 = time.perf_counter()
+        xt, corrupted, p, _ = oracle.corrupt(inp.x0, inp.cu_seqlens, seed, wl.eps, wl.noise,
+                                             wl.mask_id, wl.rand_vocab)
+        rows, tgt, w = oracle.compact(corrupted, inp.x0, inp.cu_seqlens, p, align)
         t1 = time.perf_counter()
-        oracle.head_ce(inp.hidden, inp.W, rows[:s], tgt[:s], w[:s], wl.softcap)
-        dt = time.perf_counter() - t1
-        spent += dt
-        samples.append((s, dt))
-        if s >= m_all or dt > seconds / 2 or spent > seconds:
+        oracle.head_ce(inp.hidden, inp.W, rows, tgt, w, wl.softcap)
+        t2 = time.perf_counter()
+        steps.append(dict(seed=seed, rows=int(rows.shape[0]), corrupt_compact_s=t1 - t0,
+                          head_s=t2 - t1, step_s=t2 - t0))
+        spent += t2 - t0
+        seed += 1
+        if spent >= seconds or seed >= 20:
             break
-        s *= 2
-    if len(samples) >= 2:
-        (s1, d1), (s2, d2) = samples[-2], samples[-1]
-        b = max((d2 - d1) / (s2 - s1), 0.0)
-        a = max(d2 - b * s2, 0.0)
-    else:
-        (s2, d2), = samples
-        a, b = 0.0, d2 / s2
-    est_step = t_cc + a + b * mean_rows
+    med = float(np.median([x["step_s"] for x in steps]))
     try:
         from threadpoolctl import threadpool_info
         cores = max(int(i.get("num_threads", 1)) for i in threadpool_info()) or os.cpu_count()
@@ -430,13 +488,15 @@ def cpu_baseline(inp, mean_rows, seconds):
                               if ln.startswith("model name")), None)
     except OSError:
         pass
-    return dict(value=wl.n_tokens / est_step, unit="tokens/s", cores=cores, kind="oracle",
-                host_cpus=os.cpu_count(), cpu_model=cpu_model, seconds_per_step=est_step,
-                sample=(f"oracle corrupt+compact over all {wl.n_tokens} tokens ({t_cc:.2f} s); "
-                        f"fp64 head+CE fwd+bwd timed on {', '.join(str(x) for x, _ in samples)} "
-                        f"scored rows ({spent:.1f} s in all), per-call cost {a:.2f} s + "
-                        f"{b * 1e3:.1f} ms per row, evaluated at the {mean_rows:.0f} scored "
-                        f"rows of a mean step"))
+    return dict(value=wl.n_tokens / med, unit="tokens/s", cores=cores, kind="oracle",
+                host_cpus=os.cpu_count(), cpu_model=cpu_model, seconds_per_step=med,
+                steps=steps,
+                sample=(f"{len(steps)} whole oracle steps of {wl.name} (Philox seeds "
+                        f"0..{len(steps) - 1}): fp64 corruption, row list and head + CE "
+                        f"forward and d_hidden over every scored row; rate = "
+                        f"{wl.n_tokens} tokens / median step time ({spent:.1f} s in all; "
+                        "corruption and the row list single-threaded numpy, the head's "
+                        f"matrix products on {cores} BLAS threads)"))
 
 
 def main():
@@ -476,20 +536,37 @@ def main():
     value = wl.n_tokens * K / total_s
     log(f"steps: {r['total_ms'] / K:.3f} ms/step, head+CE {head_s.mean() * 1e3:.3f} ms/call, "
         f"mean scored rows {rows.mean():.0f}, {achieved:.1f} TFLOP/s")
-    # the counters' bytes belong to the workload they were taken on
-    traffic = None
+    # the counters' bytes belong to the workload they were taken on, and to
+    # the kernels as they were then: they are reported only while the source
+    # of the fused call's kernels is byte for byte the one they were counted on
+    traffic, traffic_note = None, "no counter file"
     if args.traffic_json and os.path.exists(args.traffic_json):
         with open(args.traffic_json) as f:
             t = json.load(f)
-        if t.get("current") and t.get("workload") == wl.name:
+        src = head_source_sha256()
+        if t.get("workload") != wl.name:
+            traffic_note = f"counted on {t.get('workload')}, not this workload"
+        elif t.get("source_sha256") != src:
+            traffic_note = (f"not reported: the kernels changed since the counters were taken "
+                            f"(counted at {t.get('counted_at', '?')})")
+        else:
             traffic = t.get("bytes_per_call")
+            traffic_note = (f"FETCH_SIZE and WRITE_SIZE per call from {os.path.basename(args.traffic_json)}"
+                            f", counted at {t.get('counted_at', '?')} on the same kernel source "
+                            f"(sha256 {src[:12]})")
     bf16 = wl.dtype == "bf16"
     peak = PEAK_BF16_TFLOPS if bf16 else PEAK_FP32_VALU_TFLOPS
     roofline = dict(bound="mfma" if bf16 else "alu", achieved=achieved, peak=peak,
                     unit="TFLOP/s", frac=achieved / peak, traffic=traffic,
-                    kernel="mdlm_fused_head_ce_fwd_bwd",
+                    traffic_note=traffic_note, kernel="mdlm_fused_head_ce_fwd_bwd",
                     ms_per_call=float(head_s.mean() * 1e3),
                     algorithmic_flops_per_call=float(flops_alg.mean()))
+    step_s = np.array(r["step_ms"]) * 1e-3
+    per_seed = [dict(seed=i, rows=int(rows[i]), step_ms=float(step_s[i] * 1e3),
+                     head_ms=float(head_s[i] * 1e3),
+                     head_tflops=float(flops_alg[i] / head_s[i] / 1e12))
+                for i in range(K)]
+    med_step = float(np.median(step_s))
     out = dict(metric=METRIC, value=value, unit="tokens/s", n_gpus=1, steps=K,
                warmup=args.warmup, ms_per_step=r["total_ms"] / K, higher_is_better=True,
                scaling="weak", vs_baseline=None, dtype="bf16" if wl.dtype == "bf16" else "f32",
@@ -499,7 +576,13 @@ def main():
                            align="aligned" if r["align"] == 0 else "shifted",
                            softcap=wl.softcap, eps=wl.eps, seeds=f"0..{K - 1}",
                            mean_scored_rows=float(rows.mean()), parallelism="none (1 GPU)"),
-               roofline=roofline)
+               roofline=roofline,
+               median=dict(ms_per_step=med_step * 1e3, tokens_per_s=wl.n_tokens / med_step,
+                           head_ms=float(np.median(head_s) * 1e3),
+                           what=("median over the timed steps (each step's HIP events on the "
+                                 "launch stream); `value` is the aggregate over all of them, "
+                                 "the expectation over the noise draw")),
+               per_seed=per_seed)
     if not args.no_achievable:
         log("measuring achievable peaks")
         ach = achievable(dev, (wl.V, wl.H, int(round(rows.mean()))))
@@ -516,12 +599,14 @@ def main():
                 for op in ("corrupt", "compact"):
                     out[k][f"{op}_frac_of_achievable_copy"] = (
                         out[k][f"{op}_GBs"] / out["achievable"]["copy_GBs"])
+    if not args.no_other_workloads and args.workload == 2:
+        out["other_workloads"] = other_workloads(dev, args.other_steps, 2)
     if not args.no_variants:
         log("timing the loss variants")
         out["variants"] = variants(inp, dev, args.bandwidth_tokens)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(inp, rows.mean(), args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, r["align"])
     print(json.dumps(out), flush=True)
 
 

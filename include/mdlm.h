@@ -21,18 +21,19 @@
  *
  * The method is defined on these pages:
  *   - LLaDA-8B-MDLM-LoRA model card, "Training" table, "Objective" row:
- *     t ~ U(0,1) per sequence, mask probability p = (1 - 1e-3) t + 1e-3,
- *     cross-entropy on masked tokens divided by p; "LoRA" row: embeddings
- *     and output layer frozen.
- *   - diffusiongemma-26B-A4B-it-ALWAYS-THINK, "Finetuning notes": corrupt
- *     canvas positions with uniform-random vocabulary ids at a per-example
- *     rate t ~ U(eps, 1) (no mask token); the logit softcap is applied once.
+ *     one t ~ U(0,1) for each sequence, masking probability
+ *     p = (1 - 1e-3) t + 1e-3, and the CE of each masked token scaled by
+ *     1/p; "LoRA" row: embeddings and output layer frozen.
+ *   - diffusiongemma-26B-A4B-it-ALWAYS-THINK, "Finetuning notes": corrupted
+ *     canvas positions take uniformly drawn vocabulary ids, each example
+ *     with its own rate t ~ U(eps, 1) (no mask token); the logit softcap
+ *     acts once.
  *   - Native diffusion language-model training (Axolotl docs): model table
- *     (aligned vs shifted logits, inverse-time weighted CE), "Attention
- *     backends" (cumulative document offsets), "Packed training" (documents
- *     isolated, padding excluded from loss), "Adapters, merging and
- *     inference" (full-vocabulary CE from hidden states through a plain
- *     linear head without materialising vocabulary logits).
+ *     (aligned vs shifted logits, CE weighted by the inverse noise level),
+ *     "Attention backends" (cumulative document offsets), "Packed training"
+ *     (documents isolated, padding excluded from loss), "Adapters, merging
+ *     and inference" (CE over the whole vocabulary taken from the hidden
+ *     states through a bare linear head, no logits tensor stored).
  *
  * Conventions shared by every entry point
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
@@ -232,8 +233,9 @@ size_t mdlm_compact_rows_workspace_bytes(int64_t n_tokens, int32_t n_docs,
  * mask, and other weightings.
  *
  * Defined by: diffusiongemma card, "Finetuning notes" (total = diffusion CE +
- * encoder_loss_weight * encoder AR CE, the AR term a plain causal next-token
- * CE over the clean sequence; the rate t ~ U(eps, 1) drawn per example);
+ * encoder_loss_weight * encoder AR CE, the AR term the left-to-right
+ * next-token CE of the uncorrupted sequence; each example draws its rate
+ * t ~ U(eps, 1));
  * Axolotl docs, objective options (inv_one_minus_t time weighting with
  * example_mean reduction, 1/(1-t) capped by rhine_weight_clip) and "Packed
  * training" (tokens outside the loss are excluded).
@@ -324,9 +326,9 @@ size_t mdlm_head_ce_workspace_min_bytes(int64_t max_rows, int32_t H, int32_t V,
  * the scored rows through a frozen linear head, and its gradient.
  *
  * Defined by: Axolotl docs, "Adapters, merging and inference" (CE over the
- * full vocabulary computed from hidden states without materialising
- * vocabulary logits; plain linear head); LLaDA-8B-MDLM-LoRA card, Training
- * table (CE on masked tokens divided by p; output layer frozen, so no weight
+ * whole vocabulary taken from the hidden states, no logits tensor stored;
+ * bare linear head); LLaDA-8B-MDLM-LoRA card, Training table (the CE of
+ * each masked token scaled by 1/p; output layer frozen, so no weight
  * gradient); diffusiongemma card, "Finetuning notes" (softcap applied once).
  *
  * For j < *n_rows, with h = hidden[row_idx[j]] and z = W h (no bias):
@@ -414,6 +416,81 @@ int mdlm_fused_head_ce_fwd_bwd_dw(const void* hidden, const void* W,
                                   float* row_ce, void* d_hidden, float* dW,
                                   void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/*
+ * mdlm_scale -- y = g * x elementwise, with g a device scalar: the upstream
+ * gradient of the loss applied to d_hidden, for a trainer in which the loss
+ * is one term of what it differentiates (an autograd backward).
+ *
+ * Defined by: LLaDA-8B-MDLM-LoRA card, Training table, "Objective" row (the
+ * loss the trainer backpropagates through); by the chain rule
+ * d(g * loss)/d hidden = g * d_hidden, and mdlm_fused_head_ce_fwd_bwd forms
+ * d_hidden for an upstream gradient of 1.
+ *
+ *   x, y       n entries of element type `dtype`, each 16-byte aligned; y may
+ *              be x (in place).  bf16: the fp32 product rounded once to bf16.
+ *   dtype      MDLM_BF16 or MDLM_F32.
+ *   n          >= 0 entries.
+ *   scale      [1] float device scalar g (read on the device; no host read).
+ * Returns MDLM_OK, MDLM_EINVAL or MDLM_EHIP.
+ */
+int mdlm_scale(const void* x, void* y, int32_t dtype, int64_t n, const float* scale,
+               void* stream);
+
+/* Violation bits of the device-side precondition checks. */
+enum {
+  MDLM_CHECK_OFFSETS = 1,    /* cu_seqlens not 0 = cu[0] <= ... <= cu[n_docs] = n_tokens */
+  MDLM_CHECK_ROW_COUNT = 2,  /* *n_rows outside [0, max_rows]                           */
+  MDLM_CHECK_ROW_INDEX = 4,  /* a listed row index outside [0, n_tokens)                */
+  MDLM_CHECK_TARGET = 8,     /* a listed target outside [0, V)                          */
+  MDLM_CHECK_WEIGHT = 16,    /* a listed weight that is not finite                      */
+  MDLM_CHECK_PROB = 32       /* a p_doc entry outside (0, 1]                            */
+};
+
+/*
+ * Device-side precondition checks.  The entry points above never read
+ * device data on the host, so the preconditions on device-resident inputs
+ * are the caller's; these calls check them.  Each is asynchronous on
+ * `stream`, only reads its inputs, and ORs the MDLM_CHECK_* bits of what it
+ * finds into the device word *status (which the caller clears beforehand:
+ * several checks may accumulate into one word).
+ *
+ * Motivated by: Axolotl docs, "Packed training" (the default overflow policy
+ * raises on an oversized example rather than training on it) and the note
+ * after the model table (a configuration the trainer cannot train natively
+ * is refused).
+ *
+ *   mdlm_check_offsets  cu_seqlens [n_docs + 1] against n_tokens.
+ *   mdlm_check_probs    p_doc [n_docs] in (0, 1].
+ *   mdlm_check_rows     *n_rows in [0, max_rows]; for j < *n_rows (clamped
+ *                       to [0, max_rows]): row_idx[j] in [0, n_tokens),
+ *                       tgt[j] in [0, V) and w[j] finite (tgt and w may be
+ *                       NULL: not checked).  Distinctness of the row indices
+ *                       is not checked.
+ *   status              [1] int32 device word, 4-byte aligned.
+ * Return MDLM_OK, MDLM_EINVAL (bad host arguments; nothing enqueued) or
+ * MDLM_EHIP.
+ */
+int mdlm_check_offsets(const int32_t* cu_seqlens, int32_t n_docs, int64_t n_tokens,
+                       int32_t* status, void* stream);
+int mdlm_check_probs(const double* p_doc, int32_t n_docs, int32_t* status, void* stream);
+int mdlm_check_rows(const int32_t* row_idx, const int32_t* tgt, const float* w,
+                    const int32_t* n_rows, int64_t max_rows, int64_t n_tokens, int32_t V,
+                    int32_t* status, void* stream);
+
+/*
+ * Checking mode.  With checking on, every entry point first checks its own
+ * device inputs (as the calls above do: corruption its offsets; compaction
+ * its offsets and noise levels; the fused head its row list), waits for the result on its stream, and returns MDLM_EINVAL with a
+ * message naming what is wrong -- enqueueing none of its own work -- if a
+ * check fails.  This trades the calls' asynchrony for the checks: a call in
+ * checking mode synchronises its stream, cannot be captured in a graph (it
+ * returns MDLM_EINVAL under stream capture), and calls on several threads
+ * take turns for the check.  Off by default; the environment variable
+ * MDLM_CHECK set to anything but "0" (read at the first call) turns it on.
+ * Returns the previous setting (0 or 1).
+ */
+int mdlm_set_checking(int enable);
 
 /* Message describing the last failure on the calling thread ("" if none).
  * Valid until the next library call on that thread. */

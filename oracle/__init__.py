@@ -10,16 +10,18 @@ and obvious: numpy in float64, one library matmul per V-chunk, no fusion.
 
 Sources for what is computed:
   * LLaDA-8B-MDLM-LoRA model card, "Training" table, "Objective" row:
-    t ~ U(0,1) per sequence, mask probability p = (1-1e-3) t + 1e-3,
-    cross-entropy on masked tokens divided by p.
-  * diffusiongemma-26B-A4B-it-ALWAYS-THINK, "Finetuning notes": corrupt
-    positions with uniform-random vocabulary ids at a per-example rate
-    t ~ U(eps, 1), no mask token; the logit softcap is applied exactly once.
+    one t ~ U(0,1) for each sequence, masking probability
+    p = (1-1e-3) t + 1e-3, and the CE of each masked token scaled by 1/p.
+  * diffusiongemma-26B-A4B-it-ALWAYS-THINK, "Finetuning notes": a corrupted
+    position takes a uniformly drawn vocabulary id, each example drawing its
+    own rate t ~ U(eps, 1), and no mask token exists; the logit softcap
+    acts exactly once.
   * Native diffusion language-model training (Axolotl docs): model table
-    (aligned vs shifted logits; inverse-time weighted CE), "Packed training"
-    (documents stay isolated; padding is excluded from loss) and
-    "Adapters, merging and inference" (full-vocabulary CE from hidden states
-    through a plain linear output head, aligned targets).
+    (aligned vs shifted logits; CE weighted by the inverse noise level),
+    "Packed training" (documents stay isolated; padding is excluded from
+    loss) and "Adapters, merging and inference" (CE over the whole vocabulary
+    taken from the hidden states through a bare linear output head, aligned
+    targets).
   * LLaDA-8B-MDLM-LoRA model card, "Training" table, "Objective" row: the
     corrective mixture's option names (mixture_prob, noise_token_wt,
     clean_token_wt), all 0 for the MDLM objective.  No formula is given:

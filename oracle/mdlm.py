@@ -46,9 +46,9 @@ def _key(seed):
 def noise_levels(seed, eps, n_docs):
     """Per-document noise level t_b, corruption probability p_b and threshold.
 
-    [LLaDA] Objective row: t ~ U(0,1) per sequence, mask probability
-    p = (1 - 1e-3) t + 1e-3.  [Gemma] Finetuning notes: per-example rate
-    t ~ U(eps, 1) -- the same affine map with general eps, so both noise modes
+    [LLaDA] Objective row: one t ~ U(0,1) for each sequence, masking
+    probability p = (1 - 1e-3) t + 1e-3.  [Gemma] Finetuning notes: each
+    example draws its own rate t ~ U(eps, 1) -- the same affine map with general eps, so both noise modes
     share this step.
 
     Reading taken: t is the top 24 bits of Philox word 0 at counter
@@ -130,8 +130,8 @@ def corrupt(x0, cu_seqlens, seed, eps, noise, mask_id, rand_vocab):
 def compact(corrupted, x0, cu_seqlens, p_doc, align):
     """List the scored rows in ascending token order, with targets and weights.
 
-    [LLaDA] Objective row: the loss is cross-entropy on masked tokens divided
-    by the mask probability.  [Axolotl] model table: Nemotron uses aligned
+    [LLaDA] Objective row: the loss is the CE of each masked token, scaled
+    by 1/p.  [Axolotl] model table: Nemotron uses aligned
     logits (the hidden state at position g predicts token g), Dream uses
     shifted logits (position g-1 predicts token g).
 
@@ -141,7 +141,8 @@ def compact(corrupted, x0, cu_seqlens, p_doc, align):
         (row g-1, target x0[g]); a document start has no predecessor inside
         its own document ("Packed training": documents stay isolated);
       * weight w = 1 / (p_b * N) with N the total number of tokens in the
-        call ("loss = sum_masked CE/p / total tokens"), evaluated in fp64.
+        call (the sum of CE/p over masked tokens, over all tokens),
+        evaluated in fp64.
 
     Returns (row_idx int64[M], tgt int64[M], w float64[M]).  The weight the
     library stores is fp32; ``np.float32(w)`` is its exact expected value.
@@ -222,8 +223,8 @@ def compact_corrective(codes, x0, cu_seqlens, p_doc, align, noise_token_wt, clea
     """Scored rows of the corrective mixture's loss, in ascending token order.
 
     [LLaDA] Training table, Objective row: the option names noise_token_wt
-    and clean_token_wt; with both 0 the loss is the MDLM one (cross-entropy
-    on masked tokens divided by the mask probability).  Reading taken
+    and clean_token_wt; with both 0 the loss is the MDLM one (the CE of
+    each masked token, scaled by 1/p).  Reading taken
     (parity unpinned beyond the reductions): every position predicts its
     clean token; a masked token keeps the weight 1 / (p_b N), a replaced
     token gets noise_token_wt / (p_b N) and, when clean_token_wt is not 0,
@@ -268,7 +269,7 @@ WEIGHT_EXAMPLE_MEAN_CLIPPED = 2  # min(1 / (1 - p_b), clip), example mean
 
 
 def compact_rows(x0, cu_seqlens, align, corrupted=None, eligible=None, p_doc=None,
-                 weighting=WEIGHT_INV_P, scale=1.0, clip=None):
+                 weighting=WEIGHT_INV_P, scale=1.0, clip=float("inf")):
     """Scored rows, targets and weights for the loss variants.
 
     A token g of document b is scored when it is corrupted (every token when
@@ -281,7 +282,7 @@ def compact_rows(x0, cu_seqlens, align, corrupted=None, eligible=None, p_doc=Non
         Objective row, as in ``compact``).
       * WEIGHT_MEAN: scale / M, M the number of scored rows.  With
         corrupted=None, shifted logits and scale = lambda this is
-        lambda * (plain causal next-token CE over the clean sequence), the
+        lambda * (the left-to-right next-token CE of the clean sequence), the
         encoder AR term of [Gemma] Finetuning notes; with a mask it is the
         unweighted mean CE over the corrupted tokens.
       * WEIGHT_EXAMPLE_MEAN_CLIPPED: scale * min(1 / (1 - p_b), clip) /
@@ -293,7 +294,8 @@ def compact_rows(x0, cu_seqlens, align, corrupted=None, eligible=None, p_doc=Non
         role of t: under uniform noise the rate is drawn directly as
         t ~ U(eps, 1) ([Gemma] Finetuning notes).
         Order of evaluation: a = 1 / (1 - p_b); a = min(a, clip);
-        w = scale * a / (n_b * B).
+        w = scale * a / (n_b * B).  The default clip, +inf, caps nothing
+        (as the library's weight_clip = +inf does).
 
     Eligibility ([Axolotl] "Packed training": tokens outside the loss, such
     as prompt tokens, are excluded) applies to the target token g.
@@ -343,7 +345,7 @@ def compact_rows(x0, cu_seqlens, align, corrupted=None, eligible=None, p_doc=Non
 
 def _capped_logits(rows_h, w_chunk, softcap):
     """Logits of the plain linear head, z = h W^T (no bias: [Axolotl]
-    "Adapters, merging and inference" requires a plain linear output head),
+    "Adapters, merging and inference": the output head is a bare linear map),
     then the tanh softcap c*tanh(z/c) applied once when c > 0 ([Gemma]
     Finetuning notes: the forward already softcaps; do not apply it twice).
     Returns (capped logits, d capped / d z)."""
@@ -420,16 +422,28 @@ def head_ce(hidden, W, row_idx, tgt, w, softcap=0.0, want_grad=True, chunk=8192)
     return loss, ce, d_hidden
 
 
-def head_ce_weight_grad(hidden, W, row_idx, tgt, w, softcap=0.0, chunk=8192):
+def head_ce_weight_grad(hidden, W, row_idx, tgt, w, softcap=0.0, chunk=8192, v_rows=None):
     """Gradient of loss = sum_j w_j CE_j with respect to the head W, for a
     head that is trained (the frozen-head case of [LLaDA] forms none):
         dW_v = sum_j w_j (softmax(zhat_j)_v - [v = tgt_j]) zhat'_jv h_row_j.
-    Returns float64[V, H]."""
+    Returns float64[V, H]; with ``v_rows`` (vocabulary indices) only those
+    rows, float64[len(v_rows), H], from the same formula (the softmax still
+    normalised over the whole vocabulary)."""
     hidden = np.asarray(hidden)
     row_idx = np.asarray(row_idx, dtype=np.int64)
     tgt = np.asarray(tgt, dtype=np.int64)
     w = np.asarray(w, dtype=np.float64)
     W = np.asarray(W)
+    if v_rows is not None:
+        v_rows = np.asarray(v_rows, dtype=np.int64)
+        if row_idx.size == 0:
+            return np.zeros((v_rows.shape[0], W.shape[1]), dtype=np.float64)
+        _, lse = head_ce_rows(hidden, W, row_idx, tgt, softcap, chunk)
+        rows_h = hidden[row_idx].astype(np.float64)
+        zc, dcap = _capped_logits(rows_h, W[v_rows].astype(np.float64), softcap)
+        prob = np.exp(zc - lse[:, None])
+        prob -= (tgt[:, None] == v_rows[None, :]).astype(np.float64)
+        return (w[:, None] * prob * dcap).T @ rows_h
     dW = np.zeros(W.shape, dtype=np.float64)
     if row_idx.size == 0:
         return dW

@@ -14,8 +14,8 @@ and between rounds the key is advanced by the Weyl constants
 (k0 += W0, k1 += W1, modulo 2^32).  The "-10" variant applies ten rounds;
 the first uses the caller's key unmodified.
 
-The noise draws on the pages ("t ~ U(0,1) per sequence" on the LLaDA-8B-MDLM-
-LoRA card, Training table; uniform-token noise in the diffusiongemma card,
+The noise draws on the pages (one t ~ U(0,1) for each sequence on the
+LLaDA-8B-MDLM-LoRA card, Training table; uniform-token noise in the diffusiongemma card,
 Finetuning notes) fix only distributions.  Realising them with this counter
 generator makes every draw a pure function of (seed, index, stream tag), so a
 GPU implementation can reproduce them bit for bit.

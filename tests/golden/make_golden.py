@@ -6,6 +6,7 @@ oracle and the seeded input generators; the library never writes it.
     python tests/golden/make_golden.py
 """
 
+import base64
 import json
 import os
 import sys
@@ -54,12 +55,24 @@ def run(name):
         w_bits=[f"{v:08x}" for v in w.astype(np.float32).view(np.uint32)],
         loss=float(loss), row_ce=[float(v) for v in ce],
         d_hidden_row_norms=[float(v) for v in np.linalg.norm(dh[rows], axis=1)],
-        d_hidden_norm=float(np.linalg.norm(dh)))
+        d_hidden_norm=float(np.linalg.norm(dh)),
+        d_hidden_rows_f32_b64=encode_rows(dh[rows]))
+
+
+def encode_rows(a):
+    """The scored rows of the gradient, [M, H] in row-list order, rounded to
+    fp32, little-endian, base64."""
+    return base64.b64encode(np.ascontiguousarray(a, dtype="<f4").tobytes()).decode()
+
+
+def decode_rows(text, H):
+    return np.frombuffer(base64.b64decode(text), dtype="<f4").reshape(-1, H)
 
 
 def main():
     out = {"about": "oracle outputs on two tiny seeded cases, written by make_golden.py "
-                    "(oracle only); fp64 p and fp32 w as bit patterns",
+                    "(oracle only); fp64 p and fp32 w as bit patterns; the gradient's "
+                    "scored rows (row-list order) as fp32 little-endian, base64",
            "cases": {name: run(name) for name in CASES}}
     with open(os.path.join(HERE, "oracle_tiny.json"), "w") as f:
         json.dump(out, f, indent=1)

@@ -389,3 +389,40 @@ def test_binding_signatures_match_the_header(lib):
         fn = getattr(lib, name)
         assert fn.argtypes is not None, name
         assert len(fn.argtypes) == n, (name, len(fn.argtypes), n)
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    ((NULL, NULL, 5, 16, NULL, NULL), B.MDLM_EINVAL, "dtype"),
+    ((NULL, NULL, B.MDLM_BF16, -1, NULL, NULL), B.MDLM_EINVAL, "n < 0"),
+    ((NULL, NULL, B.MDLM_BF16, 16, NULL, NULL), B.MDLM_EINVAL, "null pointer"),
+])
+def test_scale_rejects_bad_arguments(lib, args, code, msg):
+    assert lib.mdlm_scale(*args, NULL) == code
+    assert msg in B.mdlm_last_error()
+    # nothing to scale: accepted without touching a pointer
+    assert lib.mdlm_scale(NULL, NULL, B.MDLM_F32, 0, NULL, NULL) == B.MDLM_OK
+
+
+def test_check_calls_reject_bad_arguments(lib):
+    assert lib.mdlm_check_offsets(NULL, -1, 10, NULL, NULL) == B.MDLM_EINVAL
+    assert lib.mdlm_check_offsets(NULL, 2, 10, NULL, NULL) == B.MDLM_EINVAL
+    assert "null pointer" in B.mdlm_last_error()
+    assert lib.mdlm_check_probs(NULL, -1, NULL, NULL) == B.MDLM_EINVAL
+    assert lib.mdlm_check_probs(NULL, 3, NULL, NULL) == B.MDLM_EINVAL
+    assert lib.mdlm_check_rows(NULL, NULL, NULL, NULL, -1, 10, 5, NULL, NULL) == B.MDLM_EINVAL
+    assert lib.mdlm_check_rows(NULL, NULL, NULL, NULL, 4, 10, 5, NULL, NULL) == B.MDLM_EINVAL
+    assert "null pointer" in B.mdlm_last_error()
+
+
+def test_checking_mode_switch_and_host_checks_first(lib):
+    prev = B.mdlm_set_checking(True)
+    try:
+        assert B.mdlm_set_checking(True) is True
+        # host-side checks still come first: null pointers are rejected before
+        # any device check could be enqueued
+        assert corrupt_call(lib) == B.MDLM_EINVAL
+        assert "null token pointer" in B.mdlm_last_error()
+        assert head_call(lib) == B.MDLM_EINVAL
+    finally:
+        B.mdlm_set_checking(prev)
+    assert B.mdlm_set_checking(prev) is prev

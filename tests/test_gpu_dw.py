@@ -3,11 +3,14 @@
 Small and multi-tile cases compare dW with the oracle's fp64 gradient (1e-2
 relative L2, the d_hidden bar; both products take bf16-rounded per-logit
 factors).  The call's loss, row CE and d_hidden must be bit-identical to those
-of mdlm_fused_head_ce_fwd_bwd.  At full size, where the fp64 oracle would need
-trillions of operations, two identities that hold at any size are checked, to
-within the bf16 rounding of those factors: <dW, W> = <d_hidden, hidden> (both
-equal sum_jv G_jv z_jv) and, with no softcap, sum_v dW_v = 0 (each row's
-softmax minus one-hot sums to zero).
+of mdlm_fused_head_ce_fwd_bwd.  At full size (llada8b-1x4096) 640 vocabulary
+rows of dW -- the targets of scored rows, the vocabulary's first and last
+rows and a random sample -- are compared with the oracle's, which forms
+exactly those rows (after its full log-sum-exp pass), each row on its own
+within 1e-2 relative L2; and two identities that hold at any size are
+checked, to within the bf16 rounding of those factors:
+<dW, W> = <d_hidden, hidden> (both equal sum_jv G_jv z_jv) and, with no
+softcap, sum_v dW_v = 0 (each row's softmax minus one-hot sums to zero).
 """
 
 import numpy as np
@@ -113,6 +116,27 @@ def test_dw_is_zero_without_scored_rows():
     step, m, loss, row_ce, dh, dW = _run(inp, seed, 1e-6, oracle.ALIGNED, 0.0)
     assert m == 0 and host(loss)[0] == 0.0
     assert torch.count_nonzero(dW) == 0
+
+
+def test_dw_full_size_sampled_vocabulary_rows():
+    inp = WL.generate(WL.make_workload(2))
+    wl = inp.wl
+    print(f"full-size dW, workload {wl.name}", flush=True)
+    step, m, loss, row_ce, dh, dW = _run(inp, 0, wl.eps, wl.align, wl.softcap)
+    rows, tgt, w = _oracle_rows(inp, 0, wl.eps, wl.align)
+    assert rows.shape[0] == m and m > 0
+    rng = np.random.default_rng(2)
+    pick = np.unique(np.concatenate([
+        rng.choice(np.unique(tgt), size=min(256, np.unique(tgt).shape[0]), replace=False),
+        rng.choice(wl.V, size=380, replace=False), [0, 1, wl.V - 2, wl.V - 1]]))
+    want = oracle.head_ce_weight_grad(inp.hidden, inp.W, rows, tgt, w.astype(np.float32),
+                                      wl.softcap, v_rows=pick)
+    got = host(dW[torch.from_numpy(pick).to(DEV)]).astype(np.float64)
+    assert rel_l2(got, want) < DW_RTOL
+    row_err = np.linalg.norm(got - want, axis=1) / np.linalg.norm(want, axis=1)
+    print(f"  {pick.shape[0]} vocabulary rows: rel-L2 {rel_l2(got, want):.2e}, "
+          f"worst row {row_err.max():.2e}", flush=True)
+    assert row_err.max() < DW_RTOL, (int(pick[row_err.argmax()]), float(row_err.max()))
 
 
 @pytest.mark.parametrize("k", [2, 5])

@@ -1,7 +1,9 @@
 """The library against the oracle's stored outputs on two tiny seeded cases
 (tests/golden/oracle_tiny.json, written from the oracle alone): corruption
 and row lists bit for bit, loss and per-row CE within 1e-3 relative, the
-gradient's per-row norms within 1e-2 relative L2."""
+gradient element by element (its scored rows within 1e-2 relative L2 over
+every entry, each row within 1e-2 relative L2 on its own, every other row
+exactly zero)."""
 
 import json
 import os
@@ -41,5 +43,12 @@ def test_library_matches_stored_oracle_outputs(name):
     assert abs(float(host(s.loss)[0]) - want["loss"]) <= 1e-3 * abs(want["loss"])
     np.testing.assert_allclose(host(s.row_ce)[:m], want["row_ce"], rtol=1e-3)
     rows = np.array(want["row_idx"])
-    norms = np.linalg.norm(d_hidden_host(s)[rows].astype(np.float64), axis=1)
+    g = d_hidden_host(s).astype(np.float64)
+    norms = np.linalg.norm(g[rows], axis=1)
     assert rel_l2(norms, want["d_hidden_row_norms"]) < 1e-2
+    ref = make_golden.decode_rows(want["d_hidden_rows_f32_b64"], g.shape[1]).astype(np.float64)
+    assert rel_l2(g[rows], ref) < 1e-2
+    for j in range(m):
+        assert rel_l2(g[rows[j]], ref[j]) < 1e-2, j
+    unscored = np.setdiff1d(np.arange(g.shape[0]), rows)
+    assert np.all(g[unscored] == 0.0)

@@ -1,9 +1,10 @@
 """Pins the oracle's noise levels and corruption to what the pages fix.
 
-LLaDA-8B-MDLM-LoRA card, Training table, "Objective" row: t ~ U(0,1) per
-sequence and each token is masked with probability p = (1 - 1e-3) t + 1e-3.
-diffusiongemma card, "Finetuning notes": uniform-random vocabulary ids at a
-per-example rate t ~ U(eps, 1), no mask token.
+LLaDA-8B-MDLM-LoRA card, Training table, "Objective" row: one t ~ U(0,1) for
+each sequence, and every token is masked with probability
+p = (1 - 1e-3) t + 1e-3.  diffusiongemma card, "Finetuning notes": uniformly
+drawn vocabulary ids, each example with its own rate t ~ U(eps, 1), and no
+mask token.
 
 These tests check distributions and special cases, not the formulas' text:
   * t is uniform on [0, 1) (Kolmogorov-Smirnov);

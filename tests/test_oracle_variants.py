@@ -129,6 +129,20 @@ def test_example_mean_clipped_against_a_per_document_loop():
                                                   rel=1e-12)
 
 
+def test_example_mean_without_a_clip_is_the_plain_inverse_one_minus_rate():
+    # no clip argument: nothing is capped, each document's weights sum to
+    # scale / ((1 - p_b) B), written out here per document
+    rng, cu, x0, hidden, W = _case(7, n_docs=4, max_len=20)
+    nd = cu.shape[0] - 1
+    p = np.array([0.25, 0.5, 0.9, 0.6])[:nd]
+    mask = rng.random(x0.shape[0]) < 0.6
+    rows, tgt, w = compact_rows(x0, cu, ALIGNED, mask, None, p, WEIGHT_EXAMPLE_MEAN_CLIPPED, 2.0)
+    doc = np.searchsorted(cu[1:], rows, side="right")
+    B = len(set(doc.tolist()))
+    for b in set(doc.tolist()):
+        assert w[doc == b].sum() == pytest.approx(2.0 / ((1.0 - p[b]) * B), rel=1e-12)
+
+
 @pytest.mark.parametrize("softcap", [0.0, 2.0])
 def test_head_weight_gradient_finite_differences(softcap):
     rng, cu, x0, hidden, W = _case(5, n_docs=2, max_len=6, H=3, V=7)
@@ -145,6 +159,20 @@ def test_head_weight_gradient_finite_differences(softcap):
             lp, _, _ = head_ce(hidden, Wp, rows, x0, w, softcap, want_grad=False)
             lm, _, _ = head_ce(hidden, Wm, rows, x0, w, softcap, want_grad=False)
             assert dW[v, k] == pytest.approx((lp - lm) / (2 * h), rel=1e-5, abs=1e-8)
+
+
+@pytest.mark.parametrize("softcap", [0.0, 2.0])
+def test_head_weight_gradient_selected_rows_equal_the_full_gradient(softcap):
+    # the v_rows form (a repeated index, the targets' rows, others) against
+    # the full gradient, which finite differences and the closed form pin
+    rng, cu, x0, hidden, W = _case(8, n_docs=3, max_len=12, H=6, V=13)
+    rows = np.arange(0, x0.shape[0], 2)
+    tgt = x0[rows]
+    w = rng.uniform(0.1, 1.0, size=rows.shape[0])
+    full = head_ce_weight_grad(hidden, W, rows, tgt, w, softcap)
+    pick = np.array([int(tgt[0]), 0, 12, int(tgt[0]), 5, int(tgt[-1])])
+    part = head_ce_weight_grad(hidden, W, rows, tgt, w, softcap, v_rows=pick)
+    assert np.allclose(part, full[pick], rtol=1e-12, atol=1e-15)
 
 
 def test_head_weight_gradient_closed_form_at_zero_head():

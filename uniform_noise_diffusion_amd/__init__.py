@@ -3,7 +3,8 @@
 The HIP library libmdlm.so (C ABI in include/mdlm.h) implements per-document
 noise levels, corruption, ordered compaction of scored rows and the fused
 frozen-head + cross-entropy forward and backward.  `binding` exposes its
-entry points under the same names; `pipeline` owns the buffers of one step.
+entry points under the same names; `pipeline` owns the buffers of one step;
+`autograd` wraps the fused call as a differentiable loss.
 """
 
 from .binding import (  # noqa: F401
@@ -17,3 +18,4 @@ from .binding import (  # noqa: F401
     mdlm_fused_head_ce_fwd_bwd, mdlm_last_error, mdlm_version,
 )
 from .pipeline import MdlmLossStep  # noqa: F401
+from .autograd import FusedHeadCE, masked_diffusion_loss  # noqa: F401

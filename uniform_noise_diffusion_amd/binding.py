@@ -32,6 +32,12 @@ MDLM_WEIGHT_EXAMPLE_MEAN_CLIPPED = 2
 MDLM_CODE_CLEAN = 0
 MDLM_CODE_MASKED = 1
 MDLM_CODE_REPLACED = 2
+MDLM_CHECK_OFFSETS = 1
+MDLM_CHECK_ROW_COUNT = 2
+MDLM_CHECK_ROW_INDEX = 4
+MDLM_CHECK_TARGET = 8
+MDLM_CHECK_WEIGHT = 16
+MDLM_CHECK_PROB = 32
 
 EXPORTED = (
     "mdlm_corrupt",
@@ -47,6 +53,11 @@ EXPORTED = (
     "mdlm_head_ce_dw_workspace_bytes",
     "mdlm_head_ce_dw_workspace_min_bytes",
     "mdlm_fused_head_ce_fwd_bwd_dw",
+    "mdlm_scale",
+    "mdlm_check_offsets",
+    "mdlm_check_probs",
+    "mdlm_check_rows",
+    "mdlm_set_checking",
     "mdlm_last_error",
     "mdlm_version",
 )
@@ -104,6 +115,16 @@ def load():
     lib.mdlm_fused_head_ce_fwd_bwd_dw.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp, i64,
                                                   f32, vp, vp, vp, vp, vp, sz, vp]
     lib.mdlm_fused_head_ce_fwd_bwd_dw.restype = ctypes.c_int
+    lib.mdlm_scale.argtypes = [vp, vp, i32, i64, vp, vp]
+    lib.mdlm_scale.restype = ctypes.c_int
+    lib.mdlm_check_offsets.argtypes = [vp, i32, i64, vp, vp]
+    lib.mdlm_check_offsets.restype = ctypes.c_int
+    lib.mdlm_check_probs.argtypes = [vp, i32, vp, vp]
+    lib.mdlm_check_probs.restype = ctypes.c_int
+    lib.mdlm_check_rows.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp, vp]
+    lib.mdlm_check_rows.restype = ctypes.c_int
+    lib.mdlm_set_checking.argtypes = [ctypes.c_int]
+    lib.mdlm_set_checking.restype = ctypes.c_int
     lib.mdlm_last_error.argtypes = []
     lib.mdlm_last_error.restype = ctypes.c_char_p
     lib.mdlm_version.argtypes = []
@@ -329,3 +350,49 @@ def mdlm_fused_head_ce_fwd_bwd_dw(hidden, W, row_idx, tgt, w, n_rows, max_rows, 
         _ptr(hidden), _ptr(W), n_tokens, H, V, _ptr(row_idx), _ptr(tgt), _ptr(w), _ptr(n_rows),
         int(max_rows), float(softcap), _ptr(loss), _ptr(row_ce), _ptr(d_hidden), _ptr(dW),
         _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mdlm_scale(x, y, scale, stream=None):
+    """See mdlm_scale in include/mdlm.h: y = scale * x for bf16 or float32
+    tensors of one size (y may be x); `scale` a one-element float32 device
+    tensor."""
+    dt = dtype_code(x)
+    _need(x, x.dtype, "x")
+    _need(y, x.dtype, "y")
+    _need(scale, torch.float32, "scale")
+    if y.numel() != x.numel():
+        raise ValueError("x and y must have as many entries")
+    _check(load().mdlm_scale(_ptr(x), _ptr(y), dt, x.numel(), _ptr(scale), _stream(stream)))
+
+
+def mdlm_check_offsets(cu_seqlens, n_tokens, status, stream=None):
+    """See mdlm_check_offsets in include/mdlm.h: ORs violation bits into the
+    one-element int32 device tensor `status`."""
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    _need(status, torch.int32, "status")
+    _check(load().mdlm_check_offsets(_ptr(cu_seqlens), cu_seqlens.numel() - 1, int(n_tokens),
+                                     _ptr(status), _stream(stream)))
+
+
+def mdlm_check_probs(p_doc, status, stream=None):
+    """See mdlm_check_probs in include/mdlm.h."""
+    _need(p_doc, torch.float64, "p_doc")
+    _need(status, torch.int32, "status")
+    _check(load().mdlm_check_probs(_ptr(p_doc), p_doc.numel(), _ptr(status), _stream(stream)))
+
+
+def mdlm_check_rows(row_idx, tgt, w, n_rows, max_rows, n_tokens, V, status, stream=None):
+    """See mdlm_check_rows in include/mdlm.h; `tgt` and `w` may be None."""
+    _need(row_idx, torch.int32, "row_idx")
+    _need(tgt, torch.int32, "tgt")
+    _need(w, torch.float32, "w")
+    _need(n_rows, torch.int32, "n_rows")
+    _need(status, torch.int32, "status")
+    _check(load().mdlm_check_rows(_ptr(row_idx), _ptr(tgt), _ptr(w), _ptr(n_rows),
+                                  int(max_rows), int(n_tokens), int(V), _ptr(status),
+                                  _stream(stream)))
+
+
+def mdlm_set_checking(enable):
+    """See mdlm_set_checking in include/mdlm.h; returns the previous setting."""
+    return bool(load().mdlm_set_checking(1 if enable else 0))

@@ -27,6 +27,28 @@ int check_launch(const char* what) {
   return MDLM_OK;
 }
 
+// Checking mode's step for entry points that take document offsets (and,
+// with `p`, noise levels).
+static int check_docs(const char* fn, const int32_t* cu, int32_t n_docs, int64_t n,
+                      const double* p, hipStream_t st) {
+  if (!checking_enabled() || n_docs <= 0) return MDLM_OK;
+  return run_checks(fn, st, [&](int32_t* word) {
+    hipError_t e = launch_check_offsets(cu, n_docs, n, word, st);
+    if (e == hipSuccess && p) e = launch_check_probs(p, n_docs, word, st);
+    return e;
+  });
+}
+
+// Checking mode's step for entry points that take a row list.
+static int check_row_list(const char* fn, const int32_t* row_idx, const int32_t* tgt,
+                          const float* w, const int32_t* n_rows, int64_t max_rows,
+                          int64_t n_tokens, int32_t V, hipStream_t st) {
+  if (!checking_enabled() || max_rows <= 0) return MDLM_OK;
+  return run_checks(fn, st, [&](int32_t* word) {
+    return launch_check_rows(row_idx, tgt, w, n_rows, max_rows, n_tokens, V, word, st);
+  });
+}
+
 }  // namespace mdlm
 
 using namespace mdlm;
@@ -57,6 +79,9 @@ int mdlm_corrupt(const int32_t* x0, int64_t n_tokens, const int32_t* cu_seqlens,
     return fail(MDLM_EINVAL, "mdlm_corrupt: null token pointer");
   if (n_docs > 0 && (!cu_seqlens || !p_doc || !doc_counts))
     return fail(MDLM_EINVAL, "mdlm_corrupt: null document pointer");
+  if (const int rc = check_docs("mdlm_corrupt", cu_seqlens, n_docs, n_tokens, nullptr,
+                                reinterpret_cast<hipStream_t>(stream)))
+    return rc;
   if (launch_corrupt(x0, n_tokens, cu_seqlens, n_docs, seed, eps, noise, mask_id, rand_vocab,
                      xt, corrupted, p_doc, doc_counts,
                      reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
@@ -83,6 +108,9 @@ int mdlm_corrupt_mixture(const int32_t* x0, int64_t n_tokens, const int32_t* cu_
     return fail(MDLM_EINVAL, "%s: null token pointer", fn);
   if (n_docs > 0 && (!cu_seqlens || !p_doc || !doc_counts))
     return fail(MDLM_EINVAL, "%s: null document pointer", fn);
+  if (const int rc = check_docs(fn, cu_seqlens, n_docs, n_tokens, nullptr,
+                                reinterpret_cast<hipStream_t>(stream)))
+    return rc;
   if (launch_corrupt(x0, n_tokens, cu_seqlens, n_docs, seed, eps, kNoiseMixture, mask_id,
                      rand_vocab, xt, corrupted, p_doc, doc_counts,
                      reinterpret_cast<hipStream_t>(stream), mixture_prob) != hipSuccess)
@@ -131,6 +159,9 @@ static int compact_common(const char* fn, bool need_mask, const uint8_t* corrupt
                 need);
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 4) != 0)
     return fail(MDLM_EINVAL, "%s: workspace must be 4-byte aligned", fn);
+  if (const int rc = check_docs(fn, cu_seqlens, n_docs, n_tokens, need_p ? p_doc : nullptr,
+                                reinterpret_cast<hipStream_t>(stream)))
+    return rc;
   if (launch_compact(corrupted, eligible, x0, n_tokens, cu_seqlens, n_docs, p_doc, align,
                      weighting, scale, clip, row_idx, tgt, w, n_rows, workspace,
                      reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
@@ -174,6 +205,9 @@ int mdlm_compact_corrective(const uint8_t* codes, const int32_t* x0, int64_t n_t
                 need);
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 4) != 0)
     return fail(MDLM_EINVAL, "%s: workspace must be 4-byte aligned", fn);
+  if (const int rc = check_docs(fn, cu_seqlens, n_docs, n_tokens, p_doc,
+                                reinterpret_cast<hipStream_t>(stream)))
+    return rc;
   if (launch_compact_corrective(codes, x0, n_tokens, cu_seqlens, n_docs, p_doc, align,
                                 noise_token_wt, clean_token_wt, row_idx, tgt, w, n_rows,
                                 workspace, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
@@ -259,6 +293,9 @@ static int head_common(const char* fn, const void* hidden, const void* W, int32_
                 workspace_bytes, need);
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 256) != 0)
     return fail(MDLM_EINVAL, "%s: workspace must be 256-byte aligned", fn);
+  if (const int rc = check_row_list(fn, row_idx, tgt, w, n_rows, max_rows, n_tokens, V,
+                                    reinterpret_cast<hipStream_t>(stream)))
+    return rc;
   HeadCeArgs a;
   a.hidden = hidden;
   a.W = W;
@@ -308,5 +345,59 @@ int mdlm_fused_head_ce_fwd_bwd_dw(const void* hidden, const void* W, int64_t n_t
                      max_rows, softcap, loss, row_ce, d_hidden, dW, workspace, workspace_bytes,
                      stream);
 }
+
+int mdlm_scale(const void* x, void* y, int32_t dtype, int64_t n, const float* scale,
+               void* stream) {
+  clear_error();
+  const char* fn = "mdlm_scale";
+  if (dtype != MDLM_F32 && dtype != MDLM_BF16)
+    return fail(MDLM_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (n < 0) return fail(MDLM_EINVAL, "%s: n < 0", fn);
+  if (n > 0 && (!x || !y || !scale)) return fail(MDLM_EINVAL, "%s: null pointer", fn);
+  if (n > 0 && ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(y)) % 16) != 0)
+    return fail(MDLM_EINVAL, "%s: x and y must be 16-byte aligned", fn);
+  if (launch_scale(x, y, dtype, n, scale, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return check_launch(fn);
+  return MDLM_OK;
+}
+
+int mdlm_check_offsets(const int32_t* cu_seqlens, int32_t n_docs, int64_t n_tokens,
+                       int32_t* status, void* stream) {
+  clear_error();
+  const char* fn = "mdlm_check_offsets";
+  if (n_docs < 0 || n_tokens < 0) return fail(MDLM_EINVAL, "%s: bad sizes", fn);
+  if (!cu_seqlens || !status) return fail(MDLM_EINVAL, "%s: null pointer", fn);
+  if (launch_check_offsets(cu_seqlens, n_docs, n_tokens, status,
+                           reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return check_launch(fn);
+  return MDLM_OK;
+}
+
+int mdlm_check_probs(const double* p_doc, int32_t n_docs, int32_t* status, void* stream) {
+  clear_error();
+  const char* fn = "mdlm_check_probs";
+  if (n_docs < 0) return fail(MDLM_EINVAL, "%s: n_docs < 0", fn);
+  if ((n_docs > 0 && !p_doc) || !status) return fail(MDLM_EINVAL, "%s: null pointer", fn);
+  if (launch_check_probs(p_doc, n_docs, status, reinterpret_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return check_launch(fn);
+  return MDLM_OK;
+}
+
+int mdlm_check_rows(const int32_t* row_idx, const int32_t* tgt, const float* w,
+                    const int32_t* n_rows, int64_t max_rows, int64_t n_tokens, int32_t V,
+                    int32_t* status, void* stream) {
+  clear_error();
+  const char* fn = "mdlm_check_rows";
+  if (max_rows < 0 || n_tokens < 0 || V < 0) return fail(MDLM_EINVAL, "%s: bad sizes", fn);
+  if (!n_rows || !status || (max_rows > 0 && !row_idx))
+    return fail(MDLM_EINVAL, "%s: null pointer", fn);
+  if (launch_check_rows(row_idx, tgt, w, n_rows, max_rows, n_tokens, V, status,
+                        reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return check_launch(fn);
+  return MDLM_OK;
+}
+
+int mdlm_set_checking(int enable) { return set_checking(enable); }
 
 }  // extern "C"

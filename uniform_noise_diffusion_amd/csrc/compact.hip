@@ -147,12 +147,15 @@ __device__ __forceinline__ int lanes_below(uint64_t b) {
 // For each tile k, the documents holding its first token (tile_lo[k]) and its
 // last token (tile_hi[k]).  A non-empty document holds exactly the tokens
 // [cu[b], cu[b+1]), so each tile boundary token has exactly one writer.
+// Offsets that break the preconditions (negative, decreasing, past n) are
+// clipped to [0, n] first, so every write stays inside the two tables; the
+// tables' contents are then unspecified, and tile_range clamps what it reads.
 __global__ void __launch_bounds__(kThreads)
 tile_docs_kernel(const int32_t* __restrict__ cu, int32_t n_docs, int64_t n,
                  int32_t* __restrict__ tile_lo, int32_t* __restrict__ tile_hi) {
   const int b = blockIdx.x * kThreads + threadIdx.x;
   if (b >= n_docs) return;
-  const int64_t beg = cu[b], end = min<int64_t>(cu[b + 1], n);
+  const int64_t beg = max<int64_t>(cu[b], 0), end = min<int64_t>(cu[b + 1], n);
   if (beg >= end) return;
   // tiles whose first token 4096 k lies in [beg, end)
   for (int64_t k = (beg + kTile - 1) / kTile; k * kTile < end; ++k) tile_lo[k] = b;
@@ -205,7 +208,8 @@ count_kernel(RowMasks<kC, kE> mk, int64_t n, const int32_t* __restrict__ cu, int
     }
   }
   cnt = wave_sum(cnt);
-  if (lane == 0) tile_counts[t] = cnt;
+  // (negative only when the offsets break their preconditions)
+  if (lane == 0) tile_counts[t] = max(cnt, 0);
 }
 
 // Example-mean weighting, pass 1: one wave per document counts its scored
@@ -515,10 +519,15 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
       }
     }
     __syncthreads();
+    // (offsets that break their preconditions can misplace rows; the bounds
+    // test keeps every store inside the n-entry row buffers regardless)
     for (int i = tid; i < round_total; i += kThreads) {
-      row_idx[out + i] = s_row[buf][i];
-      tgt[out + i] = s_tgt[buf][i];
-      w[out + i] = s_w[buf][i];
+      const int64_t o = out + i;
+      if (o < n) {
+        row_idx[o] = s_row[buf][i];
+        tgt[o] = s_tgt[buf][i];
+        w[o] = s_w[buf][i];
+      }
     }
     out += round_total;
     // with one buffer, the next round's staging must wait for this copy

@@ -1,8 +1,9 @@
 // Per-document noise levels and per-token corruption.
 //
-// Method: LLaDA-8B-MDLM-LoRA card, "Training" table, "Objective" row (t ~ U(0,1)
-// per sequence, mask probability p = (1 - 1e-3) t + 1e-3); diffusiongemma card,
-// "Finetuning notes" (uniform-random ids at a per-example rate t ~ U(eps, 1));
+// Method: LLaDA-8B-MDLM-LoRA card, "Training" table, "Objective" row (one
+// t ~ U(0,1) for each sequence, masking probability p = (1 - 1e-3) t + 1e-3);
+// diffusiongemma card, "Finetuning notes" (uniformly drawn ids, each example
+// with its own rate t ~ U(eps, 1));
 // Axolotl diffusion docs, "Packed training" (documents in a packed stream stay
 // isolated, so each draws its own t).  The corrective mixture (same card and
 // row: mixture_prob and noise_token_wt, no formula given) is read as

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <functional>
+
 #include "mdlm.h"
 
 namespace mdlm {
@@ -155,5 +157,28 @@ struct HeadCeArgs {
 size_t head_ce_workspace_bytes(int64_t max_rows, int32_t H, int32_t V, int32_t dtype,
                                bool minimal, bool dw);
 hipError_t launch_head_ce(const HeadCeArgs& a, hipStream_t stream);
+// y = *scale * x over n entries of `dtype` (x and y 16-byte aligned; y may be x)
+hipError_t launch_scale(const void* x, void* y, int32_t dtype, int64_t n, const float* scale,
+                        hipStream_t stream);
+
+// ---- device-side precondition checks (check.hip) -------------------------
+// Each ORs MDLM_CHECK_* bits into *status; inputs are only read.
+hipError_t launch_check_offsets(const int32_t* cu, int32_t n_docs, int64_t n, int32_t* status,
+                                hipStream_t stream);
+hipError_t launch_check_probs(const double* p, int32_t n_docs, int32_t* status,
+                              hipStream_t stream);
+hipError_t launch_check_rows(const int32_t* row_idx, const int32_t* tgt, const float* w,
+                             const int32_t* n_rows, int64_t max_rows, int64_t n_tokens,
+                             int32_t V, int32_t* status, hipStream_t stream);
+// Checking mode: off unless MDLM_CHECK is set (not "0") at the first query,
+// or switched by set_checking (which returns the previous setting).
+bool checking_enabled();
+int set_checking(int enable);
+// Enqueues checks into a cleared status word (the argument) on `stream`.
+typedef std::function<hipError_t(int32_t*)> CheckEnqueue;
+// Checking mode's step before an entry point's launches: runs `enqueue`,
+// waits for it and returns MDLM_OK, or MDLM_EINVAL naming the broken
+// preconditions (nothing of the entry point's own work enqueued).
+int run_checks(const char* fn, hipStream_t stream, const CheckEnqueue& enqueue);
 
 }  // namespace mdlm

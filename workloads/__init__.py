@@ -8,8 +8,8 @@ fp64 oracle consume what it returns.
 No dataset or trained weight is available, so every workload is synthetic:
   * tokens are uniform over a stated id range;
   * document lengths are lognormal with the stated arithmetic mean and
-    sigma 1, rounded and clipped to [16, 4096] (chunks of at most 4,096
-    tokens, chunks under 16 dropped: LLaDA-8B-MDLM-LoRA card, Training table,
+    sigma 1, rounded and clipped to [16, 4096] (chunks are capped at 4,096
+    tokens and those below 16 are discarded: LLaDA-8B-MDLM-LoRA card, Training table,
     "Data" row);
   * hidden states are N(0,1), row-wise RMS-normalised for the bf16 shapes;
   * the head W is N(0, 0.02^2), shape [V, H], row-major;
