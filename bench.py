@@ -183,6 +183,27 @@ def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
     t_cor = np.mean([a.elapsed_time(b) for a, b, _ in ec]) * 1e-3
     t_cmp = np.mean([b.elapsed_time(c) for _, b, c in ec]) * 1e-3
     m = int(step.n_rows.item())
+    # the one-pass call: the same outputs as the two calls above
+    from uniform_noise_diffusion_amd import binding as B
+    ws = torch.empty(B.mdlm_corrupt_compact_workspace_bytes(n), dtype=torch.uint8, device=dev)
+
+    def fused(seed):
+        B.mdlm_corrupt_compact(x0, cu, seed, 1e-3, 0, 126336, 126464, 0, step.xt, step.corrupted,
+                               step.p_doc, step.doc_counts, step.row_idx, step.tgt, step.w,
+                               step.n_rows, ws)
+    for i in range(2):
+        fused(i)
+    torch.cuda.synchronize()
+    ef = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for i in range(reps):
+        ef[i][0].record()
+        fused(100 + i)
+        ef[i][1].record()
+    torch.cuda.synchronize()
+    t_fused = np.mean([a.elapsed_time(b) for a, b in ef]) * 1e-3
+    m_fused = int(step.n_rows.item())
+    b_fused = 9.0 * n + 12.0 * m_fused
     # algorithmic bytes: corrupt reads x0 (4 B) and writes xt (4 B) and the
     # mask (1 B) per token; compact reads the mask (1 B) per token and, per
     # scored row, the target (4 B) and writes row, target and weight (12 B)
@@ -193,7 +214,14 @@ def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
                 corrupt_us=t_cor * 1e6, corrupt_GBs=b_cor / t_cor / 1e9,
                 corrupt_frac=b_cor / t_cor / 1e9 / PEAK_HBM_GBS,
                 compact_us=t_cmp * 1e6, compact_GBs=b_cmp / t_cmp / 1e9,
-                compact_frac=b_cmp / t_cmp / 1e9 / PEAK_HBM_GBS)
+                compact_frac=b_cmp / t_cmp / 1e9 / PEAK_HBM_GBS,
+                fused_us=t_fused * 1e6, fused_GBs=b_fused / t_fused / 1e9,
+                fused_frac=b_fused / t_fused / 1e9 / PEAK_HBM_GBS,
+                two_calls_us=(t_cor + t_cmp) * 1e6,
+                fused_what=("mdlm_corrupt_compact (corruption and the row list in one pass); "
+                            "algorithmic bytes 9 per token (x0 read, xt and mask written) + "
+                            "12 per scored row (row, target, weight written; the target is the "
+                            "token already read)"))
 
 
 def achievable(dev, gemm_shape=None):

@@ -57,7 +57,7 @@ def test_backward_scales_by_the_upstream_gradient(upstream, softcap):
     (loss * upstream).backward()
     o_loss, _, o_dh = oracle.head_ce(inp.hidden, inp.W, rows, tgt, w, softcap)
     assert loss.dim() == 0
-    assert abs(float(loss) - o_loss) <= 1e-3 * abs(o_loss)
+    assert abs(float(loss.detach()) - o_loss) <= 1e-3 * abs(o_loss)
     g = h.grad.float().cpu().numpy()
     assert rel_l2(g, upstream * o_dh) < 1e-2
     unscored = np.setdiff1d(np.arange(inp.wl.n_tokens), rows)
@@ -83,7 +83,7 @@ def test_sum_of_two_loss_terms_and_autograd_grad():
                                      weighting=oracle.WEIGHT_MEAN)
     l1, _, d1 = oracle.head_ce(inp.hidden, inp.W, rows, tgt, w)
     l2, _, d2 = oracle.head_ce(inp.hidden, inp.W, r2, t2, w2)
-    assert abs(float(total) - (l1 + lam * l2)) <= 1e-3 * abs(l1 + lam * l2)
+    assert abs(float(total.detach()) - (l1 + lam * l2)) <= 1e-3 * abs(l1 + lam * l2)
     assert rel_l2(gh.float().cpu().numpy(), -2.5 * (d1 + lam * d2)) < 1e-2
 
 

@@ -98,8 +98,12 @@ def test_checking_mode_passes_valid_inputs_unchanged(checking):
     a = run_step(inp, seed=3, eps=0.5)
     B.mdlm_set_checking(False)
     b = run_step(inp, seed=3, eps=0.5)
-    for name in ("xt", "corrupted", "row_idx", "loss"):
+    m = int(host(a.n_rows)[0])
+    assert m == int(host(b.n_rows)[0]) and m > 0
+    for name in ("xt", "corrupted", "loss"):
         assert np.array_equal(host(getattr(a, name)), host(getattr(b, name))), name
+    for name in ("row_idx", "tgt", "w"):
+        assert np.array_equal(host(getattr(a, name))[:m], host(getattr(b, name))[:m]), name
     assert torch.equal(a.d_hidden, b.d_hidden)
 
 

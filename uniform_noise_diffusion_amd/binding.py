@@ -42,6 +42,8 @@ MDLM_CHECK_PROB = 32
 EXPORTED = (
     "mdlm_corrupt",
     "mdlm_corrupt_mixture",
+    "mdlm_corrupt_compact_workspace_bytes",
+    "mdlm_corrupt_compact",
     "mdlm_compact_workspace_bytes",
     "mdlm_compact_masked",
     "mdlm_compact_corrective",
@@ -89,6 +91,11 @@ def load():
     lib.mdlm_corrupt_mixture.argtypes = [vp, i64, vp, i32, u64, f64, f64, i32, i32, vp, vp, vp,
                                          vp, vp]
     lib.mdlm_corrupt_mixture.restype = ctypes.c_int
+    lib.mdlm_corrupt_compact_workspace_bytes.argtypes = [i64]
+    lib.mdlm_corrupt_compact_workspace_bytes.restype = sz
+    lib.mdlm_corrupt_compact.argtypes = [vp, i64, vp, i32, u64, f64, i32, i32, i32, i32, vp, vp,
+                                         vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.mdlm_corrupt_compact.restype = ctypes.c_int
     lib.mdlm_compact_workspace_bytes.argtypes = [i64]
     lib.mdlm_compact_workspace_bytes.restype = sz
     lib.mdlm_compact_masked.argtypes = [vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -198,6 +205,34 @@ def mdlm_corrupt_mixture(x0, cu_seqlens, seed, eps, mixture_prob, mask_id, rand_
                                        float(mixture_prob), int(mask_id), int(rand_vocab),
                                        _ptr(xt), _ptr(codes), _ptr(p_doc), _ptr(doc_counts),
                                        _stream(stream)))
+
+
+def mdlm_corrupt_compact_workspace_bytes(n_tokens):
+    return load().mdlm_corrupt_compact_workspace_bytes(int(n_tokens))
+
+
+def mdlm_corrupt_compact(x0, cu_seqlens, seed, eps, noise, mask_id, rand_vocab, align, xt,
+                         corrupted, p_doc, doc_counts, row_idx, tgt, w, n_rows, workspace,
+                         stream=None):
+    """See mdlm_corrupt_compact in include/mdlm.h.  `corrupted` may be None;
+    `workspace` is a uint8 tensor."""
+    _need(x0, torch.int32, "x0")
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    _need(xt, torch.int32, "xt")
+    _need(corrupted, torch.uint8, "corrupted")
+    _need(p_doc, torch.float64, "p_doc")
+    _need(doc_counts, torch.int32, "doc_counts")
+    _need(row_idx, torch.int32, "row_idx")
+    _need(tgt, torch.int32, "tgt")
+    _need(w, torch.float32, "w")
+    _need(n_rows, torch.int32, "n_rows")
+    _need(workspace, torch.uint8, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(load().mdlm_corrupt_compact(
+        _ptr(x0), x0.numel(), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
+        int(seed) & 0xFFFFFFFFFFFFFFFF, float(eps), int(noise), int(mask_id), int(rand_vocab),
+        int(align), _ptr(xt), _ptr(corrupted), _ptr(p_doc), _ptr(doc_counts), _ptr(row_idx),
+        _ptr(tgt), _ptr(w), _ptr(n_rows), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def mdlm_compact_workspace_bytes(n_tokens):

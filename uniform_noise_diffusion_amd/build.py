@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmdlm.so")
-SOURCES = ["api.hip", "corrupt.hip", "compact.hip", "head_ce.hip", "check.hip", "scale.hip"]
+SOURCES = ["api.hip", "corrupt.hip", "compact.hip", "head_ce.hip", "check.hip", "scale.hip", "corrupt_compact.hip"]
 PROBE_LIB_PATH = os.path.join(PKG_DIR, "libmdlm_probe.so")
 PROBE_SOURCES = ["probe.hip"]
 ARCH = os.environ.get("MDLM_OFFLOAD_ARCH", "gfx950")

@@ -118,6 +118,49 @@ int mdlm_corrupt_mixture(const int32_t* x0, int64_t n_tokens, const int32_t* cu_
   return MDLM_OK;
 }
 
+size_t mdlm_corrupt_compact_workspace_bytes(int64_t n_tokens) {
+  return corrupt_compact_workspace_bytes(n_tokens);
+}
+
+int mdlm_corrupt_compact(const int32_t* x0, int64_t n_tokens, const int32_t* cu_seqlens,
+                         int32_t n_docs, uint64_t seed, double eps, int32_t noise,
+                         int32_t mask_id, int32_t rand_vocab, int32_t align, int32_t* xt,
+                         uint8_t* corrupted, double* p_doc, int32_t* doc_counts,
+                         int32_t* row_idx, int32_t* tgt, float* w, int32_t* n_rows,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  const char* fn = "mdlm_corrupt_compact";
+  if (n_tokens < 0) return fail(MDLM_EINVAL, "%s: n_tokens < 0", fn);
+  if (n_tokens > INT32_MAX) return fail(MDLM_EUNSUPPORTED, "%s: n_tokens must be below 2^31", fn);
+  if (n_docs < 0) return fail(MDLM_EINVAL, "%s: n_docs < 0", fn);
+  if (n_docs == 0 && n_tokens > 0) return fail(MDLM_EINVAL, "%s: tokens given but n_docs = 0", fn);
+  if (!(eps > 0.0 && eps <= 1.0)) return fail(MDLM_EINVAL, "%s: eps must lie in (0, 1]", fn);
+  if (noise != MDLM_NOISE_ABSORB && noise != MDLM_NOISE_UNIFORM)
+    return fail(MDLM_EINVAL, "%s: unknown noise mode %d", fn, noise);
+  if (noise == MDLM_NOISE_UNIFORM && rand_vocab < 1)
+    return fail(MDLM_EINVAL, "%s: rand_vocab must be >= 1", fn);
+  if (align != MDLM_ALIGNED && align != MDLM_SHIFTED)
+    return fail(MDLM_EINVAL, "%s: unknown alignment %d", fn, align);
+  if (!n_rows) return fail(MDLM_EINVAL, "%s: null n_rows", fn);
+  if (n_tokens > 0 && (!x0 || !xt || !row_idx || !tgt || !w))
+    return fail(MDLM_EINVAL, "%s: null token pointer", fn);
+  if (n_docs > 0 && (!cu_seqlens || !p_doc || !doc_counts))
+    return fail(MDLM_EINVAL, "%s: null document pointer", fn);
+  const size_t need = corrupt_compact_workspace_bytes(n_tokens);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(MDLM_EWORKSPACE, "%s: workspace of %zu bytes, need %zu", fn, workspace_bytes,
+                need);
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) % 8) != 0)
+    return fail(MDLM_EINVAL, "%s: workspace must be 8-byte aligned", fn);
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (const int rc = check_docs(fn, cu_seqlens, n_docs, n_tokens, nullptr, st)) return rc;
+  if (launch_corrupt_compact(x0, n_tokens, cu_seqlens, n_docs, seed, eps, noise, mask_id,
+                             rand_vocab, align, xt, corrupted, p_doc, doc_counts, row_idx, tgt,
+                             w, n_rows, workspace, st) != hipSuccess)
+    return check_launch(fn);
+  return MDLM_OK;
+}
+
 size_t mdlm_compact_workspace_bytes(int64_t n_tokens) {
   return compact_workspace_bytes(n_tokens, 0, MDLM_WEIGHT_INV_P);
 }

@@ -133,6 +133,16 @@ hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, con
                           double clip, int32_t* row_idx, int32_t* tgt, float* w,
                           int32_t* n_rows, void* workspace, hipStream_t stream);
 
+// corruption and the inverse-p row list in one pass (mdlm_corrupt_compact)
+size_t corrupt_compact_workspace_bytes(int64_t n_tokens);
+hipError_t launch_corrupt_compact(const int32_t* x0, int64_t n, const int32_t* cu,
+                                  int32_t n_docs, uint64_t seed, double eps, int32_t noise,
+                                  int32_t mask_id, int32_t rand_vocab, int32_t align,
+                                  int32_t* xt, uint8_t* corrupted, double* p_doc,
+                                  int32_t* doc_counts, int32_t* row_idx, int32_t* tgt,
+                                  float* w, int32_t* n_rows, void* workspace,
+                                  hipStream_t stream);
+
 struct HeadCeArgs {
   const void* hidden;
   const void* W;
