@@ -321,6 +321,31 @@ int mdlm_compact_rows(const uint8_t* corrupted, const uint8_t* eligible,
                       size_t workspace_bytes, void* stream);
 
 /*
+ * mdlm_compact_masked_noalloc -- mdlm_compact_masked for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same rows, targets, weights and
+ * row count, bit for bit, with no workspace argument.
+ *
+ * Its scratch space is an array inside the library, one copy per device,
+ * sized for streams of at most 2^28 tokens (786,688 bytes, held until the
+ * process ends); longer streams return MDLM_EUNSUPPORTED (use
+ * mdlm_compact_masked with a workspace).  The call allocates nothing and
+ * calls no allocating routine.  Every call on a device shares that device's
+ * array, so calls that overlap on one device (on different streams or from
+ * different threads) race and must not be issued; calls on one stream are
+ * ordered and safe.
+ *
+ * Arguments as for mdlm_compact_masked, without workspace and
+ * workspace_bytes.
+ * Returns MDLM_OK, MDLM_EINVAL, MDLM_EUNSUPPORTED or MDLM_EHIP.
+ */
+int mdlm_compact_masked_noalloc(const uint8_t* corrupted, const int32_t* x0,
+                                int64_t n_tokens, const int32_t* cu_seqlens,
+                                int32_t n_docs, const double* p_doc, int32_t align,
+                                int32_t* row_idx, int32_t* tgt, float* w,
+                                int32_t* n_rows, void* stream);
+
+/*
  * mdlm_compact_corrective -- the scored-row list of the corrective mixture,
  * from the codes mdlm_corrupt_mixture writes.
  *

@@ -46,6 +46,7 @@ EXPORTED = (
     "mdlm_corrupt_compact",
     "mdlm_compact_workspace_bytes",
     "mdlm_compact_masked",
+    "mdlm_compact_masked_noalloc",
     "mdlm_compact_corrective",
     "mdlm_compact_rows_workspace_bytes",
     "mdlm_compact_rows",
@@ -100,6 +101,9 @@ def load():
     lib.mdlm_compact_workspace_bytes.restype = sz
     lib.mdlm_compact_masked.argtypes = [vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.mdlm_compact_masked.restype = ctypes.c_int
+    lib.mdlm_compact_masked_noalloc.argtypes = [vp, vp, i64, vp, i32, vp, i32, vp, vp, vp, vp,
+                                                vp]
+    lib.mdlm_compact_masked_noalloc.restype = ctypes.c_int
     lib.mdlm_compact_corrective.argtypes = [vp, vp, i64, vp, i32, vp, i32, f64, f64, vp, vp, vp,
                                             vp, vp, sz, vp]
     lib.mdlm_compact_corrective.restype = ctypes.c_int
@@ -256,6 +260,23 @@ def mdlm_compact_masked(corrupted, x0, cu_seqlens, p_doc, align, row_idx, tgt, w
                                       cu_seqlens.numel() - 1, _ptr(p_doc), int(align),
                                       _ptr(row_idx), _ptr(tgt), _ptr(w), _ptr(n_rows),
                                       _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def mdlm_compact_masked_noalloc(corrupted, x0, cu_seqlens, p_doc, align, row_idx, tgt, w,
+                                n_rows, stream=None):
+    """See mdlm_compact_masked_noalloc in include/mdlm.h (no workspace)."""
+    _need(corrupted, torch.uint8, "corrupted")
+    _need(x0, torch.int32, "x0")
+    _need(cu_seqlens, torch.int32, "cu_seqlens")
+    _need(p_doc, torch.float64, "p_doc")
+    _need(row_idx, torch.int32, "row_idx")
+    _need(tgt, torch.int32, "tgt")
+    _need(w, torch.float32, "w")
+    _need(n_rows, torch.int32, "n_rows")
+    _check(load().mdlm_compact_masked_noalloc(
+        _ptr(corrupted), _ptr(x0), x0.numel(), _ptr(cu_seqlens), cu_seqlens.numel() - 1,
+        _ptr(p_doc), int(align), _ptr(row_idx), _ptr(tgt), _ptr(w), _ptr(n_rows),
+        _stream(stream)))
 
 
 def mdlm_compact_corrective(codes, x0, cu_seqlens, p_doc, align, noise_token_wt,

@@ -223,6 +223,28 @@ int mdlm_compact_masked(const uint8_t* corrupted, const int32_t* x0, int64_t n_t
                         n_rows, workspace, workspace_bytes, stream);
 }
 
+int mdlm_compact_masked_noalloc(const uint8_t* corrupted, const int32_t* x0, int64_t n_tokens,
+                                const int32_t* cu_seqlens, int32_t n_docs, const double* p_doc,
+                                int32_t align, int32_t* row_idx, int32_t* tgt, float* w,
+                                int32_t* n_rows, void* stream) {
+  clear_error();
+  const char* fn = "mdlm_compact_masked_noalloc";
+  if (n_tokens > kNoAllocMaxTokens)
+    return fail(MDLM_EUNSUPPORTED, "%s: n_tokens = %lld exceeds the %lld tokens its scratch "
+                "array serves (use mdlm_compact_masked with a workspace)", fn,
+                (long long)n_tokens, (long long)kNoAllocMaxTokens);
+  void* scratch = nullptr;
+  const size_t need = compact_workspace_bytes(n_tokens, n_docs, MDLM_WEIGHT_INV_P);
+  if (need > 0 && compact_scratch(&scratch) != hipSuccess)
+    return fail(MDLM_EHIP, "%s: no scratch array on this device", fn);
+  if (need > compact_scratch_bytes())
+    return fail(MDLM_EUNSUPPORTED, "%s: workspace of %zu bytes exceeds the scratch array", fn,
+                need);
+  return compact_common(fn, true, corrupted, nullptr, x0, n_tokens, cu_seqlens, n_docs, p_doc,
+                        align, MDLM_WEIGHT_INV_P, 1.0, 0.0, row_idx, tgt, w, n_rows, scratch,
+                        compact_scratch_bytes(), stream);
+}
+
 int mdlm_compact_corrective(const uint8_t* codes, const int32_t* x0, int64_t n_tokens,
                             const int32_t* cu_seqlens, int32_t n_docs, const double* p_doc,
                             int32_t align, double noise_token_wt, double clean_token_wt,

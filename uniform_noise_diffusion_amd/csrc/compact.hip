@@ -35,6 +35,7 @@
 #include "mdlm_internal.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace mdlm {
 namespace {
@@ -712,5 +713,50 @@ hipError_t launch_compact_corrective(const uint8_t* codes, const int32_t* x0, in
   }
   return hipGetLastError();
 }
+
+// ---- the allocation-free variant of mdlm_compact_masked -------------------
+// Its workspace is `scratch`, a file-scope device array sized for
+// kNoAllocMaxTokens tokens; each device holds its own copy, whose address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and kept.  Host code passes that address, never the array's name (which is
+// a host-side stand-in), to the kernels.  Nothing in it needs clearing: the
+// passes write every word they later read.  Calls on one device share the
+// array, so calls that overlap on one device race.
+namespace {
+
+constexpr int64_t kNoAllocTiles = (kNoAllocMaxTokens + kTile - 1) / kTile;
+constexpr int64_t kNoAllocWords = 3 * kNoAllocTiles + (kNoAllocTiles + kGroup - 1) / kGroup;
+
+__device__ __align__(256) int32_t scratch[kNoAllocWords];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // per device, once looked up
+
+}  // namespace
+
+static_assert(kNoAllocWords * sizeof(int32_t) ==
+                  3 * kNoAllocTiles * sizeof(int32_t) +
+                      ((kNoAllocTiles + kGroup - 1) / kGroup) * sizeof(int32_t),
+              "scratch holds the inverse-p workspace of kNoAllocMaxTokens tokens");
+
+hipError_t compact_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+size_t compact_scratch_bytes() { return (size_t)kNoAllocWords * sizeof(int32_t); }
 
 }  // namespace mdlm

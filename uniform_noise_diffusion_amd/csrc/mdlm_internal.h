@@ -120,6 +120,12 @@ hipError_t launch_corrupt(const int32_t* x0, int64_t n_tokens, const int32_t* cu
                           hipStream_t stream, double mixture_prob = 0.0);
 
 size_t compact_workspace_bytes(int64_t n_tokens, int32_t n_docs, int32_t weighting);
+// mdlm_compact_masked_noalloc: the largest stream its device scratch array
+// serves, that array's size, and (looked up once per device) its address on
+// the current device
+constexpr int64_t kNoAllocMaxTokens = (int64_t)1 << 28;
+size_t compact_scratch_bytes();
+hipError_t compact_scratch(void** ptr);
 // the corrective mixture's row list (mdlm_compact_corrective); workspace as
 // for the inverse-p weighting
 hipError_t launch_compact_corrective(const uint8_t* codes, const int32_t* x0, int64_t n,
