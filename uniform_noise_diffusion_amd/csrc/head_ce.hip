@@ -54,6 +54,7 @@ namespace {
 typedef __bf16 bf16_t;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 constexpr int kThreads = 256;         // reduction and utility kernels
 #ifndef MDLM_GEMM_WAVES
@@ -440,6 +441,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
       wait_vmem();
     };
     with_count<kNJ>(kj, kloop);
+    // the variants that write G stage it through the stage memory, which
+    // other waves may still be reading (their last K step) or filling (the
+    // unconsumed prefetch) until all of them are here
+    if constexpr (kStash || kGrad) __syncthreads();
 
     // ---- epilogue ---------------------------------------------------------
     // Accumulator element e of block (i, j) on lane l holds vocabulary entry
@@ -449,6 +454,42 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
     // tile that straddles v_end masks entries past the vocabulary.
     const int vl = v0 + wa * 128 + 4 * (lane >> 5);
     const int lim = a.v_end - vl;
+    // G goes out through LDS: a lane's 4-entry pieces of a block land in
+    // this wave's own 32 rows of 256 B (pitch 272 B, so that neither side
+    // conflicts on banks and every address is one base plus a constant) and
+    // leave as whole 256-B row segments, 16 B a lane, instead of 8 B in
+    // each of 32 rows per store.  The blocks of a wave reuse the region.
+    constexpr int kPitch = 272;
+    static_assert(4 * 32 * kPitch <= kStageBytes, "staging fits a stage");
+    char* const st = (wave < 4 ? smem0 : smem1) + (wave & 3) * (32 * kPitch);
+    auto stage_put = [&](int i, int q, uint2 v) __attribute__((always_inline)) {
+      *reinterpret_cast<uint2*>(st + (lane & 31) * kPitch + 8 * (lane >> 5) + 16 * (4 * i + q)) =
+          v;
+    };
+    auto stage_flush = [&](int j) __attribute__((always_inline)) {
+      // LDS work of one wave completes in order; the wait and the clobbers
+      // keep the compiler from moving the reads above this block's writes
+      // or the next block's writes above them.  The stores go through a
+      // buffer that ends at row n_rows, so rows past it are dropped by the
+      // hardware (no branch), and share one lane offset.
+      sched_fence();
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      u32x4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[k] = *reinterpret_cast<const u32x4*>(st + ((lane >> 4) + 4 * k) * kPitch +
+                                               16 * (lane & 15));
+      asm volatile("" ::: "memory");
+      const int rb = m0 + 32 * wb + kRowStride * j;
+      const int col = v0 - a.v_begin + wa * 128;
+      const __amdgpu_buffer_rsrc_t rg =
+          make_rsrc(a.G + (int64_t)rb * a.ldg + col, (int64_t)(n_rows - rb) * a.ldg * 2 - 2 * col);
+      const uint32_t voff = (uint32_t)(((lane >> 4) * a.ldg + 8 * (lane & 15)) * 2);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(v[k], rg, voff, (uint32_t)(8 * k * a.ldg), 0);
+      sched_fence();
+    };
     auto epilogue = [&](auto full_tag) __attribute__((always_inline)) {
       constexpr bool kFull = decltype(full_tag)::value;
 #pragma unroll
@@ -492,7 +533,6 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
             fs = mx == -INFINITY ? 0.f : near ? __builtin_amdgcn_exp2f(mx - R) : 1.f;
           }
           float sum = 0.f;
-          bf16_t* grow = a.G + (int64_t)m * a.ldg - a.v_begin;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -513,21 +553,21 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
                   g[r] = gv;
                 }
               }
-              if (kStash && mvalid)
-                *reinterpret_cast<uint2*>(grow + vl + 32 * i + 8 * q) =
-                    make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
+              if (kStash)
+                stage_put(i, q, make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])));
             }
+          if (kStash) stage_flush(j);
           sum += __shfl_xor(sum, 32, 64);
           if (lane < 32 && mvalid)
             a.partial[(int64_t)m * a.n_part + 2 * ((v0 - a.v_begin) / kTile) + wa] =
                 make_float2(mx, sum);
-        } else if (mvalid) {
+        } else {
           // G = w p cap' everywhere, then the target entry is rewritten with
           // w (p - 1) cap' from the capped target logit the forward pass kept
-          // (the same tile product)
-          const float lse2 = a.lse[m] * kLog2e;
-          const float wm = a.w[m];
-          bf16_t* grow = a.G + (int64_t)m * a.ldg - a.v_begin;
+          // (the same tile product).  Lanes of rows past n_rows stage
+          // zeros that are never stored.
+          const float lse2 = mvalid ? a.lse[m] * kLog2e : 0.f;
+          const float wm = mvalid ? a.w[m] : 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -542,10 +582,9 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
                 g[r] = kCap ? p * dc * wm : p * wm;
                 if (!kFull) g[r] = off < lim ? g[r] : 0.f;
               }
-              *reinterpret_cast<uint2*>(grow + vl + 32 * i + 8 * q) =
-                  make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]));
+              stage_put(i, q, make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])));
             }
-          if (holds_tgt) {
+          if (mvalid && holds_tgt) {
             const float zt2 = a.ztgt[m];
             float dc = 1.f;
             if (kCap) {
@@ -553,8 +592,11 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
               dc = 1.f - th * th;
             }
             const float p = __builtin_amdgcn_exp2f(zt2 - lse2);
-            grow[tg] = (bf16_t)((p - 1.f) * dc * wm);
+            // (over the piece this lane staged above: program order)
+            *reinterpret_cast<bf16_t*>(st + (lane & 31) * kPitch + 2 * (tg - (v0 + wa * 128))) =
+                (bf16_t)((p - 1.f) * dc * wm);
           }
+          stage_flush(j);
         }
       }
     };
