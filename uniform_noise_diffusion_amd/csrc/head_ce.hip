@@ -114,6 +114,28 @@ __device__ __forceinline__ int logical_block() {
                          : (int)((blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3));
 }
 
+// Tile (r, c) of an nr x nc grid for the linear index t, visited in blocks of
+// gr x gc tiles: bands of gr rows one after another, the blocks of a band
+// along c, each block row by row.  The tiles running at one time on an XCD
+// then form a block (a few rows and columns of operand slabs instead of one
+// row against every column, or the reverse), and the XCDs running beside it
+// walk the same band, so that its slabs are fetched once for all of them.
+// A bijection onto the grid for any sizes (edge bands and blocks are
+// smaller).
+__device__ __forceinline__ void grouped_tile(int64_t t, int nr, int nc, int gr, int gc, int* r,
+                                             int* c) {
+  const int64_t band = (int64_t)gr * nc;
+  const int br = (int)(t / band);
+  const int64_t rem = t - (int64_t)br * band;
+  const int sr = min(gr, nr - br * gr);
+  const int64_t blk = (int64_t)sr * gc;
+  const int bc = (int)(rem / blk);
+  const int64_t rem2 = rem - (int64_t)bc * blk;
+  const int sc = min(gc, nc - bc * gc);
+  *r = br * gr + (int)(rem2 / sc);
+  *c = bc * gc + (int)(rem2 - (rem2 / sc) * sc);
+}
+
 __device__ __forceinline__ float softcap_fwd(float z, float c, float inv_c, float* dcap) {
   // c * tanh(z / c) with tanh(x) = 1 - 2 / (1 + e^{2x}); saturates cleanly.
   const float e = __builtin_amdgcn_exp2f(z * inv_c * (2.0f * kLog2e));
@@ -331,7 +353,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
   const int lrow = lane >> 3, lphys = lane & 7;
 
   for (int64_t t = logical_block(); t < n_tiles; t += gridDim.x) {
-    const int vt = (int)(t / n_mt), mt = (int)(t % n_mt);
+    // bands of 4 vocabulary tiles (W, the larger operand, shared by the
+    // XCDs of a band), blocks of 4 x 8
+    int vt, mt;
+    grouped_tile(t, n_vt, n_mt, 4, 8, &vt, &mt);
     const int v0 = a.v_begin + vt * kTile;
     const int m0 = mt * kTile;
 
@@ -679,7 +704,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
   for (int64_t u = logical_block(); u < units; u += gridDim.x) {
     const int s = (int)(u / T);
     const int64_t tile = u % T;
-    const int mt = (int)(tile % n_mt), ht = (int)(tile / n_mt);
+    // bands of 8 row tiles (G, the larger operand, shared by the XCDs of a
+    // band), blocks of 8 x 4
+    int mt, ht;
+    grouped_tile(tile, n_mt, n_ht, 8, 4, &mt, &ht);
     const int m0 = mt * kTile, h0 = ht * kTile;
     const int kb = (int)((int64_t)KI * s / S), ke = (int)((int64_t)KI * (s + 1) / S);
 
@@ -844,7 +872,9 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dw_kernel(DwArgs a) {
   const int nrow = lane >> 5, nphys = lane & 31;  // N-major loads
 
   for (int64_t t = logical_block(); t < T; t += gridDim.x) {
-    const int vt = (int)(t / n_ht), ht = (int)(t % n_ht);
+    // bands of 4 vocabulary tiles (G, the larger operand), blocks of 4 x 8
+    int vt, ht;
+    grouped_tile(t, n_vt, n_ht, 4, 8, &vt, &ht);
     const int v0 = vt * kTile;  // column of G
     const int h0 = ht * kTile;
     uint32_t a_voff[2], b_voff[2];
