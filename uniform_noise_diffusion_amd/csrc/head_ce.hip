@@ -315,6 +315,100 @@ __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB r
   }
 }
 
+// The K loop of the MFMA kernels over steps [kb, ke) of kBK: two LDS stages
+// s0 and s1, operands loaded straight into LDS by issue(stage, k0), and
+// fragments read by ra(stage, kk, f) and rb(stage, kk, f) for 16-deep slice
+// kk.  Each step's barrier sits before its last slice, whose fragments are
+// already in registers: after the barrier its MFMAs run while the step two
+// ahead is loaded into the stage just finished and the first fragments of
+// the next stage are read, so no wave waits on LDS latency after a barrier.
+// At the barrier every wave is past its reads of the current stage and has
+// waited for its own loads into the next one.  The loads of the two steps
+// past ke read in-range bytes or zeros and are never consumed; the wait at
+// the end retires them.  Only the first NI A blocks and NJ B blocks take
+// part (NI NJ = 0: loads and barriers only); kReads counts a slice's LDS
+// read instructions (transpose reads twice).
+template <int NI, int NJ, int kReads, typename ReadA, typename ReadB, typename Issue>
+__device__ __forceinline__ void kloop_pipe(f32x16 (&acc)[4][kNJ], int kb, int ke, char* s0,
+                                           char* s1, ReadA ra, ReadB rb, Issue issue) {
+  constexpr int kMfma = NI * NJ;
+  constexpr int kV = 2 * kLoads;  // loads per issue()
+  constexpr int kSlices = kBK / 16;
+  bf16x8 af[2][4], bfr[2][kNJ];
+  auto mfmas = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j],
+                                                            0, 0, 0);
+  };
+  __syncthreads();  // the previous tile is done with both stages
+  issue(s0, kb * kBK);
+  issue(s1, (kb + 1) * kBK);
+  // s0's loads only (the kV loads into s1 stay in flight)
+  static_assert(kV == 8 || kV == 16, "vmcnt immediate");
+  if constexpr (kV == 8)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  __syncthreads();
+  if constexpr (kMfma > 0) {
+    ra(s0, 0, af[0]);
+    rb(s0, 0, bfr[0]);
+  }
+  auto step = [&](char* cur, char* nxt, int kt) __attribute__((always_inline)) {
+    if constexpr (kMfma > 0) {
+#pragma unroll
+      for (int kk = 0; kk + 1 < kSlices; ++kk) {
+        ra(cur, kk + 1, af[(kk + 1) & 1]);
+        rb(cur, kk + 1, bfr[(kk + 1) & 1]);
+        mfmas(kk & 1);
+      }
+      // each slice's MFMAs alternated one for one with the next slice's reads
+#pragma unroll
+      for (int kk = 0; kk + 1 < kSlices; ++kk) {
+#pragma unroll
+        for (int x = 0; x < kMfma; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (x < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int x = kMfma; x < kReads; ++x) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    sched_fence();
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue(cur, (kt + 2) * kBK);
+    if constexpr (kMfma > 0) {
+      ra(nxt, 0, af[0]);
+      rb(nxt, 0, bfr[0]);
+      mfmas((kSlices - 1) & 1);
+      // the last slice's MFMAs, each after one load and before one read
+#pragma unroll
+      for (int x = 0; x < kMfma; ++x) {
+        if (x < kV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (x < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int x = kMfma; x < kV; ++x) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+#pragma unroll
+      for (int x = kMfma; x < kReads; ++x) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    sched_fence();
+  };
+  // two steps per trip so that each access names its stage statically
+  int kt = kb;
+  for (; kt + 2 <= ke; kt += 2) {
+    step(s0, s1, kt);
+    step(s1, s0, kt + 1);
+  }
+  if (kt < ke) step(s0, s1, kt);
+  wait_vmem();
+}
+
 // Tile of 256 vocabulary rows (operand A, rows of W) by 256 scored rows
 // (operand B, rows of hidden gathered through row_idx), K = H.  Wave w owns
 // vocabulary rows 128 (w % 2) .. +127 and the scored-row blocks
@@ -419,51 +513,21 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
     // the same loads and barriers whatever their count)
     auto kloop = [&](auto nj_tag) __attribute__((always_inline)) {
       constexpr int NJ = decltype(nj_tag)::value;
-      auto compute = [&](const char* base, auto vmem) __attribute__((always_inline)) {
-        if constexpr (NJ > 0)
-          mma_k64<4 + NJ, decltype(vmem)::value, 4, NJ>(
-              acc,
-              [&](int kk, bf16x8(&f)[4]) {
-                const int coff = ((2 * kk + khalf) ^ fx) * 16;
+      kloop_pipe<4, NJ, 4 + NJ>(
+          acc, 0, KT, smem0, smem1,
+          [&](const char* base, int kk, bf16x8(&f)[4]) __attribute__((always_inline)) {
+            const int coff = ((2 * kk + khalf) ^ fx) * 16;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
-              },
-              [&](int kk, bf16x8(&f)[kNJ]) {
-                const int coff = ((2 * kk + khalf) ^ fx) * 16;
+            for (int i = 0; i < 4; ++i)
+              f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
+          },
+          [&](const char* base, int kk, bf16x8(&f)[kNJ]) __attribute__((always_inline)) {
+            const int coff = ((2 * kk + khalf) ^ fx) * 16;
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                  f[j] = *reinterpret_cast<const bf16x8*>(base + b_off + j * kRowStride * kKRow +
-                                                          coff);
-              });
-      };
-      __syncthreads();  // the previous tile is done with both stages
-      issue(smem0, 0);
-      // two K steps per trip so that each access names its stage statically;
-      // an odd last step runs after the loop.  The prefetch into smem0 is
-      // unconditional so that it shares a basic block (and so a scheduling
-      // region) with the MFMAs it is interleaved with: on the last trip of an
-      // even KT it reads past K (in-range bytes or zeros), is never consumed,
-      // and the wait after the loop retires it before the stage is reused.
-      int kt = 0;
-      for (; kt + 2 <= KT; kt += 2) {
-        wait_vmem();
-        __syncthreads();
-        issue(smem1, (kt + 1) * kBK);
-        compute(smem0, kInterleave);
-        sched_fence();
-        wait_vmem();
-        __syncthreads();
-        issue(smem0, (kt + 2) * kBK);
-        compute(smem1, kInterleave);
-        sched_fence();
-      }
-      if (kt < KT) {
-        wait_vmem();
-        __syncthreads();
-        compute(smem0, kNoLoads);
-      }
-      wait_vmem();
+            for (int j = 0; j < NJ; ++j)
+              f[j] = *reinterpret_cast<const bf16x8*>(base + b_off + j * kRowStride * kKRow + coff);
+          },
+          issue);
     };
     with_count<kNJ>(kj, kloop);
     // the variants that write G stage it through the stage memory, which
@@ -750,53 +814,26 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
     const int ki = max(0, (nv - 32 * wa + 63) / 64);
     auto kloop = [&](auto ni_tag) __attribute__((always_inline)) {
       constexpr int NI = decltype(ni_tag)::value;
-      auto compute = [&](const char* base, auto vmem) __attribute__((always_inline)) {
-        const char* bb = base + kOpBytes;
-        if constexpr (NI > 0)
-          mma_k64<NI + 2 * kNJ, decltype(vmem)::value, NI, kNJ>(
-              acc,
-              [&](int kk, bf16x8(&f)[4]) {
-                const int coff = ((2 * kk + khalf) ^ fx) * 16;
+      kloop_pipe<NI, kNJ, NI + 2 * kNJ>(
+          acc, kb, ke, smem0, smem1,
+          [&](const char* base, int kk, bf16x8(&f)[4]) __attribute__((always_inline)) {
+            const int coff = ((2 * kk + khalf) ^ fx) * 16;
 #pragma unroll
-                for (int i = 0; i < NI; ++i)
-                  f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 64 * kKRow + coff);
-              },
-              [&](int kk, bf16x8(&f)[kNJ]) {
-                const char* brow_p = bb + (16 * kk + tr_row) * kNRow;
+            for (int i = 0; i < NI; ++i)
+              f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 64 * kKRow + coff);
+          },
+          [&](const char* base, int kk, bf16x8(&f)[kNJ]) __attribute__((always_inline)) {
+            const char* brow_p = base + kOpBytes + (16 * kk + tr_row) * kNRow;
 #pragma unroll
-                for (int j = 0; j < kNJ; ++j) {
-                  const shortx4 lo = ds_read_tr(brow_p + b_col_off[j]);
-                  const shortx4 hi = ds_read_tr(brow_p + 4 * kNRow + b_col_off[j]);
-                  const short v8 __attribute__((__vector_size__(16))) = {
-                      lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                  f[j] = __builtin_bit_cast(bf16x8, v8);
-                }
-              });
-      };
-
-      __syncthreads();
-      issue(smem0, kb * kBK);
-      // same pipeline as the logits tiles (unconditional last prefetch,
-      // retired by the wait after the loop)
-      int kt = kb;
-      for (; kt + 2 <= ke; kt += 2) {
-        wait_vmem();
-        __syncthreads();
-        issue(smem1, (kt + 1) * kBK);
-        compute(smem0, kInterleave);
-        sched_fence();
-        wait_vmem();
-        __syncthreads();
-        issue(smem0, (kt + 2) * kBK);
-        compute(smem1, kInterleave);
-        sched_fence();
-      }
-      if (kt < ke) {
-        wait_vmem();
-        __syncthreads();
-        compute(smem0, kNoLoads);
-      }
-      wait_vmem();
+            for (int j = 0; j < kNJ; ++j) {
+              const shortx4 lo = ds_read_tr(brow_p + b_col_off[j]);
+              const shortx4 hi = ds_read_tr(brow_p + 4 * kNRow + b_col_off[j]);
+              const short v8 __attribute__((__vector_size__(16))) = {
+                  lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              f[j] = __builtin_bit_cast(bf16x8, v8);
+            }
+          },
+          issue);
     };
     with_count<4>(ki, kloop);
 
