@@ -22,6 +22,8 @@ timed on a bounded sample of the same workload.
 """
 
 import argparse
+import contextlib
+import gc
 import json
 import os
 import sys
@@ -70,6 +72,20 @@ def parse():
                                                           "head_ce_traffic.json"),
                    help="measured HBM traffic of the fused call, if current")
     return p.parse_args()
+
+
+@contextlib.contextmanager
+def quiet_host():
+    """No Python garbage collection inside a timed region: a collection that
+    lands between a start event and the launches after it (when the GPU
+    queue is empty) shows up in the event time as a gap with no kernel
+    running."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
 
 
 def head_source_sha256():
@@ -122,13 +138,14 @@ def gpu_steps(args, inp, dev):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(K):
-        one(i, evs[i])
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with quiet_host():
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(K):
+            one(i, evs[i])
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
     head_ms = [e[1].elapsed_time(e[2]) for e in evs]
     step_ms = [e[0].elapsed_time(e[2]) for e in evs]
@@ -173,15 +190,19 @@ def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
     torch.cuda.synchronize()
     ec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for i in range(reps):
-        ec[i][0].record()
-        step.corrupt(x0, cu, 100 + i, 1e-3, 0, 126336, 126464)
-        ec[i][1].record()
-        step.compact(x0, cu, 0)
-        ec[i][2].record()
-    torch.cuda.synchronize()
-    t_cor = np.mean([a.elapsed_time(b) for a, b, _ in ec]) * 1e-3
-    t_cmp = np.mean([b.elapsed_time(c) for _, b, c in ec]) * 1e-3
+    with quiet_host():
+        for i in range(reps):
+            ec[i][0].record()
+            step.corrupt(x0, cu, 100 + i, 1e-3, 0, 126336, 126464)
+            ec[i][1].record()
+            step.compact(x0, cu, 0)
+            ec[i][2].record()
+        torch.cuda.synchronize()
+    # medians over the repetitions (the per-repetition times are reported too)
+    r_cor = [a.elapsed_time(b) * 1e3 for a, b, _ in ec]
+    r_cmp = [b.elapsed_time(c) * 1e3 for _, b, c in ec]
+    t_cor = float(np.median(r_cor)) * 1e-6
+    t_cmp = float(np.median(r_cmp)) * 1e-6
     m = int(step.n_rows.item())
     # the one-pass call: the same outputs as the two calls above
     from uniform_noise_diffusion_amd import binding as B
@@ -196,12 +217,14 @@ def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
     torch.cuda.synchronize()
     ef = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
-    for i in range(reps):
-        ef[i][0].record()
-        fused(100 + i)
-        ef[i][1].record()
-    torch.cuda.synchronize()
-    t_fused = np.mean([a.elapsed_time(b) for a, b in ef]) * 1e-3
+    with quiet_host():
+        for i in range(reps):
+            ef[i][0].record()
+            fused(100 + i)
+            ef[i][1].record()
+        torch.cuda.synchronize()
+    r_fused = [a.elapsed_time(b) * 1e3 for a, b in ef]
+    t_fused = float(np.median(r_fused)) * 1e-6
     m_fused = int(step.n_rows.item())
     b_fused = 9.0 * n + 12.0 * m_fused
     # algorithmic bytes: corrupt reads x0 (4 B) and writes xt (4 B) and the
@@ -218,6 +241,11 @@ def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
                 fused_us=t_fused * 1e6, fused_GBs=b_fused / t_fused / 1e9,
                 fused_frac=b_fused / t_fused / 1e9 / PEAK_HBM_GBS,
                 two_calls_us=(t_cor + t_cmp) * 1e6,
+                timing=(f"medians over {reps} calls (HIP events on the launch stream); per call "
+                        "below, in us"),
+                corrupt_us_per_call=[round(x, 1) for x in r_cor],
+                compact_us_per_call=[round(x, 1) for x in r_cmp],
+                fused_us_per_call=[round(x, 1) for x in r_fused],
                 fused_what=("mdlm_corrupt_compact (corruption and the row list in one pass); "
                             "algorithmic bytes 9 per token (x0 read, xt and mask written) + "
                             "12 per scored row (row, target, weight written; the target is the "
@@ -295,11 +323,12 @@ def _timed(fn, reps):
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
-    for a, b in ev:
-        a.record()
-        fn()
-        b.record()
-    torch.cuda.synchronize()
+    with quiet_host():
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
 
 
