@@ -170,26 +170,26 @@ int mdlm_corrupt_mixture(const int32_t* x0, int64_t n_tokens, const int32_t* cu_
                          void* stream);
 
 /*
- * Workspace bytes that mdlm_corrupt_compact needs for n_tokens tokens: 16
- * bytes per 4096-token tile and 16 more.  Returns 0 for n_tokens <= 0.
+ * Workspace bytes that mdlm_corrupt_compact needs for n_tokens tokens:
+ * mdlm_compact_workspace_bytes(n_tokens) and one byte per token (the mask,
+ * kept there when the caller passes no `corrupted`), each rounded up to 256.
+ * Returns 0 for n_tokens <= 0.
  */
 size_t mdlm_corrupt_compact_workspace_bytes(int64_t n_tokens);
 
 /*
- * mdlm_corrupt_compact -- mdlm_corrupt followed by mdlm_compact_masked, in
- * one pass over the tokens: the same xt, corrupted, p_doc, doc_counts,
- * row_idx, tgt, w and n_rows, bit for bit.
+ * mdlm_corrupt_compact -- mdlm_corrupt followed by mdlm_compact_masked
+ * (inverse-p weights) in one call: the same xt, corrupted, p_doc,
+ * doc_counts, row_idx, tgt, w and n_rows, bit for bit.
  *
  * Defined by: as for mdlm_corrupt and mdlm_compact_masked (LLaDA-8B-MDLM-
  * LoRA card, Training table, "Objective" row; diffusiongemma card,
  * "Finetuning notes"; Axolotl docs, model table and "Packed training").
  *
- * Each 4096-token tile is read once: its tokens are corrupted and written
- * back, and its scored rows go straight to their place in the list (the
- * rows of all earlier tiles, summed by a look-back over per-tile counts the
- * tiles publish as they go).  Traffic: 9 bytes per token plus 12 per scored
- * row, against about 19 per token for the two calls at half the tokens
- * scored.
+ * The corruption pass also counts each 4096-token tile's corrupted tokens
+ * (the compaction's tiles), so the compaction skips its own count pass over
+ * the mask: one read of the mask (1 byte per token) and one launch fewer than
+ * the two calls.
  *
  *   x0, n_tokens, cu_seqlens, n_docs, seed, eps, noise, mask_id, rand_vocab:
  *               as for mdlm_corrupt.
@@ -199,9 +199,7 @@ size_t mdlm_corrupt_compact_workspace_bytes(int64_t n_tokens);
  *   p_doc       [n_docs] double out.
  *   doc_counts  [n_docs] int32 out.
  *   row_idx, tgt, w   [n_tokens] out (first *n_rows valid).
- *   n_rows      [1] int32 out (device scalar).  -1 would mean that a tile's
- *               bounded wait for its predecessors expired (the list is then
- *               incomplete); a launch that follows this header never sees it.
+ *   n_rows      [1] int32 out (device scalar).
  *   workspace   >= mdlm_corrupt_compact_workspace_bytes(n_tokens) bytes of
  *               device memory, 8-byte aligned; contents on entry are ignored.
  * Calls sharing a workspace must not overlap.

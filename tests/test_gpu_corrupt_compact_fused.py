@@ -1,5 +1,6 @@
 """GPU parity of mdlm_corrupt_compact (corruption and the row list in one
-pass) against the oracle: every output bit for bit (xt, corrupted, p_doc's
+call, the compaction sized by the corruption's per-tile counts) against the
+oracle: every output bit for bit (xt, corrupted, p_doc's
 fp64 bits, doc_counts, n_rows, row_idx, tgt, w's fp32 bits), on the layouts
 the two-call tests use (tiny and empty documents, documents spanning tiles,
 more documents per tile than it caches, one-tile streams, many tiles), on the
@@ -125,8 +126,7 @@ def test_fused_bit_exact_workloads(k, align):
 
 def test_fused_reused_workspace_and_buffers():
     """Three calls in a row on one workspace and one set of outputs, the
-    stream shrinking and growing: the look-back state of each call starts
-    clean."""
+    stream shrinking and growing: the tile counts of each call start clean."""
     x_big, cu_big = _case(21, 400, 900)
     x_small, cu_small = _case(22, 30, 700)
     n = x_big.shape[0]

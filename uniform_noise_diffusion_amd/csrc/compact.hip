@@ -151,13 +151,18 @@ __device__ __forceinline__ int lanes_below(uint64_t b) {
 // Offsets that break the preconditions (negative, decreasing, past n) are
 // clipped to [0, n] first, so every write stays inside the two tables; the
 // tables' contents are then unspecified, and tile_range clamps what it reads.
+// With start_mask (tile counts of corrupted tokens given, shifted rows): a
+// document whose first token is marked takes that token out of its tile's
+// count, which then counts the tile's scored rows.
 __global__ void __launch_bounds__(kThreads)
 tile_docs_kernel(const int32_t* __restrict__ cu, int32_t n_docs, int64_t n,
-                 int32_t* __restrict__ tile_lo, int32_t* __restrict__ tile_hi) {
+                 int32_t* __restrict__ tile_lo, int32_t* __restrict__ tile_hi,
+                 const uint8_t* __restrict__ start_mask, int32_t* __restrict__ tile_counts) {
   const int b = blockIdx.x * kThreads + threadIdx.x;
   if (b >= n_docs) return;
   const int64_t beg = max<int64_t>(cu[b], 0), end = min<int64_t>(cu[b + 1], n);
   if (beg >= end) return;
+  if (start_mask && start_mask[beg]) atomicSub(&tile_counts[beg / kTile], 1);
   // tiles whose first token 4096 k lies in [beg, end)
   for (int64_t k = (beg + kTile - 1) / kTile; k * kTile < end; ++k) tile_lo[k] = b;
   // tiles whose last token min(4096 (k + 1), n) - 1 lies in [beg, end)
@@ -297,7 +302,8 @@ group_scan_kernel(int32_t* __restrict__ tile_counts, int64_t n_tiles,
   __shared__ int s_wave[kGroup / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t i = (int64_t)blockIdx.x * kGroup + tid;
-  const int v = i < n_tiles ? tile_counts[i] : 0;
+  // (negative only when the offsets break their preconditions)
+  const int v = i < n_tiles ? max(tile_counts[i], 0) : 0;
   int incl = v;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -569,6 +575,7 @@ struct Launch {
   hipStream_t stream;
   CodeWeights cwt;  // corrective mixture only
   bool single;      // one tile, per-document weights needing no totals: scatter alone
+  bool counts_given;  // the tile counts are in place (from the corruption pass)
 };
 
 // The passes after tile_docs_kernel, for one combination of alignment and
@@ -595,9 +602,11 @@ void run_passes(const Launch& L, RowMasks<kC, kE> mk) {
                                                               L.doc_rows);
     examples_kernel<<<1, 1024, 0, st>>>(L.doc_rows, L.n_docs, L.n_examples);
   }
-  const unsigned count_grid = (unsigned)((L.tiles + kWaves - 1) / kWaves);
-  count_kernel<kShifted, kC, kE><<<count_grid, kThreads, 0, st>>>(
-      mk, L.n, L.cu, L.n_docs, L.tile_lo, L.tile_hi, L.tiles, L.counts);
+  if (!L.counts_given) {
+    const unsigned count_grid = (unsigned)((L.tiles + kWaves - 1) / kWaves);
+    count_kernel<kShifted, kC, kE><<<count_grid, kThreads, 0, st>>>(
+        mk, L.n, L.cu, L.n_docs, L.tile_lo, L.tile_hi, L.tiles, L.counts);
+  }
   group_scan_kernel<<<(unsigned)L.groups, kGroup, 0, st>>>(L.counts, L.tiles, L.group_sums);
   if (L.w_doc)
     doc_weights_kernel<<<(unsigned)((L.n_docs + kThreads - 1) / kThreads), kThreads, 0, st>>>(
@@ -622,7 +631,7 @@ hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, con
                           int64_t n, const int32_t* cu, int32_t n_docs, const double* p_doc,
                           int32_t align, int32_t weighting, double scale, double clip,
                           int32_t* row_idx, int32_t* tgt, float* w, int32_t* n_rows,
-                          void* workspace, hipStream_t stream) {
+                          void* workspace, hipStream_t stream, bool counts_given) {
   if (n <= 0) {
     set_int_kernel<<<1, 1, 0, stream>>>(n_rows, 0);
     return hipGetLastError();
@@ -649,16 +658,18 @@ hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, con
   // a single tile with per-document weights needs none of the passes before
   // the scatter
   const bool single = tiles == 1 && weighting == MDLM_WEIGHT_INV_P;
+  const bool shifted = align == MDLM_SHIFTED;
+  // (given counts are of corrupted tokens: only with the mask alone)
+  counts_given = counts_given && corrupted && !eligible;
   if (!single)
     tile_docs_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
-        cu, n_docs, n, tile_lo, tile_hi);
+        cu, n_docs, n, tile_lo, tile_hi, counts_given && shifted ? corrupted : nullptr, counts);
   const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)corrupted % 4 == 0) &&
                    ((uintptr_t)eligible % 4 == 0);
   const Launch L{n,        cu,     n_docs, tiles,     groups, counts,    tile_lo,
                  tile_hi,  group_sums, doc_rows, n_examples, w_doc, x0, wa,
                  row_idx,  tgt,    w,      n_rows,    vec,    stream,    CodeWeights{},
-                 single};
-  const bool shifted = align == MDLM_SHIFTED;
+                 single,   counts_given};
   const int key = (shifted ? 4 : 0) | (corrupted ? 2 : 0) | (eligible ? 1 : 0);
   switch (key) {
     case 0: run_passes<false, false, false>(L, {corrupted, eligible}); break;
@@ -693,13 +704,13 @@ hipError_t launch_compact_corrective(const uint8_t* codes, const int32_t* x0, in
   const bool single = tiles == 1;
   if (!single)
     tile_docs_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
-        cu, n_docs, n, tile_lo, tile_hi);
+        cu, n_docs, n, tile_lo, tile_hi, nullptr, nullptr);
   const bool vec = ((uintptr_t)x0 % 16 == 0) && ((uintptr_t)codes % 4 == 0);
   const CodeWeights cwt{codes, noise_wt, (float)(clean_wt / (double)n)};
   const Launch L{n,        cu,     n_docs,  tiles,   groups, counts,  tile_lo,
                  tile_hi,  group_sums, nullptr, nullptr, nullptr, x0,  wa,
                  row_idx,  tgt,    w,       n_rows,  vec,    stream,  cwt,
-                 single};
+                 single,   false};
   const bool shifted = align == MDLM_SHIFTED;
   // without clean rows the codes are the selection mask (nonzero: corrupted
   // either way); with them every token is a row

@@ -164,7 +164,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
                int32_t n_docs, uint32_t k0, uint32_t k1, const double* __restrict__ p_doc,
                int32_t mask_id, uint32_t rand_vocab, uint32_t thr_mix, int32_t* __restrict__ xt,
                uint8_t* __restrict__ corrupted, int32_t* __restrict__ doc_counts, bool hints,
-               double* __restrict__ p_out, double eps) {
+               double* __restrict__ p_out, double eps, int32_t* __restrict__ tile_counts) {
   __shared__ int s_dlo, s_dhi;
   __shared__ int32_t s_cu[kLdsDocs + 1];
   __shared__ int s_cnt[kLdsDocs];
@@ -172,6 +172,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
   // per 256-token window of the block (window wave + 4 j is round j of wave
   // `wave`): its first local document | (last - first) << 16
   __shared__ int s_win[kRounds * kThreads / 64];
+  __shared__ int s_tile[kThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t blk0 = (int64_t)blockIdx.x * kTokPerBlock;
@@ -261,6 +262,20 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
   }
   // Bernoulli threshold of local document d (from LDS when cached)
   auto thr_of = [&](int d) { return cached ? s_thr[d] : threshold_of(p_doc[dlo + d]); };
+  // With tile_counts: the block's corrupted tokens (its 4096 tokens are one
+  // tile of the row list), from each thread's share; called block-uniformly.
+  int tile_mine = 0;
+  auto put_tile_count = [&]() {
+    const int c = wave_sum(tile_mine);
+    if (lane == 0) s_tile[wave] = c;
+    __syncthreads();
+    if (tid == 0) {
+      int t = 0;
+#pragma unroll
+      for (int i = 0; i < kThreads / 64; ++i) t += s_tile[i];
+      tile_counts[blockIdx.x] = t;
+    }
+  };
 
   // Whole block in one document: all four rounds' loads are issued first.
   if (kVec && cached && nd == 1 && blk1 - blk0 == kTokPerBlock) {
@@ -276,6 +291,10 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
       c += corrupt4<kMode>(v[j], blk0 + 4 * (int64_t)(tid + kThreads * j), thr, k0, k1,
                            mask_id, rand_vocab, thr_mix, xt, corrupted);
     if (lane == 0 && c) atomicAdd(&doc_counts[dlo], c);
+    if (tile_counts) {
+      tile_mine = lane == 0 ? c : 0;
+      put_tile_count();
+    }
     return;
   }
 
@@ -300,6 +319,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
         const int c = corrupt4<kMode>(v, g0, s_thr[dw], k0, k1, mask_id, rand_vocab, thr_mix,
                                       xt, corrupted);
         if (lane == 0 && c) atomicAdd(&s_cnt[dw], c);
+        if (lane == 0) tile_mine += c;
         continue;
       }
       if (span <= 3) {
@@ -319,6 +339,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
         }
         const uint32_t bits = corrupt4_core<kMode>(v, g0, tk[0], tk[1], tk[2], tk[3], k0, k1,
                                                    mask_id, rand_vocab, thr_mix, xt, corrupted);
+        tile_mine += __popc(bits);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (i > span) break;
@@ -395,6 +416,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
         }
       }
     }
+    tile_mine += __popc(flag_bits);
     // Per-document counts.  Active lanes form a prefix of the wave and their
     // documents rise with the lane.  When the wave's tokens lie in one
     // document, ballots count its corrupted tokens; otherwise tokens in the
@@ -447,6 +469,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
     for (int i = tid; i < nd; i += kThreads)
       if (s_cnt[i]) atomicAdd(&doc_counts[dlo + i], s_cnt[i]);
   }
+  if (tile_counts) put_tile_count();
 }
 
 }  // namespace
@@ -455,7 +478,7 @@ hipError_t launch_corrupt(const int32_t* x0, int64_t n, const int32_t* cu, int32
                           uint64_t seed, double eps, int32_t noise, int32_t mask_id,
                           int32_t rand_vocab, int32_t* xt, uint8_t* corrupted,
                           double* p_doc, int32_t* doc_counts, hipStream_t stream,
-                          double mixture_prob) {
+                          double mixture_prob, int32_t* tile_counts) {
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   const bool hints = n > 0 && n < (int64_t)n_docs * kHintMaxMeanLen;
   // one block over at most kLdsDocs documents: it draws the noise levels too
@@ -476,7 +499,8 @@ hipError_t launch_corrupt(const int32_t* x0, int64_t n, const int32_t* cu, int32
                                                         single ? nullptr : p_doc,          \
                                                         mask_id, rv, thr_mix, xt, corrupted, \
                                                         doc_counts, hints && !single,      \
-                                                        single ? p_doc : nullptr, eps)
+                                                        single ? p_doc : nullptr, eps,     \
+                                                        tile_counts)
     if (noise == MDLM_NOISE_UNIFORM) {
       if (vec) MDLM_CORRUPT_LAUNCH(MDLM_NOISE_UNIFORM, true);
       else MDLM_CORRUPT_LAUNCH(MDLM_NOISE_UNIFORM, false);

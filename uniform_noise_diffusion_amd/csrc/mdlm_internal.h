@@ -117,7 +117,8 @@ hipError_t launch_corrupt(const int32_t* x0, int64_t n_tokens, const int32_t* cu
                           int32_t n_docs, uint64_t seed, double eps, int32_t noise,
                           int32_t mask_id, int32_t rand_vocab, int32_t* xt,
                           uint8_t* corrupted, double* p_doc, int32_t* doc_counts,
-                          hipStream_t stream, double mixture_prob = 0.0);
+                          hipStream_t stream, double mixture_prob = 0.0,
+                          int32_t* tile_counts = nullptr);
 
 size_t compact_workspace_bytes(int64_t n_tokens, int32_t n_docs, int32_t weighting);
 // mdlm_compact_masked_noalloc: the largest stream its device scratch array
@@ -137,7 +138,8 @@ hipError_t launch_compact(const uint8_t* corrupted, const uint8_t* eligible, con
                           int64_t n_tokens, const int32_t* cu, int32_t n_docs,
                           const double* p_doc, int32_t align, int32_t weighting, double scale,
                           double clip, int32_t* row_idx, int32_t* tgt, float* w,
-                          int32_t* n_rows, void* workspace, hipStream_t stream);
+                          int32_t* n_rows, void* workspace, hipStream_t stream,
+                          bool counts_given = false);
 
 // corruption and the inverse-p row list in one pass (mdlm_corrupt_compact)
 size_t corrupt_compact_workspace_bytes(int64_t n_tokens);
