@@ -246,10 +246,12 @@ def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
                 corrupt_us_per_call=[round(x, 1) for x in r_cor],
                 compact_us_per_call=[round(x, 1) for x in r_cmp],
                 fused_us_per_call=[round(x, 1) for x in r_fused],
-                fused_what=("mdlm_corrupt_compact (corruption and the row list in one pass); "
-                            "algorithmic bytes 9 per token (x0 read, xt and mask written) + "
-                            "12 per scored row (row, target, weight written; the target is the "
-                            "token already read)"))
+                fused_what=("mdlm_corrupt_compact (corruption writing per-tile counts, then "
+                            "the row list without a count pass); algorithmic bytes 9 per token "
+                            "(x0 read, xt and mask written) + 12 per scored row (row, target, "
+                            "weight written; the target is the token already read) -- the "
+                            "least any implementation moves; this one also reads the mask and "
+                            "x0 again (5 bytes per token)"))
 
 
 def achievable(dev, gemm_shape=None):
