@@ -189,3 +189,44 @@ def test_fused_equals_two_calls_at_bandwidth_size(layout):
         assert torch.equal(o.tgt[:m], ref.tgt[:m])
         assert torch.equal(o.w[:m].view(torch.int32), ref.w[:m].view(torch.int32))
         del ref, o
+
+
+def _random_layout(rng, max_tokens):
+    n_docs = int(rng.integers(1, 300))
+    max_len = int(rng.integers(1, max(2, max_tokens // n_docs)))
+    lengths = rng.integers(1, max_len + 1, size=n_docs)
+    lengths[rng.random(n_docs) < rng.choice([0.0, 0.2])] = 0
+    lengths[rng.random(n_docs) < 0.05] = 1
+    cu = np.zeros(n_docs + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lengths)
+    return cu
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_fused_random_sweep(case):
+    """Seeded random layouts (empty and one-token documents, one to tens of
+    tiles), both noise modes and alignments, eps from 1e-3 to 1, with and
+    without the mask output: bit for bit against the oracle."""
+    rng = np.random.default_rng(5000 + case)
+    cu = _random_layout(rng, 60000)
+    V = int(rng.integers(2, 200000))
+    x0 = rng.integers(0, V, size=int(cu[-1])).astype(np.int32)
+    eps = float(rng.choice([1e-3, rng.random(), 1.0]))
+    noise = int(rng.integers(0, 2))
+    align = int(rng.integers(0, 2))
+    seed = int(rng.integers(0, 2**63))
+    mask = bool(rng.integers(0, 2))
+    _check(x0, cu, seed, eps, noise, int(rng.integers(0, V)), V, align, mask=mask)
+
+
+@pytest.mark.parametrize("align", [oracle.ALIGNED, oracle.SHIFTED])
+def test_fused_documents_on_tile_boundaries(align):
+    """Every document starts on a 4096-token tile boundary and every token is
+    corrupted (eps = 1): with shifted rows each tile's count loses exactly
+    its first token."""
+    cu = np.arange(0, 4096 * 9 + 1, 4096, dtype=np.int32)
+    cu = np.concatenate([cu, [cu[-1] + 100]]).astype(np.int32)  # a ragged last tile
+    x0 = np.random.default_rng(7).integers(0, 999, size=int(cu[-1])).astype(np.int32)
+    o = _check(x0, cu, 99, 1.0, oracle.NOISE_ABSORB, 999, 1000, align)
+    n = int(cu[-1])
+    assert int(host(o.n_rows)[0]) == (n - (cu.shape[0] - 1) if align == oracle.SHIFTED else n)
