@@ -470,8 +470,9 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
     }
     if (!done && mv != 0) {
       int d = cached ? lds_find_doc(s_cu, nd, g0) : find_doc(cu, dlo, dhi, g0) - dlo;
-      int64_t d_beg = cached ? s_cu[d] : cu[dlo + d];
-      int64_t d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
+      const DocOffsets cu_at(s_cu, cu, dlo, n_docs, cached);  // cu[dlo + i]
+      int64_t d_beg = cu_at[d];
+      int64_t d_end = cu_at[d + 1];
       auto weight_of = [&](int dd) { return cached ? s_wd[dd] : weight_of_doc(dlo + dd); };
       auto weight2_of = [&](int dd) { return cached ? s_wd2[dd] : weight2_of_doc(dlo + dd); };
       float wd = weight_of(d);
@@ -484,9 +485,9 @@ scatter_kernel(const uint8_t* __restrict__ corrupted, const uint8_t* __restrict_
             // (bounded by the last document even if cu_seqlens is malformed)
             do {
               ++d;
-              d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
+              d_end = cu_at[d + 1];
             } while (g >= d_end && d < nd - 1);
-            d_beg = cached ? s_cu[d] : cu[dlo + d];
+            d_beg = cu_at[d];
             wd = weight_of(d);
             if (kCode) wr = weight2_of(d);
           }

@@ -110,6 +110,33 @@ __device__ __forceinline__ int lds_find_doc(const int32_t* s_cu, int nd, int64_t
   return a - 1;
 }
 
+// Document offsets cu[lo + i] of a block that caches them in LDS as
+// s_cu[i] when `cached`.  The uncached read goes through a buffer resource:
+// written as plain loads, the two reads are merged by the compiler into one
+// load through a selected generic pointer, i.e. a flat load that the cached
+// case pays too.  The resource spans 2^30 offsets past lo (byte offsets fit
+// 32 bits); offsets beyond that read as zero, which only a block spanning
+// over 2^30 (empty) documents could reach.
+struct DocOffsets {
+  const int32_t* s_cu;
+  __amdgpu_buffer_rsrc_t rsrc;
+  bool cached;
+  __device__ __forceinline__ DocOffsets(const int32_t* s, const int32_t* cu, int lo, int n_docs,
+                                        bool c)
+      : s_cu(s),
+        rsrc(__builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t*>(cu + lo), (short)0,
+            (int)(uint32_t)(4 * (((int64_t)n_docs + 1 - lo) < ((int64_t)1 << 30)
+                                     ? ((int64_t)n_docs + 1 - lo)
+                                     : ((int64_t)1 << 30))),
+            0x00020000)),
+        cached(c) {}
+  __device__ __forceinline__ int64_t operator[](int i) const {
+    if (cached) return s_cu[i];
+    return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(rsrc, 4u * (uint32_t)i, 0, 0);
+  }
+};
+
 // ---- launchers implemented in the kernel translation units ---------------
 // noise: MDLM_NOISE_ABSORB, MDLM_NOISE_UNIFORM or kNoiseMixture (then
 // mixture_prob in [0, 1] is the share of corrupted tokens replaced)
