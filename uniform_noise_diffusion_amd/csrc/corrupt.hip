@@ -25,6 +25,8 @@
 // noise levels itself.
 #include "mdlm_internal.h"
 
+#include <algorithm>
+
 namespace mdlm {
 namespace {
 
@@ -34,6 +36,7 @@ constexpr int kThreads = 256;
 #endif
 constexpr int kRounds = MDLM_CORRUPT_ROUNDS;
 constexpr int kTokPerBlock = kThreads * 4 * kRounds;  // 4096 by default
+static_assert(kRounds <= 64, "one lane per round finds a wave's window documents");
 #ifndef MDLM_CORRUPT_PRELOAD
 #define MDLM_CORRUPT_PRELOAD 1
 #endif
@@ -68,13 +71,17 @@ __device__ __forceinline__ double doc_p(int b, uint32_t k0, uint32_t k1, double 
   return eps + scaled;
 }
 
+// With tile_counts: the first n_tiles entries are cleared as well (one per
+// thread), for corrupt_kernel to add each block's count to.
 __global__ void __launch_bounds__(kThreads)
 noise_level_kernel(int32_t n_docs, uint32_t k0, uint32_t k1, double eps,
                    double* __restrict__ p_doc, int32_t* __restrict__ doc_counts,
                    const int32_t* __restrict__ cu, int64_t n, int32_t* __restrict__ xt,
-                   bool hints) {
-  const int b = blockIdx.x * kThreads + threadIdx.x;
-  if (b >= n_docs) return;
+                   bool hints, int32_t* __restrict__ tile_counts, int64_t n_tiles) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (tile_counts && i < n_tiles) tile_counts[i] = 0;
+  if (i >= n_docs) return;
+  const int b = (int)i;
   p_doc[b] = doc_p(b, k0, k1, eps);
   doc_counts[b] = 0;
   if (!hints) return;
@@ -169,10 +176,6 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
   __shared__ int32_t s_cu[kLdsDocs + 1];
   __shared__ int s_cnt[kLdsDocs];
   __shared__ uint32_t s_thr[kLdsDocs];
-  // per 256-token window of the block (window wave + 4 j is round j of wave
-  // `wave`): its first local document | (last - first) << 16
-  __shared__ int s_win[kRounds * kThreads / 64];
-  __shared__ int s_tile[kThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t blk0 = (int64_t)blockIdx.x * kTokPerBlock;
@@ -211,27 +214,31 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
       s_cnt[b] = 0;
       s_thr[b] = threshold_of(p);
     }
-    if (tid == 0) s_cu[n_docs] = cu[n_docs];
+    if (tid == 0) {
+      s_cu[n_docs] = cu[n_docs];
+      if (tile_counts) tile_counts[0] = 0;  // (the waves add to it after the barrier)
+    }
     nd = n_docs;
     hinted = true;
     __syncthreads();
   } else if (hints) {
-    if (tid == 0) {
-      s_dlo = xt[blk0];
-      s_dhi = blk1 - blk0 >= 2 ? xt[blk0 + 1] : s_dlo;
-    }
-    __syncthreads();
-    dlo = s_dlo;
-    const int64_t nd_hint = (int64_t)s_dhi - dlo + 1;
+    // Every thread reads the two slots (the same values block-wide); no
+    // thread writes a token before the barrier that follows the table fill,
+    // so every read sees the hints.
+    const int h0 = xt[blk0];
+    const int h1 = blk1 - blk0 >= 2 ? xt[blk0 + 1] : h0;
+    dlo = h0;
+    const int64_t nd_hint = (int64_t)h1 - h0 + 1;
     nd = (int)min<int64_t>(max<int64_t>(nd_hint, 0), kLdsDocs);
-    hinted = dlo >= 0 && nd_hint >= 1 && nd_hint <= kLdsDocs && s_dhi < n_docs;
+    hinted = h0 >= 0 && nd_hint >= 1 && nd_hint <= kLdsDocs && h1 < n_docs;
     if (hinted) {
       fill(dlo, nd);
       __syncthreads();
       hinted =
           s_cu[0] <= blk0 && blk0 < s_cu[1] && s_cu[nd - 1] <= blk1 - 1 && blk1 - 1 < s_cu[nd];
     }
-    if (!hinted) __syncthreads();  // (s_dlo, s_dhi and s_cu were read above)
+    // (a failed check falls through to the search, whose barrier precedes
+    // its own table fill, after every thread's check has read s_cu)
   }
   if (!hinted) {
     if (wave == 0) {
@@ -248,33 +255,28 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
     __syncthreads();
   }
   const bool cached = nd <= kLdsDocs;
-  if (cached && nd > 1) {
-    // the windows' document ranges, once per block (block-uniform branch)
-    if (tid < kRounds * kThreads / 64) {
-      const int64_t ws = blk0 + 256 * (int64_t)tid;
-      if (ws < blk1) {
-        const int d0 = lds_find_doc(s_cu, nd, ws);
-        const int d1 = lds_find_doc(s_cu, nd, min(ws + 256, blk1) - 1);
-        s_win[tid] = d0 | ((d1 - d0) << 16);
-      }
+  // The document range of this wave's window in each round (256 tokens from
+  // 4 (64 wave + 256 j)): lane j finds round j's, as first local document |
+  // (last - first) << 16; the rounds read it with a lane read.
+  int win = 0;
+  if (cached && nd > 1 && lane < kRounds) {
+    const int64_t ws = blk0 + 4 * (int64_t)(64 * wave + kThreads * lane);
+    if (ws < blk1) {
+      const int d0 = lds_find_doc(s_cu, nd, ws);
+      const int d1 = lds_find_doc(s_cu, nd, min(ws + 256, blk1) - 1);
+      win = d0 | ((d1 - d0) << 16);
     }
-    __syncthreads();
   }
   // Bernoulli threshold of local document d (from LDS when cached)
   auto thr_of = [&](int d) { return cached ? s_thr[d] : threshold_of(p_doc[dlo + d]); };
-  // With tile_counts: the block's corrupted tokens (its 4096 tokens are one
-  // tile of the row list), from each thread's share; called block-uniformly.
+  const DocOffsets cu_at(s_cu, cu, dlo, n_docs, cached);  // cu[dlo + i]
+  // With tile_counts (cleared beforehand): the block's corrupted tokens (its
+  // 4096 tokens are one tile of the row list), added once per wave from each
+  // thread's share.
   int tile_mine = 0;
-  auto put_tile_count = [&]() {
+  auto add_tile_count = [&]() {
     const int c = wave_sum(tile_mine);
-    if (lane == 0) s_tile[wave] = c;
-    __syncthreads();
-    if (tid == 0) {
-      int t = 0;
-#pragma unroll
-      for (int i = 0; i < kThreads / 64; ++i) t += s_tile[i];
-      tile_counts[blockIdx.x] = t;
-    }
+    if (lane == 0 && c) atomicAdd(&tile_counts[blockIdx.x], c);
   };
 
   // Whole block in one document: all four rounds' loads are issued first.
@@ -291,10 +293,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
       c += corrupt4<kMode>(v[j], blk0 + 4 * (int64_t)(tid + kThreads * j), thr, k0, k1,
                            mask_id, rand_vocab, thr_mix, xt, corrupted);
     if (lane == 0 && c) atomicAdd(&doc_counts[dlo], c);
-    if (tile_counts) {
-      tile_mine = lane == 0 ? c : 0;
-      put_tile_count();
-    }
+    if (tile_counts && lane == 0 && c) atomicAdd(&tile_counts[blockIdx.x], c);
     return;
   }
 
@@ -310,7 +309,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
     if (kVec && cached && gw + 256 <= n) {
       int dw = 0, span = 0;
       if (nd > 1) {
-        const int pk = s_win[wave + 4 * j];
+        const int pk = __shfl(win, j, 64);
         dw = pk & 0xffff;
         span = pk >> 16;
       }
@@ -379,8 +378,8 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
         for (int k = 0; k < 4; ++k) in[k] = k < cnt_here ? x0[g0 + k] : 0;
       }
       // document of the first token, then walk forward
-      int d = cached ? lds_find_doc(s_cu, nd, g0) : find_doc(cu, dlo, s_dhi, g0) - dlo;
-      int64_t d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
+      int d = cached ? lds_find_doc(s_cu, nd, g0) : find_doc(cu, dlo, dlo + nd - 1, g0) - dlo;
+      int64_t d_end = cu_at[d + 1];
       uint32_t thr = thr_of(d);
       int32_t out[4];
 #pragma unroll
@@ -392,7 +391,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
           if (g >= d_end) {
             do {
               ++d;
-              d_end = cached ? s_cu[d + 1] : cu[dlo + d + 1];
+              d_end = cu_at[d + 1];
             } while (g >= d_end && d < nd - 1);
             thr = thr_of(d);
           }
@@ -469,7 +468,7 @@ corrupt_kernel(const int32_t* __restrict__ x0, int64_t n, const int32_t* __restr
     for (int i = tid; i < nd; i += kThreads)
       if (s_cnt[i]) atomicAdd(&doc_counts[dlo + i], s_cnt[i]);
   }
-  if (tile_counts) put_tile_count();
+  if (tile_counts) add_tile_count();
 }
 
 }  // namespace
@@ -483,12 +482,16 @@ hipError_t launch_corrupt(const int32_t* x0, int64_t n, const int32_t* cu, int32
   const bool hints = n > 0 && n < (int64_t)n_docs * kHintMaxMeanLen;
   // one block over at most kLdsDocs documents: it draws the noise levels too
   const bool single = n > 0 && n <= kTokPerBlock && n_docs <= kLdsDocs;
-  if (n_docs > 0 && !single) {
-    noise_level_kernel<<<(n_docs + kThreads - 1) / kThreads, kThreads, 0, stream>>>(
-        n_docs, k0, k1, eps, p_doc, doc_counts, cu, n, xt, hints);
+  const int64_t tiles = n > 0 ? (n + kTokPerBlock - 1) / kTokPerBlock : 0;
+  if ((n_docs > 0 || tile_counts) && !single) {
+    const int64_t threads = std::max<int64_t>(n_docs, tile_counts ? tiles : 0);
+    if (threads > 0)
+      noise_level_kernel<<<(unsigned)((threads + kThreads - 1) / kThreads), kThreads, 0,
+                           stream>>>(n_docs, k0, k1, eps, p_doc, doc_counts, cu, n, xt, hints,
+                                     tile_counts, tiles);
   }
   if (n > 0) {
-    const unsigned grid = (unsigned)((n + kTokPerBlock - 1) / kTokPerBlock);
+    const unsigned grid = (unsigned)tiles;
     const uint32_t rv = (uint32_t)rand_vocab;
     // ceil(mixture_prob * 2^24): exact (power-of-two scaling), 0 .. 2^24
     const uint32_t thr_mix = (uint32_t)ceil(mixture_prob * 16777216.0);
