@@ -49,7 +49,8 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    # ~0.1 s of steps: the GPU's speed settles after the idle set-up
+    p.add_argument("--warmup", type=int, default=25)
     p.add_argument("--workload", type=int, default=2)
     p.add_argument("--align", type=int, default=None)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -130,15 +131,17 @@ def gpu_steps(args, inp, dev):
         if ev is not None:
             ev[2].record()
 
-    for i in range(args.warmup):
-        one(1_000_000 + i)
-    torch.cuda.synchronize()
     K = args.steps
     evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(K)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    # (the host's garbage collection runs before the warm-up steps, so that
+    # only the synchronize separates them from the timed steps: after an idle
+    # spell the GPU's next tens of milliseconds of work run measurably slower)
     with quiet_host():
+        for i in range(args.warmup):
+            one(1_000_000 + i)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         start.record()
         for i in range(K):
@@ -184,27 +187,7 @@ def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
     g = torch.Generator(device=dev).manual_seed(0)
     x0 = torch.randint(0, 126336, (n,), dtype=torch.int32, device=dev, generator=g)
     step = MdlmLossStep(n, n_docs, 64, 64, device=dev, head_workspace_bytes=0, want_grad=False)
-    for i in range(2):
-        step.corrupt(x0, cu, i, 1e-3, 0, 126336, 126464)
-        step.compact(x0, cu, 0)
-    torch.cuda.synchronize()
-    ec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    with quiet_host():
-        for i in range(reps):
-            ec[i][0].record()
-            step.corrupt(x0, cu, 100 + i, 1e-3, 0, 126336, 126464)
-            ec[i][1].record()
-            step.compact(x0, cu, 0)
-            ec[i][2].record()
-        torch.cuda.synchronize()
-    # medians over the repetitions (the per-repetition times are reported too)
-    r_cor = [a.elapsed_time(b) * 1e3 for a, b, _ in ec]
-    r_cmp = [b.elapsed_time(c) * 1e3 for _, b, c in ec]
-    t_cor = float(np.median(r_cor)) * 1e-6
-    t_cmp = float(np.median(r_cmp)) * 1e-6
-    m = int(step.n_rows.item())
-    # the one-pass call: the same outputs as the two calls above
+    # the one-pass call: the same outputs as the two calls
     from uniform_noise_diffusion_amd import binding as B
     ws = torch.empty(B.mdlm_corrupt_compact_workspace_bytes(n), dtype=torch.uint8, device=dev)
 
@@ -212,20 +195,40 @@ def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
         B.mdlm_corrupt_compact(x0, cu, seed, 1e-3, 0, 126336, 126464, 0, step.xt, step.corrupted,
                                step.p_doc, step.doc_counts, step.row_idx, step.tgt, step.w,
                                step.n_rows, ws)
-    for i in range(2):
-        fused(i)
-    torch.cuda.synchronize()
+    # The two forms are timed alternately (call i of each on the same seed),
+    # right behind an untimed warm-up of about 0.1 s that is queued with no
+    # wait in between: when the GPU has been idle, even for a few
+    # milliseconds, calls of this size drift in time over the next tens of
+    # milliseconds (up to 20% slower, then settling).
+    ec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     ef = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
+    torch.cuda.synchronize()
     with quiet_host():
+        for i in range(100):
+            step.corrupt(x0, cu, i, 1e-3, 0, 126336, 126464)
+            step.compact(x0, cu, 0)
+            fused(i)
         for i in range(reps):
+            ec[i][0].record()
+            step.corrupt(x0, cu, 100 + i, 1e-3, 0, 126336, 126464)
+            ec[i][1].record()
+            step.compact(x0, cu, 0)
+            ec[i][2].record()
             ef[i][0].record()
             fused(100 + i)
             ef[i][1].record()
         torch.cuda.synchronize()
+    # medians over the repetitions (the per-repetition times are reported too)
+    r_cor = [a.elapsed_time(b) * 1e3 for a, b, _ in ec]
+    r_cmp = [b.elapsed_time(c) * 1e3 for _, b, c in ec]
+    t_cor = float(np.median(r_cor)) * 1e-6
+    t_cmp = float(np.median(r_cmp)) * 1e-6
     r_fused = [a.elapsed_time(b) * 1e3 for a, b in ef]
     t_fused = float(np.median(r_fused)) * 1e-6
-    m_fused = int(step.n_rows.item())
+    # (each fused call repeats the two-call pair's seed: the same rows)
+    m = m_fused = int(step.n_rows.item())
     b_fused = 9.0 * n + 12.0 * m_fused
     # algorithmic bytes: corrupt reads x0 (4 B) and writes xt (4 B) and the
     # mask (1 B) per token; compact reads the mask (1 B) per token and, per
@@ -241,8 +244,10 @@ def bandwidth(n_tokens, dev, reps=10, doc_mean=None):
                 fused_us=t_fused * 1e6, fused_GBs=b_fused / t_fused / 1e9,
                 fused_frac=b_fused / t_fused / 1e9 / PEAK_HBM_GBS,
                 two_calls_us=(t_cor + t_cmp) * 1e6,
-                timing=(f"medians over {reps} calls (HIP events on the launch stream); per call "
-                        "below, in us"),
+                timing=(f"medians over {reps} calls (HIP events on the launch stream), the "
+                        "two-call pair and the one call alternating right behind 100 untimed "
+                        "rounds; "
+                        "per call below, in us"),
                 corrupt_us_per_call=[round(x, 1) for x in r_cor],
                 compact_us_per_call=[round(x, 1) for x in r_cmp],
                 fused_us_per_call=[round(x, 1) for x in r_fused],
@@ -320,12 +325,22 @@ def achievable(dev, gemm_shape=None):
 
 
 def _timed(fn, reps):
+    """Mean seconds per call of `reps` calls of fn (HIP events), queued right
+    behind untimed calls worth about 0.1 s with no wait in between: after
+    even a short idle spell the GPU's next tens of milliseconds of work run
+    at a drifting speed."""
     import torch
+    a0, b0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
     fn()
+    b0.record()
     torch.cuda.synchronize()
+    warm = int(min(50, max(2, np.ceil(100.0 / max(a0.elapsed_time(b0), 1e-3)))))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
     with quiet_host():
+        for _ in range(warm):
+            fn()
         for a, b in ev:
             a.record()
             fn()
@@ -659,7 +674,7 @@ def main():
                     out[k][f"{op}_frac_of_achievable_copy"] = (
                         out[k][f"{op}_GBs"] / out["achievable"]["copy_GBs"])
     if not args.no_other_workloads and args.workload == 2:
-        out["other_workloads"] = other_workloads(dev, args.other_steps, 2)
+        out["other_workloads"] = other_workloads(dev, args.other_steps, 10)
     if not args.no_variants:
         log("timing the loss variants")
         out["variants"] = variants(inp, dev, args.bandwidth_tokens)
