@@ -89,6 +89,19 @@ static_assert(2 * kLoads * kVmemEvery <= 4 * (16 / kWaves) * (64 / 16), "loads f
 #define MDLM_STASH 1
 #endif
 constexpr int kMaxSplit = 8;          // K-splits of the dH product
+#ifndef MDLM_DH_ROWS
+#define MDLM_DH_ROWS 320
+#endif
+// The dH product's tile: kDhRows scored rows (kDhNI 32-row blocks per wave)
+// by kTile hidden columns.
+constexpr int kDhRows = MDLM_DH_ROWS;
+constexpr int kDhNI = kDhRows / 64;
+constexpr int kDhABytes = kDhRows * kKRow;            // G's K-major tile
+constexpr int kDhALoads = kDhABytes / 1024 / kWaves;  // its 1 KiB loads per wave
+constexpr int kDhStageBytes = kDhABytes + kOpBytes;   // G + W
+static_assert(kDhRows % 64 == 0 && kDhALoads * 1024 * kWaves == kDhABytes,
+              "whole 1 KiB loads per wave");
+static_assert(2 * kDhStageBytes <= 160 * 1024, "two stages in LDS");
 // The stash of a half tile is taken relative to the row's reference R (its
 // target logit) when the half tile's maximum m_h is at most kStashSpan above
 // R (log2 units), so entries stay below 2^64 and sums of them far below the
@@ -328,13 +341,14 @@ __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB r
 // the end retires them.  Only the first NI A blocks and NJ B blocks take
 // part (NI NJ = 0: loads and barriers only); kReads counts a slice's LDS
 // read instructions (transpose reads twice).
-template <int NI, int NJ, int kReads, typename ReadA, typename ReadB, typename Issue>
-__device__ __forceinline__ void kloop_pipe(f32x16 (&acc)[4][kNJ], int kb, int ke, char* s0,
+template <int NI, int NJ, int kReads, int kNIMax = 4, int kV = 2 * kLoads, typename ReadA,
+          typename ReadB, typename Issue>
+__device__ __forceinline__ void kloop_pipe(f32x16 (&acc)[kNIMax][kNJ], int kb, int ke, char* s0,
                                            char* s1, ReadA ra, ReadB rb, Issue issue) {
+  // kNIMax: A blocks per wave (the accumulator rows); kV: loads per issue()
   constexpr int kMfma = NI * NJ;
-  constexpr int kV = 2 * kLoads;  // loads per issue()
   constexpr int kSlices = kBK / 16;
-  bf16x8 af[2][4], bfr[2][kNJ];
+  bf16x8 af[2][kNIMax], bfr[2][kNJ];
   auto mfmas = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
@@ -347,11 +361,8 @@ __device__ __forceinline__ void kloop_pipe(f32x16 (&acc)[4][kNJ], int kb, int ke
   issue(s0, kb * kBK);
   issue(s1, (kb + 1) * kBK);
   // s0's loads only (the kV loads into s1 stay in flight)
-  static_assert(kV == 8 || kV == 16, "vmcnt immediate");
-  if constexpr (kV == 8)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  static_assert(kV < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kV) : "memory");
   __syncthreads();
   if constexpr (kMfma > 0) {
     ra(s0, 0, af[0]);
@@ -730,19 +741,19 @@ __host__ __device__ __forceinline__ int dh_splits(int64_t tiles, int grid, int k
   return best;
 }
 
-// Tile of 256 scored rows (operand A, rows of G) by 256 hidden columns
+// Tile of kDhRows scored rows (operand A, rows of G) by 256 hidden columns
 // (operand B, columns of W read through transpose loads), K = vocabulary.
-// Wave w owns the row blocks 32 (w % 2) + 64 i .. +31, i < 4 (dealt in turn,
+// Wave w owns the row blocks 32 (w % 2) + 64 i .. +31, i < kDhNI (dealt in turn,
 // so that a partial tile's rows fall evenly on both SIMD pairs; only blocks
 // holding scored rows are computed) and columns kWB (w / 2) .. +kWB-1.
 __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
-  __shared__ __attribute__((aligned(1024))) char smem0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char smem1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem0[kDhStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem1[kDhStageBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wa = wave & 1, wb = wave >> 1;
   const int n_rows = min(*a.n_rows, a.max_rows);
-  const int n_mt = (n_rows + kTile - 1) / kTile;
+  const int n_mt = (n_rows + kDhRows - 1) / kDhRows;
   const int n_ht = (a.H + kTile - 1) / kTile;
   const int64_t T = (int64_t)n_mt * n_ht;
   const int KI = (a.v_end - a.v_begin + kBK - 1) / kBK;
@@ -772,7 +783,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
     // band), blocks of 8 x 4
     int mt, ht;
     grouped_tile(tile, n_mt, n_ht, 8, 4, &mt, &ht);
-    const int m0 = mt * kTile, h0 = ht * kTile;
+    const int m0 = mt * kDhRows, h0 = ht * kTile;
     const int kb = (int)((int64_t)KI * s / S), ke = (int)((int64_t)KI * (s + 1) / S);
 
     // load q (0..kLoads-1): K-major rows 8 (kLoads wave + q) + l / 8 of G,
@@ -783,47 +794,53 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
         make_rsrc(a.G + (int64_t)m0 * a.ldg, (int64_t)(n_rows - m0) * a.ldg * 2);
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(a.W + (int64_t)a.v_begin * a.H, (int64_t)(a.v_end - a.v_begin) * a.H * 2);
+    // (G's load q fills LDS rows 8 (kDhALoads wave + q) .. +7, whose swizzle
+    // parity is that of kDhALoads wave + q)
+    const int wpar = (kDhALoads & 1) ? (wave & 1) : 0;
     uint32_t a_voff[2], b_voff[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-      a_voff[par] = (uint32_t)((lrow * a.ldg + 8 * (lphys ^ lrow ^ par)) * 2);
+      a_voff[par] = (uint32_t)((lrow * a.ldg + 8 * (lphys ^ lrow ^ par ^ wpar)) * 2);
       const int cn = nphys ^ swz_n(2 * par + nrow);
       // columns past H read the following row (finite values whose products
       // land only in columns that are never stored)
       b_voff[par] = (uint32_t)((nrow * a.H + h0 + 8 * cn) * 2);
     }
-    f32x16 acc[4][kNJ];
+    f32x16 acc[kDhNI][kNJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kDhNI; ++i)
 #pragma unroll
       for (int j = 0; j < kNJ; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     auto issue = [&](char* stage, int k0) {
-      char* sa = stage + (kLoads * wave) * 1024;
+      char* sa = stage + (kDhALoads * wave) * 1024;
+      char* sb = stage + kDhABytes + (kLoads * wave) * 1024;
 #pragma unroll
-      for (int q = 0; q < kLoads; ++q) {
-        buf2l(ra, sa + q * 1024, a_voff[q & 1],
-              (uint32_t)((8 * (kLoads * wave + q) * a.ldg + k0) * 2));
-        buf2l(rb, sa + kOpBytes + q * 1024, b_voff[q & 1],
-              (uint32_t)((2 * (kLoads * wave + q) + k0) * a.H * 2));
+      for (int q = 0; q < (kDhALoads > kLoads ? kDhALoads : kLoads); ++q) {
+        if (q < kDhALoads)
+          buf2l(ra, sa + q * 1024, a_voff[q & 1],
+                (uint32_t)((8 * (kDhALoads * wave + q) * a.ldg + k0) * 2));
+        if (q < kLoads)
+          buf2l(rb, sb + q * 1024, b_voff[q & 1],
+                (uint32_t)((2 * (kLoads * wave + q) + k0) * a.H * 2));
       }
     };
-    // this wave's row blocks that hold scored rows (a prefix of its four)
-    const int nv = min(kTile, n_rows - m0);
+    // this wave's row blocks that hold scored rows (a prefix of its kDhNI)
+    const int nv = min(kDhRows, n_rows - m0);
     const int ki = max(0, (nv - 32 * wa + 63) / 64);
     auto kloop = [&](auto ni_tag) __attribute__((always_inline)) {
       constexpr int NI = decltype(ni_tag)::value;
-      kloop_pipe<NI, kNJ, NI + 2 * kNJ>(
+      kloop_pipe<NI, kNJ, NI + 2 * kNJ, kDhNI, kDhALoads + kLoads>(
           acc, kb, ke, smem0, smem1,
-          [&](const char* base, int kk, bf16x8(&f)[4]) __attribute__((always_inline)) {
+          [&](const char* base, int kk, bf16x8(&f)[kDhNI]) __attribute__((always_inline)) {
             const int coff = ((2 * kk + khalf) ^ fx) * 16;
 #pragma unroll
             for (int i = 0; i < NI; ++i)
               f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 64 * kKRow + coff);
           },
           [&](const char* base, int kk, bf16x8(&f)[kNJ]) __attribute__((always_inline)) {
-            const char* brow_p = base + kOpBytes + (16 * kk + tr_row) * kNRow;
+            const char* brow_p = base + kDhABytes + (16 * kk + tr_row) * kNRow;
 #pragma unroll
             for (int j = 0; j < kNJ; ++j) {
               const shortx4 lo = ds_read_tr(brow_p + b_col_off[j]);
@@ -835,13 +852,13 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dh_kernel(DhArgs a) {
           },
           issue);
     };
-    with_count<4>(ki, kloop);
+    with_count<kDhNI>(ki, kloop);
 
     // acc element e of block (i, j) on lane l: row m0 + 32 wa + 64 i + 8(e/4)
     // + 4(l/32) + e%4, column h0 + wb*kWB + 32j + l%32.
     float* out = a.part + (int64_t)s * a.max_rows * a.H;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kDhNI; ++i) {
       if (i >= ki) break;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -1279,7 +1296,8 @@ scatter_kernel(const float* __restrict__ part, int H, int grid, int v_span,
                const int32_t* __restrict__ row_idx, const int32_t* __restrict__ n_rows_ptr,
                int max_rows, int64_t n_tokens, T* __restrict__ d_hidden, StashFix fx) {
   const int n_rows = min(*n_rows_ptr, max_rows);
-  const int64_t tiles = (int64_t)((n_rows + kTile - 1) / kTile) * ((H + kTile - 1) / kTile);
+  // (the dH product's tile grid and split, as dh_kernel counts them)
+  const int64_t tiles = (int64_t)((n_rows + kDhRows - 1) / kDhRows) * ((H + kTile - 1) / kTile);
   const int S = dh_splits(tiles, grid, (v_span + kBK - 1) / kBK);
   const int64_t slice = (int64_t)max_rows * H;
   for (int j = blockIdx.x; j < n_rows; j += gridDim.x) {
