@@ -104,6 +104,18 @@ def test_bf16_many_rows_spanning_persistent_rounds():
     _compare_full(inp, seed=8, eps=1.0)
 
 
+@pytest.mark.parametrize("rows", [319, 320, 321, 639, 640, 641, 1281])
+@pytest.mark.parametrize("H", [256, 320])
+def test_bf16_row_counts_around_the_gradient_tiles(rows, H):
+    # eps = 1 corrupts every token, so one document of `rows` tokens gives
+    # exactly that many aligned rows: counts just below, at and above whole
+    # multiples of the gradient product's 320-row tiles (and of the forward's
+    # 256-row ones), with one hidden tile or one and a ragged second
+    inp = _small(rows + H, n_docs=1, max_len=0, H=H, V=1100, lengths=[rows])
+    s, _, _ = _compare_full(inp, seed=6, eps=1.0, align=oracle.ALIGNED)
+    assert int(host(s.n_rows)[0]) == rows
+
+
 def test_f32_tiny_workload_full():
     inp = WL.generate(WL.make_workload(1))
     _, le, de = _compare_full(inp, seed=0)

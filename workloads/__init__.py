@@ -219,14 +219,18 @@ def generate(wl, with_hidden=True, with_head=True):
 
 def small_case(seed, n_docs, max_len, H, V, dtype="bf16", noise=NOISE_ABSORB,
                align=ALIGNED, softcap=0.0, eps=1e-3, empty_docs=False,
-               philox_seed=None, hidden_scale=1.0, w_scale=0.02):
+               philox_seed=None, hidden_scale=1.0, w_scale=0.02, lengths=None):
     """A small random case for parity tests: random document lengths in
-    [1, max_len] (some zero when ``empty_docs``), uniform tokens over [0, V-1),
-    mask id V-1, hidden N(0, hidden_scale^2), head N(0, w_scale^2)."""
+    [1, max_len] (some zero when ``empty_docs``), or the given ``lengths``,
+    uniform tokens over [0, V-1), mask id V-1, hidden N(0, hidden_scale^2),
+    head N(0, w_scale^2)."""
     rng = np.random.default_rng(seed)
-    lengths = rng.integers(1, max_len + 1, size=n_docs)
-    if empty_docs:
-        lengths[rng.random(n_docs) < 0.25] = 0
+    if lengths is None:
+        lengths = rng.integers(1, max_len + 1, size=n_docs)
+        if empty_docs:
+            lengths[rng.random(n_docs) < 0.25] = 0
+    else:
+        lengths = np.asarray(lengths, dtype=np.int64)
     wl = Workload(f"small-{seed}", 0, dtype, H=H, V=V, noise=noise, align=align,
                   mask_id=V - 1, rand_vocab=V, eps=eps, softcap=softcap,
                   seed=seed if philox_seed is None else philox_seed,
