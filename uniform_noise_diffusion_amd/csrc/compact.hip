@@ -42,7 +42,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTile = 4096;          // tokens per tile
+constexpr int kTile = kRowTile;      // tokens per tile (4096)
 #ifndef MDLM_COMPACT_LDS_DOCS
 #define MDLM_COMPACT_LDS_DOCS 1024
 #endif

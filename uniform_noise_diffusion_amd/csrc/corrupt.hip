@@ -31,12 +31,10 @@ namespace mdlm {
 namespace {
 
 constexpr int kThreads = 256;
-#ifndef MDLM_CORRUPT_ROUNDS
-#define MDLM_CORRUPT_ROUNDS 4
-#endif
-constexpr int kRounds = MDLM_CORRUPT_ROUNDS;
+constexpr int kRounds = 4;
 constexpr int kTokPerBlock = kThreads * 4 * kRounds;  // 4096 by default
 static_assert(kRounds <= 64, "one lane per round finds a wave's window documents");
+static_assert(kTokPerBlock == kRowTile, "a corruption block is one tile of the row list");
 #ifndef MDLM_CORRUPT_PRELOAD
 #define MDLM_CORRUPT_PRELOAD 1
 #endif

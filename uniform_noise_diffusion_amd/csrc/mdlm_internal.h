@@ -147,6 +147,11 @@ hipError_t launch_corrupt(const int32_t* x0, int64_t n_tokens, const int32_t* cu
                           hipStream_t stream, double mixture_prob = 0.0,
                           int32_t* tile_counts = nullptr);
 
+// Tokens per tile of the row list: one compaction tile, and one corruption
+// block, whose per-tile corrupted counts the one-call path hands to the
+// compaction's scan.
+constexpr int kRowTile = 4096;
+
 size_t compact_workspace_bytes(int64_t n_tokens, int32_t n_docs, int32_t weighting);
 // mdlm_compact_masked_noalloc: the largest stream its device scratch array
 // serves, that array's size, and (looked up once per device) its address on
