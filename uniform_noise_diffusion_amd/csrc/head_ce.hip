@@ -601,6 +601,12 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
         const int dt = tg - vl;
         const bool holds_tgt = (unsigned)dt < 128u && (dt & 4) == 0;
         if (!kGrad) {
+          // sv: the scaled logits s = z log2(e) (capped first), or without a
+          // cap the logits z themselves, scaled where they are used: the
+          // maximum and the target are scaled after the selection (a
+          // positive factor commutes with max, and each is rounded once, as
+          // before), and 2^(s - mref) takes s - mref as one fma.
+          constexpr bool kRaw = !kCap;
           float sv[4][16];
           float mx = -INFINITY;
 #pragma unroll
@@ -610,16 +616,20 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
               const int off = 32 * i + 8 * (e >> 2) + (e & 3);
               float zc = acc[i][j][e], dc;
               if (kCap) zc = softcap_fwd(zc, a.softcap, a.inv_softcap, &dc);
-              float sc = zc * kLog2e;
+              float sc = kRaw ? zc : zc * kLog2e;
               if (!kFull) sc = off < lim ? sc : -INFINITY;
               sv[i][e] = sc;
               mx = fmaxf(mx, sc);
             }
           // (the target is never past the vocabulary, so never masked)
-          if (mvalid && holds_tgt) a.ztgt[m] = pick_entry(sv, dt);
+          if (mvalid && holds_tgt) {
+            const float pt = pick_entry(sv, dt);
+            a.ztgt[m] = kRaw ? pt * kLog2e : pt;
+          }
           // the row's maximum over this wave's 128 entries (two lanes hold
           // 64 each); -inf when all of them lie past the vocabulary
           mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+          if (kRaw) mx *= kLog2e;
           const float mref = mx == -INFINITY ? 0.f : mx;
           // the stash is 2^(s - rho) = 2^(s - mref) fs with rho = R when m_h
           // is within kStashSpan of it (fs <= 2^64; it may underflow to 0
@@ -641,7 +651,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const float sc = sv[i][4 * q + r];
-                const float e2 = __builtin_amdgcn_exp2f(sc - mref);
+                const float e2 = __builtin_amdgcn_exp2f(kRaw ? __builtin_fmaf(sc, kLog2e, -mref)
+                                                             : sc - mref);
                 sum += e2;
                 if (kStash) {
                   float gv = e2 * fs;
