@@ -328,6 +328,20 @@ __device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB r
   }
 }
 
+// Waits for this wave's LDS accesses and until at most n of its memory
+// operations are outstanding, then joins the workgroup's barrier.  Written
+// as one asm block: in front of each barrier it emits itself (from
+// __syncthreads or the barrier builtin), the compiler waits for every
+// outstanding memory operation, which would also retire loads meant to stay
+// in flight across it and stores nothing after it depends on.  (Vector
+// memory operations complete in issue order, so n counts those issued after
+// the ones waited for; n = 63, the counter's limit, waits for none.)
+template <int n>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(n) : "memory");
+}
+
 // The K loop of the MFMA kernels over steps [kb, ke) of kBK: two LDS stages
 // s0 and s1, operands loaded straight into LDS by issue(stage, k0), and
 // fragments read by ra(stage, kk, f) and rb(stage, kk, f) for 16-deep slice
@@ -357,13 +371,13 @@ __device__ __forceinline__ void kloop_pipe(f32x16 (&acc)[kNIMax][kNJ], int kb, i
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j],
                                                             0, 0, 0);
   };
-  __syncthreads();  // the previous tile is done with both stages
+  // the previous tile is done with both stages (its LDS reads; its stores
+  // may still be in flight)
+  wait_barrier<63>();
   issue(s0, kb * kBK);
   issue(s1, (kb + 1) * kBK);
   // s0's loads only (the kV loads into s1 stay in flight)
-  static_assert(kV < 64, "vmcnt immediate");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kV) : "memory");
-  __syncthreads();
+  wait_barrier<kV>();
   if constexpr (kMfma > 0) {
     ra(s0, 0, af[0]);
     rb(s0, 0, bfr[0]);
@@ -389,8 +403,7 @@ __device__ __forceinline__ void kloop_pipe(f32x16 (&acc)[kNIMax][kNJ], int kb, i
       }
     }
     sched_fence();
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __syncthreads();
+    wait_barrier<0>();
     issue(cur, (kt + 2) * kBK);
     if constexpr (kMfma > 0) {
       ra(nxt, 0, af[0]);
