@@ -68,11 +68,14 @@ def _small(seed, n_docs, max_len, H, V, **kw):
     return WL.small_case(seed, n_docs, max_len, H, V, **kw)
 
 
-@pytest.mark.parametrize("H,V", [(64, 1000), (192, 300), (320, 2600), (256, 4096)])
+@pytest.mark.parametrize("H,V", [(64, 1000), (192, 300), (320, 2600), (256, 4096), (128, 600)])
 @pytest.mark.parametrize("align", [oracle.ALIGNED, oracle.SHIFTED])
 def test_bf16_small_tiles_and_ragged_tails(H, V, align):
     # ~300 scored rows: several 128-row tiles with a ragged last one; V with a
-    # ragged 256-wide vocabulary tile; H multiples of 64 but not of 256
+    # ragged last vocabulary tile, of 256 entries or (the forward pass with
+    # the stash and no softcap) 320, including last tiles more than 256
+    # entries short of full (V = 300, 600, 4096); H multiples of 64 but not
+    # of 256
     inp = _small(H + V, n_docs=5, max_len=250, H=H, V=V)
     _compare_full(inp, seed=5, eps=0.5, align=align)
 

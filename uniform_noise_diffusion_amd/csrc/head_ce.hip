@@ -88,6 +88,9 @@ static_assert(2 * kLoads * kVmemEvery <= 4 * (16 / kWaves) * (64 / 16), "loads f
 #ifndef MDLM_STASH
 #define MDLM_STASH 1
 #endif
+#ifndef MDLM_WIDE_TILE
+#define MDLM_WIDE_TILE 1
+#endif
 constexpr int kMaxSplit = 8;          // K-splits of the dH product
 #ifndef MDLM_DH_ROWS
 #define MDLM_DH_ROWS 320
@@ -221,31 +224,36 @@ __device__ __forceinline__ shortx4 ds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((MDLM_LDS shortx4*)(p));
 }
 
-// Entry at offset dt (0 <= dt < 128, bit 2 clear) of a lane's 64 accumulator
-// entries, where entry e of block i sits at offset 32 i + 8 (e / 4) + e % 4:
-// a select tree on the bits of dt (six masks, 63 selects) rather than one
-// compare per entry.
+// Entry at offset dt (0 <= dt < 32 NA, bit 2 clear) of a lane's 16 NA
+// entries of row block j, where entry e of block i sits at offset
+// 32 i + 8 (e / 4) + e % 4: a select tree on the bits of dt (63 selects for
+// four blocks) rather than one compare per entry.
 __device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
 
-__device__ __forceinline__ float pick_entry(const float (&sv)[4][16], int dt) {
+template <int NA>
+__device__ __forceinline__ float pick_entry(const f32x16 (&acc)[NA][kNJ], int j, int dt) {
   // (selects on values, never on array elements: a conditional lvalue would
   // select addresses and force the arrays into scratch memory)
-  const bool b0 = dt & 1, b1 = dt & 2, b3 = dt & 8, b4 = dt & 16, b5 = dt & 32, b6 = dt & 64;
-  float g[16];  // g[4 i + q]: entry 4 q + (dt % 4) of block i
+  static_assert(NA == 4 || NA == 5, "four or five blocks");
+  const bool b0 = dt & 1, b1 = dt & 2, b3 = dt & 8, b4 = dt & 16, b5 = dt & 32, b6 = dt & 64,
+             b7 = dt & 128;
+  float g[4 * NA];  // g[4 i + q]: entry 4 q + (dt % 4) of block i
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NA; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float x0 = sv[i][4 * q], x1 = sv[i][4 * q + 1];
-      const float x2 = sv[i][4 * q + 2], x3 = sv[i][4 * q + 3];
+      const float x0 = acc[i][j][4 * q], x1 = acc[i][j][4 * q + 1];
+      const float x2 = acc[i][j][4 * q + 2], x3 = acc[i][j][4 * q + 3];
       g[4 * i + q] = sel(b1, sel(b0, x3, x2), sel(b0, x1, x0));
     }
-  float h8[8], h4[4];
+  float h8[2 * NA], h4[NA];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) h8[k] = sel(b3, g[2 * k + 1], g[2 * k]);
+  for (int k = 0; k < 2 * NA; ++k) h8[k] = sel(b3, g[2 * k + 1], g[2 * k]);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) h4[k] = sel(b4, h8[2 * k + 1], h8[2 * k]);
-  return sel(b6, sel(b5, h4[3], h4[2]), sel(b5, h4[1], h4[0]));
+  for (int k = 0; k < NA; ++k) h4[k] = sel(b4, h8[2 * k + 1], h8[2 * k]);
+  const float lo = sel(b6, sel(b5, h4[3], h4[2]), sel(b5, h4[1], h4[0]));
+  if constexpr (NA == 5) return sel(b7, h4[4], lo);
+  return lo;
 }
 
 // --------------------------------------------------------------------------
@@ -444,50 +452,62 @@ __device__ __forceinline__ void kloop_pipe(f32x16 (&acc)[kNIMax][kNJ], int kb, i
 // kStashSpan) or, far above it, the row's maximum m_h over the wave's
 // 128-entry half of the tile.  The partials are (m_h, sum 2^(s - m_h)) either
 // way, the same as without the stash.
-template <bool kGrad, bool kCap, bool kStash = false>
+// kNA: 32-row blocks of W per wave, so a vocabulary tile of 64 kNA rows
+// (256, or 320 for the forward pass with the stash and no softcap), each
+// wave owning half of it: 32 kNA entries per row and partial.
+template <bool kGrad, bool kCap, bool kStash = false, int kNA = 4>
 __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
   static_assert(!(kGrad && kStash), "the stash is written by the forward pass");
+  static_assert(kNA == 4 || (kNA == 5 && kStash && !kCap), "320 rows: the stash, no softcap");
+  constexpr int kVT = 64 * kNA;            // vocabulary rows of a tile
+  constexpr int kHalf = 32 * kNA;          // a wave's entries per row
+  constexpr int kAB = kVT * kKRow;         // W's bytes in a stage
+  constexpr int kSB = kAB + kOpBytes;      // W + the scored rows
+  static_assert(2 * kSB <= 160 * 1024, "two stages in LDS");
   // the two stages are separate objects so that the compiler can tell a
   // prefetch into one from reads of the other
-  __shared__ __attribute__((aligned(1024))) char smem0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char smem1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char smem0[kSB];
+  __shared__ __attribute__((aligned(1024))) char smem1[kSB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wa = wave & 1, wb = wave >> 1;
   const int n_rows = min(*a.n_rows, a.max_rows);
   const int n_mt = (n_rows + kTile - 1) / kTile;
-  const int n_vt = (a.v_end - a.v_begin + kTile - 1) / kTile;
+  const int n_vt = (a.v_end - a.v_begin + kVT - 1) / kVT;
   const int64_t n_tiles = (int64_t)n_mt * n_vt;
   const int KT = a.H / kBK;
 
   // fragment-read offsets (bytes within a stage)
   const int fx = swz_k(lane & 15), khalf = lane >> 5;
-  const int a_off = (wa * 128 + (lane & 31)) * kKRow;
-  const int b_off = kOpBytes + (32 * wb + (lane & 31)) * kKRow;
-  // direct-load roles: load q (0..kLoads-1) of this wave fills tile rows
-  // 8 (kLoads wave + q) .. +7; lane l supplies row 8 (kLoads wave + q) + l / 8
-  // at physical chunk l % 8
+  const int a_off = (wa * kHalf + (lane & 31)) * kKRow;
+  const int b_off = kAB + (32 * wb + (lane & 31)) * kKRow;
+  // direct-load roles: load q (0..kNA-1) of this wave fills W rows
+  // 8 (kNA wave + q) .. +7, load q (0..kLoads-1) the scored rows
+  // 8 (kLoads wave + q) .. +7; lane l supplies row 8 (...) + l / 8 at
+  // physical chunk l % 8
   const int lrow = lane >> 3, lphys = lane & 7;
+  const int wpar = (kNA * wave) & 1;
 
   for (int64_t t = logical_block(); t < n_tiles; t += gridDim.x) {
     // bands of 4 vocabulary tiles (W, the larger operand, shared by the
     // XCDs of a band), blocks of 4 x 8
     int vt, mt;
     grouped_tile(t, n_vt, n_mt, 4, 8, &vt, &mt);
-    const int v0 = a.v_begin + vt * kTile;
+    const int v0 = a.v_begin + vt * kVT;
     const int m0 = mt * kTile;
 
     // A: rows v0.. of W, read as one buffer that ends at v_end (rows past it
-    // read as zeros).  Row r = 8 (kLoads wave + q) + l / 8 has r % 8 = l / 8
-    // and (r / 8) % 2 = q % 2, so its swizzled chunk depends on q only through
-    // q % 2: two lane offsets serve all loads, the rest is scalar.
+    // read as zeros).  Row r = 8 (kNA wave + q) + l / 8 has r % 8 = l / 8
+    // and (r / 8) % 2 = wpar ^ (q % 2), so its swizzled chunk depends on q
+    // only through q % 2: two lane offsets serve all loads, the rest is
+    // scalar.
     const __amdgpu_buffer_rsrc_t ra =
         make_rsrc(a.W + (int64_t)v0 * a.H, (int64_t)(a.v_end - v0) * a.H * 2);
     uint32_t a_voff[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par)
-      a_voff[par] = (uint32_t)((lrow * a.H + 8 * (lphys ^ lrow ^ par)) * 2);
+      a_voff[par] = (uint32_t)((lrow * a.H + 8 * (lphys ^ lrow ^ par ^ wpar)) * 2);
     // B: gathered rows of hidden; rows past n_rows point past the buffer
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.hidden, a.n_tokens * a.H * 2);
     uint32_t b_voff[kLoads];
@@ -503,46 +523,50 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
       b_voff[q] = row < 0 ? 0xFFFFFFF0u
                           : (uint32_t)((row * a.H + 8 * (lphys ^ swz_k(r))) * 2);
     }
-    f32x16 acc[4][kNJ];
+    f32x16 acc[kNA][kNJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kNA; ++i)
 #pragma unroll
       for (int j = 0; j < kNJ; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     auto issue = [&](char* stage, int k0) {
-      char* sa = stage + (kLoads * wave) * 1024;
+      char* sa = stage + (kNA * wave) * 1024;
+      char* sb = stage + kAB + (kLoads * wave) * 1024;
 #pragma unroll
-      for (int q = 0; q < kLoads; ++q) {
+      for (int q = 0; q < kNA; ++q) {
         buf2l(ra, sa + q * 1024, a_voff[q & 1],
-              (uint32_t)((8 * (kLoads * wave + q) * a.H + k0) * 2));
-        buf2l(rb, sa + kOpBytes + q * 1024, b_voff[q], (uint32_t)(k0 * 2));
+              (uint32_t)((8 * (kNA * wave + q) * a.H + k0) * 2));
+        if (q < kLoads) buf2l(rb, sb + q * 1024, b_voff[q], (uint32_t)(k0 * 2));
       }
     };
     // this wave's blocks that hold scored rows (a prefix of its kNJ)
     const int nv = min(kTile, n_rows - m0);
     const int kj = max(0, (nv - 32 * wb + kRowStride - 1) / kRowStride);
     // the epilogue's per-row inputs, loaded before the K loop so that they
-    // arrive during it (the loop's waits keep later loads from moving up)
+    // arrive during it (the loop's waits keep later loads from moving up);
+    // the five-block tile, whose registers are full, loads them in the
+    // epilogue instead
+    constexpr bool kPre = kNA == 4;
     int tg_pre[kNJ];
     float ref_pre[kNJ];
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) {
       const int m = m0 + 32 * wb + kRowStride * j + (lane & 31);
       const bool mv = m < n_rows;
-      tg_pre[j] = mv ? a.tgt[m] : -1;
-      ref_pre[j] = kStash && mv ? a.rref[m] : 0.f;
+      tg_pre[j] = kPre && mv ? a.tgt[m] : -1;
+      ref_pre[j] = kPre && kStash && mv ? a.rref[m] : 0.f;
     }
     // the K loop, specialised on that count (the waves of a workgroup run
     // the same loads and barriers whatever their count)
     auto kloop = [&](auto nj_tag) __attribute__((always_inline)) {
       constexpr int NJ = decltype(nj_tag)::value;
-      kloop_pipe<4, NJ, 4 + NJ>(
+      kloop_pipe<kNA, NJ, kNA + NJ, kNA, kNA + kLoads>(
           acc, 0, KT, smem0, smem1,
-          [&](const char* base, int kk, bf16x8(&f)[4]) __attribute__((always_inline)) {
+          [&](const char* base, int kk, bf16x8(&f)[kNA]) __attribute__((always_inline)) {
             const int coff = ((2 * kk + khalf) ^ fx) * 16;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kNA; ++i)
               f[i] = *reinterpret_cast<const bf16x8*>(base + a_off + i * 32 * kKRow + coff);
           },
           [&](const char* base, int kk, bf16x8(&f)[kNJ]) __attribute__((always_inline)) {
@@ -560,23 +584,29 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
     if constexpr (kStash || kGrad) __syncthreads();
 
     // ---- epilogue ---------------------------------------------------------
+    // (the lane index passes through an empty asm so that the epilogue's
+    // lane offsets are formed here, per tile, rather than hoisted out of the
+    // tile loop and held in registers across the K loop)
+    int el = lane;
+    asm volatile("" : "+v"(el));
     // Accumulator element e of block (i, j) on lane l holds vocabulary entry
-    // vl + 32i + 8(e/4) + e%4, vl = v0 + wa*128 + 4(l/32), for row
+    // vl + 32i + 8(e/4) + e%4, vl = v0 + wa*kHalf + 4(l/32), for row
     // m0 + 32 wb + kRowStride j + l%32.  A row's target sits in this lane's registers
-    // iff its offset dt from vl lies in [0, 128) with bit 2 clear.  Only the
+    // iff its offset dt from vl lies in [0, kHalf) with bit 2 clear.  Only the
     // tile that straddles v_end masks entries past the vocabulary.
-    const int vl = v0 + wa * 128 + 4 * (lane >> 5);
+    const int vl = v0 + wa * kHalf + 4 * (el >> 5);
     const int lim = a.v_end - vl;
     // G goes out through LDS: a lane's 4-entry pieces of a block land in
-    // this wave's own 32 rows of 256 B (pitch 272 B, so that neither side
-    // conflicts on banks and every address is one base plus a constant) and
-    // leave as whole 256-B row segments, 16 B a lane, instead of 8 B in
-    // each of 32 rows per store.  The blocks of a wave reuse the region.
-    constexpr int kPitch = 272;
-    static_assert(4 * 32 * kPitch <= kStageBytes, "staging fits a stage");
+    // this wave's own 32 rows of 2 kHalf bytes (256 or 320; pitch 16 B more,
+    // so that any 16 consecutive rows start on distinct 4-bank groups, the
+    // writes do not conflict on banks, and every address is one base plus a
+    // constant) and leave as whole row segments, 16 B a lane, instead of 8 B
+    // in each of 32 rows per store.  The blocks of a wave reuse the region.
+    constexpr int kPitch = 2 * kHalf + 16;
+    static_assert(4 * 32 * kPitch <= kSB, "staging fits a stage");
     char* const st = (wave < 4 ? smem0 : smem1) + (wave & 3) * (32 * kPitch);
     auto stage_put = [&](int i, int q, uint2 v) __attribute__((always_inline)) {
-      *reinterpret_cast<uint2*>(st + (lane & 31) * kPitch + 8 * (lane >> 5) + 16 * (4 * i + q)) =
+      *reinterpret_cast<uint2*>(st + (el & 31) * kPitch + 8 * (el >> 5) + 16 * (4 * i + q)) =
           v;
     };
     auto stage_flush = [&](int j) __attribute__((always_inline)) {
@@ -587,20 +617,53 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
       // hardware (no branch), and share one lane offset.
       sched_fence();
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      u32x4 v[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        v[k] = *reinterpret_cast<const u32x4*>(st + ((lane >> 4) + 4 * k) * kPitch +
-                                               16 * (lane & 15));
-      asm volatile("" ::: "memory");
       const int rb = m0 + 32 * wb + kRowStride * j;
-      const int col = v0 - a.v_begin + wa * 128;
+      const int col = v0 - a.v_begin + wa * kHalf;
       const __amdgpu_buffer_rsrc_t rg =
           make_rsrc(a.G + (int64_t)rb * a.ldg + col, (int64_t)(n_rows - rb) * a.ldg * 2 - 2 * col);
-      const uint32_t voff = (uint32_t)(((lane >> 4) * a.ldg + 8 * (lane & 15)) * 2);
+      if constexpr (kNA == 4) {
+        // 16 lanes per 256-byte row segment, four rows per store
+        u32x4 v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        __builtin_amdgcn_raw_buffer_store_b128(v[k], rg, voff, (uint32_t)(8 * k * a.ldg), 0);
+        for (int k = 0; k < 8; ++k)
+          v[k] = *reinterpret_cast<const u32x4*>(st + ((el >> 4) + 4 * k) * kPitch +
+                                                 16 * (el & 15));
+        asm volatile("" ::: "memory");
+        const uint32_t voff = (uint32_t)(((el >> 4) * a.ldg + 8 * (el & 15)) * 2);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          __builtin_amdgcn_raw_buffer_store_b128(v[k], rg, voff, (uint32_t)(8 * k * a.ldg), 0);
+      } else {
+        // 320-byte rows as a 256-byte segment (16 lanes a row, four rows a
+        // store, as above) and a 64-byte one (4 lanes a row, sixteen rows a
+        // store): lane offsets plus scalar ones.  G is ldg columns wide (a
+        // multiple of 256), so the last tile's pieces from column ldg on
+        // (entries past the vocabulary, all zeros) are not stored.
+        static_assert(kNA == 5, "256 + 64 bytes per row");
+        u32x4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          v[k] = *reinterpret_cast<const u32x4*>(st + ((el >> 4) + 4 * k) * kPitch +
+                                                 16 * (el & 15));
+        u32x4 t[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          t[k] = *reinterpret_cast<const u32x4*>(st + ((el >> 2) + 16 * k) * kPitch + 256 +
+                                                 16 * (el & 3));
+        asm volatile("" ::: "memory");
+        const uint32_t voff = (uint32_t)(((el >> 4) * a.ldg + 8 * (el & 15)) * 2);
+        if (col + 8 * (el & 15) < a.ldg) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(v[k], rg, voff, (uint32_t)(8 * k * a.ldg), 0);
+        }
+        const uint32_t toff = (uint32_t)(((el >> 2) * a.ldg + 128 + 8 * (el & 3)) * 2);
+        if (col + 128 + 8 * (el & 3) < a.ldg) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(t[k], rg, toff, (uint32_t)(32 * k * a.ldg), 0);
+        }
+      }
       sched_fence();
     };
     auto epilogue = [&](auto full_tag) __attribute__((always_inline)) {
@@ -608,22 +671,23 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
 #pragma unroll
       for (int j = 0; j < kNJ; ++j) {
         if (j >= kj) break;  // (no scored row in this block or the next)
-        const int m = m0 + 32 * wb + kRowStride * j + (lane & 31);
+        const int m = m0 + 32 * wb + kRowStride * j + (el & 31);
         const bool mvalid = m < n_rows;
-        const int tg = tg_pre[j];
+        const int tg = kPre ? tg_pre[j] : mvalid ? a.tgt[m] : -1;
         const int dt = tg - vl;
-        const bool holds_tgt = (unsigned)dt < 128u && (dt & 4) == 0;
+        const bool holds_tgt = (unsigned)dt < (unsigned)kHalf && (dt & 4) == 0;
         if (!kGrad) {
-          // sv: the scaled logits s = z log2(e) (capped first), or without a
-          // cap the logits z themselves, scaled where they are used: the
-          // maximum and the target are scaled after the selection (a
-          // positive factor commutes with max, and each is rounded once, as
-          // before), and 2^(s - mref) takes s - mref as one fma.
+          // The accumulators of row block j become, in place, the scaled
+          // logits s = z log2(e) (capped first), or without a cap the logits
+          // z themselves, scaled where they are used: the maximum and the
+          // target are scaled after the selection (a positive factor
+          // commutes with max, and each is rounded once, as before), and
+          // 2^(s - mref) takes s - mref as one fma.  (In place: a copy
+          // would hold a second set of the block's values in registers.)
           constexpr bool kRaw = !kCap;
-          float sv[4][16];
           float mx = -INFINITY;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < kNA; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
               const int off = 32 * i + 8 * (e >> 2) + (e & 3);
@@ -631,16 +695,16 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
               if (kCap) zc = softcap_fwd(zc, a.softcap, a.inv_softcap, &dc);
               float sc = kRaw ? zc : zc * kLog2e;
               if (!kFull) sc = off < lim ? sc : -INFINITY;
-              sv[i][e] = sc;
+              acc[i][j][e] = sc;
               mx = fmaxf(mx, sc);
             }
           // (the target is never past the vocabulary, so never masked)
           if (mvalid && holds_tgt) {
-            const float pt = pick_entry(sv, dt);
+            const float pt = pick_entry(acc, j, dt);
             a.ztgt[m] = kRaw ? pt * kLog2e : pt;
           }
-          // the row's maximum over this wave's 128 entries (two lanes hold
-          // 64 each); -inf when all of them lie past the vocabulary
+          // the row's maximum over this wave's kHalf entries (two lanes hold
+          // half each); -inf when all of them lie past the vocabulary
           mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
           if (kRaw) mx *= kLog2e;
           const float mref = mx == -INFINITY ? 0.f : mx;
@@ -650,20 +714,20 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
           // else rho = m_h and the row is flagged
           float fs = 1.f;
           if (kStash) {
-            const float R = ref_pre[j];
+            const float R = kPre ? ref_pre[j] : mvalid ? a.rref[m] : 0.f;
             const bool near = !(mx - R > kStashSpan);
-            if (!near && mvalid && lane < 32) a.row_flag[m] = 1;
+            if (!near && mvalid && el < 32) a.row_flag[m] = 1;
             fs = mx == -INFINITY ? 0.f : near ? __builtin_amdgcn_exp2f(mx - R) : 1.f;
           }
           float sum = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < kNA; ++i) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               float g[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                const float sc = sv[i][4 * q + r];
+                const float sc = acc[i][j][4 * q + r];
                 const float e2 = __builtin_amdgcn_exp2f(kRaw ? __builtin_fmaf(sc, kLog2e, -mref)
                                                              : sc - mref);
                 sum += e2;
@@ -680,10 +744,14 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
               if (kStash)
                 stage_put(i, q, make_uint2(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])));
             }
+            // (five blocks: the sum is formed block by block, so that the
+            // block's exponentials are not all held until the end for it)
+            if constexpr (kNA == 5) asm volatile("" : "+v"(sum));
+          }
           if (kStash) stage_flush(j);
           sum += __shfl_xor(sum, 32, 64);
-          if (lane < 32 && mvalid)
-            a.partial[(int64_t)m * a.n_part + 2 * ((v0 - a.v_begin) / kTile) + wa] =
+          if (el < 32 && mvalid)
+            a.partial[(int64_t)m * a.n_part + 2 * ((v0 - a.v_begin) / kVT) + wa] =
                 make_float2(mx, sum);
         } else {
           // G = w p cap' everywhere, then the target entry is rewritten with
@@ -693,7 +761,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
           const float lse2 = mvalid ? a.lse[m] * kLog2e : 0.f;
           const float wm = mvalid ? a.w[m] : 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < kNA; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               float g[4];
@@ -717,14 +785,14 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
             }
             const float p = __builtin_amdgcn_exp2f(zt2 - lse2);
             // (over the piece this lane staged above: program order)
-            *reinterpret_cast<bf16_t*>(st + (lane & 31) * kPitch + 2 * (tg - (v0 + wa * 128))) =
+            *reinterpret_cast<bf16_t*>(st + (el & 31) * kPitch + 2 * (tg - (v0 + wa * kHalf))) =
                 (bf16_t)((p - 1.f) * dc * wm);
           }
           stage_flush(j);
         }
       }
     };
-    if (v0 + kTile <= a.v_end)
+    if (v0 + kVT <= a.v_end)
       epilogue(std::true_type{});
     else
       epilogue(std::false_type{});
@@ -1205,7 +1273,7 @@ __device__ __forceinline__ void sum_block_sums(const double* __restrict__ block_
 
 __global__ void __launch_bounds__(kThreads)
 stash_scale_kernel(bf16_t* __restrict__ G, int64_t ldg, const float2* __restrict__ partial,
-                   int n_part, int max_rows, const float* __restrict__ lse, const float* __restrict__ ztgt,
+                   int n_part, int half, int max_rows, const float* __restrict__ lse, const float* __restrict__ ztgt,
                    const int32_t* __restrict__ tgt, const float* __restrict__ w,
                    const int32_t* __restrict__ n_rows_ptr, int V, float inv_softcap,
                    const float* __restrict__ rref, const int* __restrict__ row_flag,
@@ -1234,19 +1302,22 @@ stash_scale_kernel(bf16_t* __restrict__ G, int64_t ldg, const float2* __restrict
       gt = (__builtin_amdgcn_exp2f(zt2 - lse2) - 1.f) * dc * wm;
     }
     uint4* grow = reinterpret_cast<uint4*>(G + (int64_t)m * ldg);
+    // the columns the partials cover (n_part partials of `half` entries;
+    // the stash beyond them, if any, lies past the vocabulary and is not read)
+    const int vend = (int)min(ldg, (int64_t)n_part * half);
     // four 16-byte groups in flight per thread
-    for (int v0 = (int)threadIdx.x * 8; v0 < ldg; v0 += 4 * kScaleSeg) {
+    for (int v0 = (int)threadIdx.x * 8; v0 < vend; v0 += 4 * kScaleSeg) {
       uint4 in[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int v = v0 + b * kScaleSeg;
-        if (v < ldg) in[b] = grow[v / 8];
+        if (v < vend) in[b] = grow[v / 8];
       }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int v = v0 + b * kScaleSeg;
-        if (v >= ldg) break;
-        const float mh = partial[(int64_t)m * n_part + v / (kTile / 2)].x;
+        if (v >= vend) break;
+        const float mh = partial[(int64_t)m * n_part + v / half].x;
         const float rho = mh - R > kStashSpan ? mh : R;
         const float f = wm * __builtin_amdgcn_exp2f(rho - lse2);
         const uint32_t wd[4] = {in[b].x, in[b].y, in[b].z, in[b].w};
@@ -1570,6 +1641,12 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   }
   const bool stash = MDLM_STASH && grad && x.dtype == MDLM_BF16 && vc >= x.V;
   if (!stash) zero_dh();
+  // The forward pass with the stash and no softcap takes vocabulary tiles of
+  // 320 rows (five 32-row blocks per wave), the others 256: one partial per
+  // wave's half of a tile, `half` entries each.
+  const bool wide = MDLM_WIDE_TILE && stash && x.softcap <= 0.f;
+  const int half = wide ? 160 : kTile / 2;
+  const int n_part_f = 2 * (int)((x.V + 2 * half - 1) / (2 * half));
   bf16_t* G = reinterpret_cast<bf16_t*>(ws + L.G);
   float* rref = reinterpret_cast<float*>(ws + L.rref);
   int* row_flag = reinterpret_cast<int*>(ws + L.flag);
@@ -1591,7 +1668,7 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     la.v_begin = 0;
     la.v_end = x.V;
     la.partial = partial;
-    la.n_part = 2 * L.n_vt;
+    la.n_part = n_part_f;
     la.ztgt = ztgt;
     la.G = G;
     la.ldg = vc;
@@ -1606,6 +1683,8 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
           reinterpret_cast<uint4*>(x.d_hidden), dh16, dh_tail_ptr, dh_tail);
       if (x.softcap > 0.f)
         logits_kernel<false, true, true><<<grid, kGemmThreads, 0, stream>>>(la);
+      else if (wide)
+        logits_kernel<false, false, true, 5><<<grid, kGemmThreads, 0, stream>>>(la);
       else
         logits_kernel<false, false, true><<<grid, kGemmThreads, 0, stream>>>(la);
     } else if (x.softcap > 0.f) {
@@ -1633,8 +1712,8 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
     dim3 g((unsigned)max_rows, (unsigned)L.n_vt);
     f32_logits_kernel<false><<<g, kThreads, 0, stream>>>(fa);
   }
-  // (bf16: one partial per 128-entry half tile; fp32: one per 256-entry tile)
-  const int n_part = x.dtype == MDLM_BF16 ? 2 * L.n_vt : L.n_vt;
+  // (bf16: one partial per half tile; fp32: one per 256-entry tile)
+  const int n_part = x.dtype == MDLM_BF16 ? n_part_f : L.n_vt;
   merge_kernel<<<L.n_bsum, kThreads, 0, stream>>>(partial, n_part, (int)max_rows, ztgt, x.tgt,
                                                   x.V, x.w, x.n_rows, lse, x.row_ce, bsum);
   // with the stash the loss is summed by the first scaling launch below
@@ -1671,7 +1750,7 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   auto scale_rows = [&](int which, bool with_loss) {
     const unsigned sgrid = (unsigned)std::min<int64_t>(max_rows, (int64_t)cus * 8);
     stash_scale_kernel<<<sgrid, kThreads, 0, stream>>>(
-        G, vc, partial, 2 * L.n_vt, (int)max_rows, lse, ztgt, x.tgt, x.w, x.n_rows, x.V,
+        G, vc, partial, n_part_f, half, (int)max_rows, lse, ztgt, x.tgt, x.w, x.n_rows, x.V,
         inv_cap, rref, row_flag, which, with_loss ? bsum : nullptr, L.n_bsum, x.loss);
   };
   if (stash) scale_rows(want_dh ? 1 : -1, true);
