@@ -11,11 +11,12 @@
 //   0. (gradient with the preferred workspace) stash_ref_kernel: each row's
 //      reference R, its capped target logit in log2 units from a plain dot
 //      product; its spare blocks clear d_hidden.
-//   1. logits_kernel<fwd>: z = W h over 256 x 256 (vocab x row) tiles, K = H,
-//      on bf16 MFMA with fp32 accumulation.  Operands go from global memory
-//      straight into a two-stage LDS ring (no register staging), two waves per
-//      SIMD.  The epilogue caps, takes each row's partial (m_h, sum 2^(s-m_h))
-//      over each 128-entry half of the tile (m_h: the half's maximum) and
+//   1. logits_kernel<fwd>: z = W h over 256 x 256 (vocab x row) tiles, or
+//      320 x 256 with the stash and no softcap, K = H, on bf16 MFMA with
+//      fp32 accumulation.  Operands go from global memory straight into a
+//      two-stage LDS ring (no register staging), two waves per SIMD.  The
+//      epilogue caps, takes each row's partial (m_h, sum 2^(s-m_h)) over each
+//      half of the tile (128 or 160 entries; m_h: the half's maximum) and
 //      picks the target logit.  Logits never leave registers.  With the
 //      preferred workspace and the gradient wanted, the epilogue also stashes
 //      2^(s - rho) zhat' (zhat' = 1 - (zhat/c)^2 with a softcap c, else 1) in
@@ -274,9 +275,9 @@ struct LogitsArgs {
   float inv_softcap;
   int v_begin;  // vocabulary range of this launch
   int v_end;
-  float2* partial;  // fwd: [max_rows][n_part] (max, sum) per 128-entry half tile, in
-                    // log2 units (row-major, so that a row's partials are contiguous)
-  int n_part;       // 2 ceil(V/kTile)
+  float2* partial;  // fwd: [max_rows][n_part] (max, sum) per half tile, in log2
+                    // units (row-major, so that a row's partials are contiguous)
+  int n_part;       // 2 ceil(V / tile rows): 256, or 320 (see logits_kernel)
   float* ztgt;      // [max_rows] capped target logit x log2(e) (fwd writes, grad reads)
   const float* lse; // grad: [max_rows]
   bf16_t* G;        // grad, or fwd with the stash: [max_rows][ldg], column = v - v_begin
@@ -441,17 +442,17 @@ __device__ __forceinline__ void kloop_pipe(f32x16 (&acc)[kNIMax][kNJ], int kb, i
   wait_vmem();
 }
 
-// Tile of 256 vocabulary rows (operand A, rows of W) by 256 scored rows
+// Tile of 64 kNA vocabulary rows (operand A, rows of W) by 256 scored rows
 // (operand B, rows of hidden gathered through row_idx), K = H.  Wave w owns
-// vocabulary rows 128 (w % 2) .. +127 and the scored-row blocks
-// 32 (w / 2) + kRowStride j .. +31, j < kNJ: a 4 x kNJ grid of 32 x 32 MFMA
-// blocks, of which only those holding scored rows are computed.
+// vocabulary rows 32 kNA (w % 2) .. + 32 kNA - 1 and the scored-row blocks
+// 32 (w / 2) + kRowStride j .. +31, j < kNJ: a kNA x kNJ grid of 32 x 32
+// MFMA blocks, of which only those holding scored rows are computed.
 // kStash (forward only): the epilogue also keeps the tile's unnormalised
 // softmax, 2^(s - rho) zhat', as bf16 in G, so that the gradient needs no
 // second pass over the logits.  rho is the row's reference R (see
-// kStashSpan) or, far above it, the row's maximum m_h over the wave's
-// 128-entry half of the tile.  The partials are (m_h, sum 2^(s - m_h)) either
-// way, the same as without the stash.
+// kStashSpan) or, far above it, the row's maximum m_h over the wave's half
+// of the tile.  The partials are (m_h, sum 2^(s - m_h)) either way, the same
+// as without the stash.
 // kNA: 32-row blocks of W per wave, so a vocabulary tile of 64 kNA rows
 // (256, or 320 for the forward pass with the stash and no softcap), each
 // wave owning half of it: 32 kNA entries per row and partial.
