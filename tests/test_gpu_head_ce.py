@@ -72,8 +72,8 @@ def _small(seed, n_docs, max_len, H, V, **kw):
 @pytest.mark.parametrize("align", [oracle.ALIGNED, oracle.SHIFTED])
 def test_bf16_small_tiles_and_ragged_tails(H, V, align):
     # ~300 scored rows: several 128-row tiles with a ragged last one; V with a
-    # ragged last vocabulary tile, of 256 entries or (the forward pass with
-    # the stash and no softcap) 320, including last tiles more than 256
+    # ragged last vocabulary tile, of 256 entries or (the forward pass
+    # without a softcap) 320, including last tiles more than 256
     # entries short of full (V = 300, 600, 4096); H multiples of 64 but not
     # of 256
     inp = _small(H + V, n_docs=5, max_len=250, H=H, V=V)

@@ -12,7 +12,7 @@
 //      reference R, its capped target logit in log2 units from a plain dot
 //      product; its spare blocks clear d_hidden.
 //   1. logits_kernel<fwd>: z = W h over 256 x 256 (vocab x row) tiles, or
-//      320 x 256 with the stash and no softcap, K = H, on bf16 MFMA with
+//      320 x 256 without a softcap, K = H, on bf16 MFMA with
 //      fp32 accumulation.  Operands go from global memory straight into a
 //      two-stage LDS ring (no register staging), two waves per SIMD.  The
 //      epilogue caps, takes each row's partial (m_h, sum 2^(s-m_h)) over each
@@ -454,12 +454,12 @@ __device__ __forceinline__ void kloop_pipe(f32x16 (&acc)[kNIMax][kNJ], int kb, i
 // of the tile.  The partials are (m_h, sum 2^(s - m_h)) either way, the same
 // as without the stash.
 // kNA: 32-row blocks of W per wave, so a vocabulary tile of 64 kNA rows
-// (256, or 320 for the forward pass with the stash and no softcap), each
+// (256, or 320 for the forward pass without a softcap), each
 // wave owning half of it: 32 kNA entries per row and partial.
 template <bool kGrad, bool kCap, bool kStash = false, int kNA = 4>
 __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
   static_assert(!(kGrad && kStash), "the stash is written by the forward pass");
-  static_assert(kNA == 4 || (kNA == 5 && kStash && !kCap), "320 rows: the stash, no softcap");
+  static_assert(kNA == 4 || (kNA == 5 && !kGrad && !kCap), "320 rows: forward, no softcap");
   constexpr int kVT = 64 * kNA;            // vocabulary rows of a tile
   constexpr int kHalf = 32 * kNA;          // a wave's entries per row
   constexpr int kAB = kVT * kKRow;         // W's bytes in a stage
@@ -1642,10 +1642,11 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
   }
   const bool stash = MDLM_STASH && grad && x.dtype == MDLM_BF16 && vc >= x.V;
   if (!stash) zero_dh();
-  // The forward pass with the stash and no softcap takes vocabulary tiles of
-  // 320 rows (five 32-row blocks per wave), the others 256: one partial per
-  // wave's half of a tile, `half` entries each.
-  const bool wide = MDLM_WIDE_TILE && stash && x.softcap <= 0.f;
+  // The bf16 forward pass without a softcap takes vocabulary tiles of 320
+  // rows (five 32-row blocks per wave), with a softcap 256: one partial per
+  // wave's half of a tile, `half` entries each.  (The gradient recompute
+  // reads only the log-sum-exp and the target logit.)
+  const bool wide = MDLM_WIDE_TILE && x.dtype == MDLM_BF16 && x.softcap <= 0.f;
   const int half = wide ? 160 : kTile / 2;
   const int n_part_f = 2 * (int)((x.V + 2 * half - 1) / (2 * half));
   bf16_t* G = reinterpret_cast<bf16_t*>(ws + L.G);
@@ -1690,6 +1691,8 @@ hipError_t launch_head_ce(const HeadCeArgs& x, hipStream_t stream) {
         logits_kernel<false, false, true><<<grid, kGemmThreads, 0, stream>>>(la);
     } else if (x.softcap > 0.f) {
       logits_kernel<false, true><<<grid, kGemmThreads, 0, stream>>>(la);
+    } else if (wide) {
+      logits_kernel<false, false, false, 5><<<grid, kGemmThreads, 0, stream>>>(la);
     } else {
       logits_kernel<false, false><<<grid, kGemmThreads, 0, stream>>>(la);
     }
