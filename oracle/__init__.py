@@ -25,10 +25,14 @@ Sources for what is computed:
   * LLaDA-8B-MDLM-LoRA model card, "Training" table, "Objective" row: the
     corrective mixture's option names (mixture_prob, noise_token_wt,
     clean_token_wt), all 0 for the MDLM objective.  No formula is given:
-    ``corrupt_mixture`` and ``compact_corrective`` take a stated reading and
-    are pinned only through their reductions (mixture 0 = absorbing noise,
-    mixture 1 = the uniform-noise ids, zero weights = the MDLM row list) and
-    the mixture's frequency; beyond those, parity unpinned.
+    ``corrupt_mixture`` and ``compact_corrective`` take a stated reading.
+    ``corrupt_mixture`` is pinned only through its reductions (mixture 0 =
+    absorbing noise, mixture 1 = the uniform-noise ids) and the mixture's
+    frequency; beyond those (which Philox stream decides a replacement),
+    parity unpinned.  ``compact_corrective`` is pinned at its ends (zero
+    weights = the MDLM row list, noise weight 1 = the uniform-noise MDLM row
+    list, the clean weight alone = the mean CE) and, in between, by the loss
+    being the straight line through those ends in each weight.
 """
 
 from .philox import philox4x32_10  # noqa: F401

@@ -224,8 +224,10 @@ def compact_corrective(codes, x0, cu_seqlens, p_doc, align, noise_token_wt, clea
 
     [LLaDA] Training table, Objective row: the option names noise_token_wt
     and clean_token_wt; with both 0 the loss is the MDLM one (the CE of
-    each masked token, scaled by 1/p).  Reading taken
-    (parity unpinned beyond the reductions): every position predicts its
+    each masked token, scaled by 1/p).  Reading taken (pinned at the ends,
+    zero weights, noise weight 1 and the clean weight alone, by reductions,
+    and in between by the loss being linear in each weight): every position
+    predicts its
     clean token; a masked token keeps the weight 1 / (p_b N), a replaced
     token gets noise_token_wt / (p_b N) and, when clean_token_wt is not 0,
     every uncorrupted token gets clean_token_wt / N.  Rows are the corrupted

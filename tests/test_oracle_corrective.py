@@ -2,8 +2,9 @@
 compact_corrective) against what holds independently of the reading taken
 for its options: the reductions to absorbing and uniform noise and to the
 MDLM row list, the mixture's frequency and its independence from the
-corruption decision, a vectorised brute force of the row list, and the
-clean-token weighting against torch's cross-entropy."""
+corruption decision, a vectorised brute force of the row list, the
+clean-token weighting against torch's cross-entropy, and the whole loss at
+any weight as the straight line through its pinned ends."""
 
 import numpy as np
 import pytest
@@ -117,3 +118,34 @@ def test_clean_weight_is_mean_ce_over_all_tokens():
     z = torch.from_numpy(h) @ torch.from_numpy(W).T
     want = 0.7 * F.cross_entropy(z, torch.from_numpy(x0).long()).item()
     assert abs(loss - want) <= 1e-12 * abs(want)
+
+
+@pytest.mark.parametrize("align", [ALIGNED, SHIFTED])
+def test_weights_interpolate_between_their_pinned_ends(align):
+    # The ends are pinned above: noise_token_wt 0 gives the MDLM list of the
+    # masked tokens, 1 the MDLM list of every corrupted token (as uniform
+    # noise scores it), and clean_token_wt scales the mean CE over the clean
+    # tokens.  A weight enters the loss as a factor of its rows' CE, so the
+    # whole loss (row list, then head + CE) at any other weight is the
+    # straight line through those ends; a weight applied twice, squared, or
+    # to the wrong rows leaves it.
+    x0, cu, V = _stream(5, n_docs=12, max_len=120, V=300)
+    rng = np.random.default_rng(11)
+    n, H = x0.shape[0], 16
+    h = rng.standard_normal((n, H))
+    W = rng.standard_normal((V, H)) * 0.3
+    _, codes, p, _ = corrupt_mixture(x0, cu, 9, 0.4, 0.3, V - 1, V)
+    assert (codes == CODE_MASKED).sum() > 50 and (codes == CODE_REPLACED).sum() > 20
+
+    def loss(a, c=0.0):
+        rows, tgt, w = compact_corrective(codes, x0, cu, p, align, a, c)
+        return head_ce(h, W, rows, tgt, w)[0]
+
+    l0, l1, lc = loss(0.0), loss(1.0), loss(0.0, 1.0)
+    assert l1 > l0 > 0 and lc > l0
+    for a in (0.25, 0.5, 2.0, 3.7):
+        want = (1.0 - a) * l0 + a * l1
+        assert abs(loss(a) - want) <= 1e-12 * (1.0 + abs(a)) * l1
+    for c in (0.3, 0.7):
+        want = (1.0 - c) * l0 + c * lc
+        assert abs(loss(0.0, c) - want) <= 1e-12 * lc

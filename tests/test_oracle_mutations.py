@@ -9,7 +9,8 @@ log-sum-exp that misses a vocabulary chunk, and in the variants the
 example-mean divisor, the eligibility position, the mean's denominator and
 the weight in the head-weight gradient, and in the corrective mixture the
 masked and replaced weights swapped, the replace decision inverted or drawn
-from the corruption word, and the clean weight taken over the clean tokens.
+from the corruption word, the clean weight taken over the clean tokens, the
+noise weight squared, and the clean weight leaking onto the replaced rows.
 """
 
 import math
@@ -261,3 +262,30 @@ def test_clean_weight_over_clean_tokens(monkeypatch):
         return rows, tgt, np.where(clean, w * n / n_clean, w)
     _patch_c(monkeypatch, "compact_corrective", bad)
     _fails(TC.test_row_list_brute_force, M.ALIGNED, 2.0, 0.25)
+
+
+def test_replaced_weight_squared(monkeypatch):
+    # noise_token_wt applied as its square: equal at the pinned ends 0 and 1,
+    # wrong in between; the interpolation pin (which does not restate the
+    # weight formula) catches it
+    orig = M.compact_corrective
+
+    def bad(codes, x0, cu_seqlens, p_doc, align, a, c):
+        return orig(codes, x0, cu_seqlens, p_doc, align, a * a, c)
+    _patch_c(monkeypatch, "compact_corrective", bad)
+    _fails(TC.test_weights_interpolate_between_their_pinned_ends, M.ALIGNED)
+
+
+def test_clean_weight_on_replaced_rows_too(monkeypatch):
+    # clean_token_wt added to the replaced rows as well: the clean end (c = 1)
+    # moves with it, but the line through the ends does not hold
+    orig = M.compact_corrective
+
+    def bad(codes, x0, cu_seqlens, p_doc, align, a, c):
+        rows, tgt, w = orig(codes, x0, cu_seqlens, p_doc, align, a, c)
+        codes = np.asarray(codes)
+        g = rows + 1 if align == M.SHIFTED else rows
+        rep = codes[g] == M.CODE_REPLACED
+        return rows, tgt, np.where(rep, w + c * c / codes.shape[0], w)
+    _patch_c(monkeypatch, "compact_corrective", bad)
+    _fails(TC.test_weights_interpolate_between_their_pinned_ends, M.SHIFTED)
