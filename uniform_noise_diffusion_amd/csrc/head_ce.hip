@@ -81,11 +81,6 @@ constexpr int kRowStride = 32 * (kWaves / 2);
 constexpr int kOpBytes = kTile * kKRow;       // one operand tile: 32 KiB
 constexpr int kStageBytes = 2 * kOpBytes;     // A + B: 64 KiB
 constexpr int kLdsBytes = 2 * kStageBytes;    // two stages: 128 KiB
-#ifndef MDLM_VMEM_EVERY
-#define MDLM_VMEM_EVERY 2
-#endif
-constexpr int kVmemEvery = MDLM_VMEM_EVERY;  // MFMAs per interleaved prefetch load
-static_assert(2 * kLoads * kVmemEvery <= 4 * (16 / kWaves) * (64 / 16), "loads fit in a step");
 #ifndef MDLM_STASH
 #define MDLM_STASH 1
 #endif
@@ -204,10 +199,6 @@ __device__ __forceinline__ void with_count(int n, F&& f) {
   }
 }
 
-// Compile-time count of prefetch loads interleaved with a step's MFMAs.
-constexpr std::integral_constant<int, 2 * kLoads> kInterleave{};
-constexpr std::integral_constant<int, 0> kNoLoads{};
-
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Keeps the scheduler from moving instructions across this point: used so a
@@ -285,57 +276,6 @@ struct LogitsArgs {
   const float* rref;  // fwd with the stash: [max_rows] per-row reference, log2 units
   int* row_flag;      // fwd with the stash: [max_rows] set where the reference was not used
 };
-
-// Software-pipelined MFMA block for one 64-deep K step of a wave's tile: the
-// fragments of 16-deep slice kk+1 are read from LDS while the MFMAs of slice
-// kk run.  `ra` reads the A fragments of a slice, `rb` the B fragments.
-// kVmem global->LDS loads issued just before the call (the next stage's
-// prefetch) are spread over the first MFMAs of the step, one before every
-// kVmemEvery-th MFMA, rather than left to the scheduler, which would sink
-// them to the end of the step (leaving them no time to land).
-// Only the first NI A blocks and NJ B blocks take part (the rest lie past the
-// scored rows); the readers' unused fragments are dead and dropped.
-template <int kReads, int kVmem, int NI = 4, int NJ = kNJ, typename ReadA, typename ReadB>
-__device__ __forceinline__ void mma_k64(f32x16 (&acc)[4][kNJ], ReadA ra, ReadB rb) {
-  bf16x8 af[2][4], bfr[2][kNJ];
-  ra(0, af[0]);
-  rb(0, bfr[0]);
-#pragma unroll
-  for (int kk = 0; kk < kBK / 16; ++kk) {
-    const int cur = kk & 1;
-    if (kk + 1 < kBK / 16) {
-      ra(kk + 1, af[cur ^ 1]);
-      rb(kk + 1, bfr[cur ^ 1]);
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
-                                                            0, 0, 0);
-  }
-  // Issue order for the scheduler: the first slice's reads, then each slice's
-  // MFMAs alternated one for one with the next slice's reads (transpose reads
-  // count twice in `kReads`), with the loads interleaved as above.
-  constexpr int kMfma = NI * NJ;
-  constexpr int kSlices = kBK / 16;
-  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-#pragma unroll
-  for (int kk = 0; kk < kSlices; ++kk) {
-#pragma unroll
-    for (int x = 0; x < kMfma; ++x) {
-      const int gx = kk * kMfma + x;
-      if (kVmem > 0 && gx % kVmemEvery == 0 && gx / kVmemEvery < kVmem)
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (kk + 1 < kSlices && x < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    if (kk + 1 < kSlices) {
-#pragma unroll
-      for (int x = kMfma; x < kReads; ++x) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-  }
-}
 
 // Waits for this wave's LDS accesses and until at most n of its memory
 // operations are outstanding, then joins the workgroup's barrier.  Written
@@ -1053,56 +993,33 @@ __global__ void __launch_bounds__(kGemmThreads, 1) dw_kernel(DwArgs a) {
         buf2l(rb, sa + kOpBytes + q * 1024, b_voff[q & 1], (uint32_t)(r * a.H * 2));
       }
     };
-    auto compute = [&](const char* base, auto vmem) {
-      mma_k64<2 * 4 + 2 * kNJ, decltype(vmem)::value>(
-          acc,
-          [&](int kk, bf16x8(&f)[4]) {
-            const char* arow_p = base + (16 * kk + tr_row) * kNRow;
+    // the K loop of the other MFMA kernels (each step's barrier before its
+    // last slice; the prefetch past the last row reads empty ranges)
+    kloop_pipe<4, kNJ, 2 * 4 + 2 * kNJ>(
+        acc, 0, KT, smem0, smem1,
+        [&](const char* base, int kk, bf16x8(&f)[4]) __attribute__((always_inline)) {
+          const char* arow_p = base + (16 * kk + tr_row) * kNRow;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const shortx4 lo = ds_read_tr(arow_p + a_col_off[i]);
-              const shortx4 hi = ds_read_tr(arow_p + 4 * kNRow + a_col_off[i]);
-              const short v8 __attribute__((__vector_size__(16))) = {
-                  lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              f[i] = __builtin_bit_cast(bf16x8, v8);
-            }
-          },
-          [&](int kk, bf16x8(&f)[kNJ]) {
-            const char* brow_p = base + kOpBytes + (16 * kk + tr_row) * kNRow;
+          for (int i = 0; i < 4; ++i) {
+            const shortx4 lo = ds_read_tr(arow_p + a_col_off[i]);
+            const shortx4 hi = ds_read_tr(arow_p + 4 * kNRow + a_col_off[i]);
+            const short v8 __attribute__((__vector_size__(16))) = {
+                lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            f[i] = __builtin_bit_cast(bf16x8, v8);
+          }
+        },
+        [&](const char* base, int kk, bf16x8(&f)[kNJ]) __attribute__((always_inline)) {
+          const char* brow_p = base + kOpBytes + (16 * kk + tr_row) * kNRow;
 #pragma unroll
-            for (int j = 0; j < kNJ; ++j) {
-              const shortx4 lo = ds_read_tr(brow_p + b_col_off[j]);
-              const shortx4 hi = ds_read_tr(brow_p + 4 * kNRow + b_col_off[j]);
-              const short v8 __attribute__((__vector_size__(16))) = {
-                  lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-              f[j] = __builtin_bit_cast(bf16x8, v8);
-            }
-          });
-    };
-
-    __syncthreads();
-    issue(smem0, 0);
-    // same pipeline as the other MFMA kernels (unconditional last prefetch,
-    // of empty ranges, retired by the wait after the loop)
-    int kt = 0;
-    for (; kt + 2 <= KT; kt += 2) {
-      wait_vmem();
-      __syncthreads();
-      issue(smem1, (kt + 1) * kBK);
-      compute(smem0, kInterleave);
-      sched_fence();
-      wait_vmem();
-      __syncthreads();
-      issue(smem0, (kt + 2) * kBK);
-      compute(smem1, kInterleave);
-      sched_fence();
-    }
-    if (kt < KT) {
-      wait_vmem();
-      __syncthreads();
-      compute(smem0, kNoLoads);
-    }
-    wait_vmem();
+          for (int j = 0; j < kNJ; ++j) {
+            const shortx4 lo = ds_read_tr(brow_p + b_col_off[j]);
+            const shortx4 hi = ds_read_tr(brow_p + 4 * kNRow + b_col_off[j]);
+            const short v8 __attribute__((__vector_size__(16))) = {
+                lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            f[j] = __builtin_bit_cast(bf16x8, v8);
+          }
+        },
+        issue);
 
     // acc element e of block (i, j) on lane l: vocabulary entry v_begin + v0
     // + wa*128 + 32i + 8(e/4) + 4(l/32) + e%4, hidden column h0 + wb*kWB +
