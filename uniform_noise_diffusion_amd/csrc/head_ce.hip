@@ -431,12 +431,12 @@ __global__ void __launch_bounds__(kGemmThreads, 1) logits_kernel(LogitsArgs a) {
   const int wpar = (kNA * wave) & 1;
 
   for (int64_t t = logical_block(); t < n_tiles; t += gridDim.x) {
-    // bands of vocabulary tiles (W, the larger operand, shared by the XCDs
-    // of a band): blocks of 4 x 8 tiles, or of 8 x 4 with the 320-row tiles
-    // (measured against 4 x 8, 2 x 16, 16 x 2 and 32 x 1 there: 0.4% faster
-    // than 4 x 8 on llada8b-1x4096, 1.5% on packed)
+    // bands of 8 vocabulary tiles (W, the larger operand, shared by the
+    // XCDs of a band), blocks of 8 x 4 (measured against 4 x 8, 2 x 16,
+    // 16 x 2 and 32 x 1: 0.4% faster than 4 x 8 per call on llada8b-1x4096,
+    // 1.5% on packed, 0.6% on canvas with its 256-row tiles)
     int vt, mt;
-    grouped_tile(t, n_vt, n_mt, kNA == 5 ? 8 : 4, kNA == 5 ? 4 : 8, &vt, &mt);
+    grouped_tile(t, n_vt, n_mt, 8, 4, &vt, &mt);
     const int v0 = a.v_begin + vt * kVT;
     const int m0 = mt * kTile;
 
